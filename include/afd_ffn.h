@@ -1,0 +1,181 @@
+/*
+ * afd_ffn.h -- C ABI of the expert (FFN) side of an attention-FFN
+ * disaggregated mixture-of-experts layer, for one AMD MI355X (gfx950).
+ *
+ * The operation (sources: "FastAFD" structured summary, System Design items
+ * 1-4 and the legend of Eq. (3); vLLM AFD plugin blog, "FFN service" and
+ * "connector layer"): the attention side keeps norms, projections and top-k
+ * routing and publishes, per layer, token hidden states (block-FP8 in FastAFD)
+ * with the routing metadata; the FFN side runs the routed experts' FFNs as
+ * grouped GEMMs with the activation and returns the combined output.  This
+ * library is that FFN-side computation on one GPU, for one layer and one
+ * batch of tokens:
+ *
+ *   out[t] = sum_{k: ids[t,k] >= 0} w[t,k] * FFN_{ids[t,k]}(x_t)  (+ FFN_S(x_t))
+ *   FFN_e(x) = Wd_e^T ( silu(Wg_e^T x) * (Wu_e^T x) )
+ *
+ * computed as: per-expert histogram of the ids, exclusive prefix scan,
+ * stable expert-major permutation of the (token, slot) assignments, grouped
+ * GEMM gate/up with fused SwiGLU, grouped GEMM down, and the top-k weighted
+ * combine.  The pages do not spell the expert FFN out; SwiGLU is the reading
+ * taken here.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named "device" point to GPU memory of the handle's device; the
+ *    library never copies them to the host.  Rows are row-major, contiguous.
+ *  - Every call returns an afd_status; nothing is thrown across the ABI.
+ *    Argument and shape errors are found on the host before any GPU work;
+ *    afd_ffn_last_error() then holds a message for the calling thread.
+ *  - Work is enqueued asynchronously on the `stream` argument (a hipStream_t
+ *    passed as void*; NULL = the device's null stream) and never synchronised
+ *    by the library, except where an entry point says otherwise.
+ *  - A handle may be used by one stream at a time: its workspace is reused
+ *    by every forward.  Use afd_ffn_clone for a second concurrent stream.
+ *  - The library must be loaded into a process whose HIP runtime is the one
+ *    the caller allocates with (e.g. after `import torch` on ROCm).
+ */
+#ifndef AFD_FFN_H
+#define AFD_FFN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct afd_ffn afd_ffn_t; /* opaque handle */
+
+typedef enum {
+    AFD_OK = 0,
+    AFD_ERR_INVALID_ARG = 1,   /* NULL pointer, bad size, T > max_tokens ...   */
+    AFD_ERR_UNSUPPORTED = 2,   /* shape or dtype this build does not handle      */
+    AFD_ERR_OUT_OF_MEMORY = 3, /* device allocation failed in create / clone     */
+    AFD_ERR_HIP = 4,           /* a HIP runtime call failed (message has it)     */
+    AFD_ERR_BAD_ROUTING = 5    /* ids outside [-1, E) were seen (error query)    */
+} afd_status;
+
+typedef enum {
+    AFD_DTYPE_F32 = 0,       /* fp32 activations, weights and output            */
+    AFD_DTYPE_BF16 = 1,      /* bf16 activations, weights and output            */
+    AFD_DTYPE_FP8_BLOCK = 2  /* OCP E4M3FN codes with fp32 scales: activations
+                                per 1x128 group along H, weights per 128x128
+                                block; output bf16 ("block-FP8" experts and FP8
+                                tokens, FastAFD System Design items 1-2)        */
+} afd_dtype;
+
+/*
+ * Layer description for afd_ffn_create.  H = hidden, I = inter,
+ * E = num_experts (experts on this GPU), K = top_k.
+ *
+ * Weights (device, read only during afd_ffn_create, which copies and
+ * re-lays them out into library-owned memory; the caller may free them as
+ * soon as create returns):
+ *   w_gate, w_up  [E, H, I]   element type per dtype (fp32 | bf16 | e4m3 code)
+ *   w_down        [E, I, H]
+ *   s_gate, s_up  [E, H/128, I/128] fp32   (AFD_DTYPE_FP8_BLOCK only, else NULL)
+ *   s_down        [E, I/128, H/128] fp32   (AFD_DTYPE_FP8_BLOCK only, else NULL)
+ * Optional shared expert (shared_inter > 0; applied to every token with
+ * weight 1 after the routed sum; shared_inter must equal inter):
+ *   sh_gate, sh_up [H, shared_inter], sh_down [shared_inter, H], and for FP8
+ *   sh_s_gate, sh_s_up [H/128, shared_inter/128], sh_s_down [shared_inter/128, H/128].
+ *
+ * Limits: 1 <= E <= 512, 1 <= K <= 32, 1 <= max_tokens, max_tokens*K < 2^26;
+ * H and I multiples of 128 for every dtype.
+ */
+typedef struct {
+    int32_t hidden;        /* H                                                */
+    int32_t inter;         /* I                                                */
+    int32_t num_experts;   /* E                                                */
+    int32_t top_k;         /* K                                                */
+    int32_t max_tokens;    /* largest T any forward will pass                  */
+    int32_t shared_inter;  /* 0 = no shared expert                             */
+    int32_t dtype;         /* afd_dtype                                        */
+    int32_t device;        /* HIP device ordinal the handle lives on           */
+    const void *w_gate, *w_up, *w_down;
+    const float *s_gate, *s_up, *s_down;
+    const void *sh_gate, *sh_up, *sh_down;
+    const float *sh_s_gate, *sh_s_up, *sh_s_down;
+} afd_ffn_config;
+
+/* Host-only check of a configuration: the same checks afd_ffn_create makes
+ * before touching the GPU (no HIP call is made). */
+afd_status afd_ffn_validate_config(const afd_ffn_config *cfg);
+
+/* Create a handle: validates `cfg`, allocates library-owned device memory
+ * for the re-laid-out weights and a workspace sized for max_tokens, and packs
+ * the weights (synchronously, on the device's null stream).  On success
+ * *out_handle owns all of it; on failure nothing is leaked and *out_handle is
+ * set to NULL. */
+afd_status afd_ffn_create(const afd_ffn_config *cfg, afd_ffn_t **out_handle);
+
+/* A second handle sharing src's packed weights (reference counted) with a
+ * workspace of its own, so two microbatches can run on two streams at once
+ * (FastAFD System Design item 4: two ping-pong microbatches). */
+afd_status afd_ffn_clone(const afd_ffn_t *src, afd_ffn_t **out_handle);
+
+/*
+ * One layer forward for T = num_tokens tokens (0 <= T <= max_tokens):
+ *   hidden         device [T, H]: fp32 | bf16 | e4m3 codes (per dtype)
+ *   hidden_scales  device [T, H/128] fp32 for AFD_DTYPE_FP8_BLOCK, else NULL
+ *   topk_ids       device [T, K] int32; each in [0, E) or -1 ("expert not on
+ *                  this GPU": contributes nothing).  Duplicate ids in a row
+ *                  are separate assignments.  Ids outside [-1, E) are treated
+ *                  as -1 and counted (see afd_ffn_routing_errors).
+ *   topk_weights   device [T, K] fp32, used exactly as given
+ *   out            device [T, H]: fp32 for AFD_DTYPE_F32, else bf16; every
+ *                  element is written (rows with no local expert and no shared
+ *                  expert are 0).  Must not alias the inputs.
+ * Asynchronous on `stream`; inputs and out must stay valid until the stream
+ * work completes.  The dispatch (counts, offsets, permutation) of this call
+ * stays in the handle's workspace until the next forward on the handle.
+ */
+afd_status afd_ffn_forward(afd_ffn_t *handle, int32_t num_tokens, const void *hidden,
+                           const float *hidden_scales, const int32_t *topk_ids,
+                           const float *topk_weights, void *out, void *stream);
+
+/* Release a handle (NULL is accepted).  Packed weights are freed when their
+ * last sharer is destroyed.  Call only after the handle's stream work has
+ * completed. */
+afd_status afd_ffn_destroy(afd_ffn_t *handle);
+
+/* Static text for a status code. */
+const char *afd_ffn_status_string(afd_status status);
+
+/* Message of the last failed call on the calling thread ("" if none). */
+const char *afd_ffn_last_error(void);
+
+/*
+ * Copy the dispatch of the last forward into caller device buffers
+ * (asynchronous on `stream`; any pointer may be NULL to skip it):
+ *   counts        [E]      assignments per expert
+ *   offsets       [E+1]    exclusive prefix sums, offsets[E] = N
+ *   sorted_assign [N]      flat slot indices t*K+k, expert by expert, each
+ *                          expert's in ascending flat order
+ *   row_of        [T, K]   position of slot (t,k) in sorted_assign, -1 if none
+ * N = number of slots with a valid id; the caller sizes sorted_assign for T*K.
+ */
+afd_status afd_ffn_debug_dispatch(afd_ffn_t *handle, int32_t *counts, int32_t *offsets,
+                                  int32_t *sorted_assign, int32_t *row_of, void *stream);
+
+/* Number of ids outside [-1, E) seen by the last forward (synchronises the
+ * stream; *count is host memory).  Returns AFD_ERR_BAD_ROUTING if > 0. */
+afd_status afd_ffn_routing_errors(afd_ffn_t *handle, int32_t *count, void *stream);
+
+/*
+ * Per-kernel timing of forwards, for measurement.  When enabled, forward
+ * records HIP events on its stream around each of its kernels; the query
+ * synchronises on the last event and returns, per stage, the summed time in
+ * milliseconds and the number of forwards since the last reset, then resets.
+ * Stages: 0 dispatch count+scan, 1 dispatch scatter, 2 grouped GEMM
+ * gate/up + SwiGLU, 3 grouped GEMM down, 4 combine.  ms must hold
+ * AFD_NUM_STAGES floats.
+ */
+#define AFD_NUM_STAGES 5
+afd_status afd_ffn_set_timing(afd_ffn_t *handle, int32_t enable);
+afd_status afd_ffn_get_timing(afd_ffn_t *handle, float *ms, int32_t *num_forwards);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AFD_FFN_H */

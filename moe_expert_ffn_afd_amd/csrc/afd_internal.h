@@ -1,0 +1,141 @@
+// afd_internal.h -- shared definitions of the HIP kernels and the host API.
+//
+// Data layout in HBM (all owned by the library):
+//
+//  Packed expert weights, "panel-major fragment" order.  A panel is 32 output
+//  columns of one weight matrix over its whole reduction length K, cut into
+//  super-steps of 128 bytes of K (64 bf16 or 128 e4m3 elements).  One
+//  super-step of one panel is 4 KiB laid out exactly as four 1 KiB MFMA
+//  operand loads of a 64-lane wave: lane l holds column n = l % 32 and the
+//  64 contiguous bytes of K that start at byte 64 * (l / 32) of the super-step.
+//  Load j (0..3) of lane l is bytes [16 j, 16 j + 16) of that run, so each
+//  load instruction of a wave reads 1 KiB of contiguous memory.
+//    bf16: load j = MFMA 32x32x16 number j; element e of the load is
+//          k = 64 c + 32 g + 8 j + e   (c = super-step, g = l / 32)
+//    e4m3: loads (2i, 2i+1) = the 32-byte operand of MFMA 32x32x64 number i;
+//          byte b of that operand is k = 128 c + 64 g + 32 i + b
+//  Activation rows ([rows, K] row-major) are read with the same k mapping, so
+//  A and B operands agree lane by lane (the MFMA sums over whatever k each
+//  (lane group, element) pair carries, as long as both operands carry the same).
+//
+//  Gate/up weights of one expert are one buffer of 2 I / 32 panels with gate
+//  panel p at index 2p and up panel p at 2p + 1 (a wave streams both with one
+//  base pointer and finds gate and up of the same h column in the same
+//  accumulator register).  Down weights of one expert are H / 32 panels.
+//  The shared expert, if any, is stored as expert index E.
+//
+//  Block-FP8 scales: gate [E+S][H/128][I/128], up likewise, down
+//  [E+S][I/128][H/128] (fp32, copies of the caller's); one super-step is one
+//  128-deep scale block and one panel lies inside one 128-column block.
+//
+//  Workspace (per handle, sized for max_tokens T_max; N_max = T_max * K):
+//    counts[E], offsets[E+1], err[1], num_mtiles[1]
+//    chunk_base[n_chunks][E]          first sorted row of each (chunk, expert)
+//    sorted_assign[N_max], row_of[N_max]
+//    mtiles[max_mtiles] (int4)        {expert, first row, rows, 0}
+//    h   [N_max + T_max, I]           routed rows in sorted order, then the
+//                                     shared expert's rows (token order) at
+//                                     row N_max; bf16 | e4m3 (+ scales
+//                                     [rows, I/128] fp32) | fp32
+//    y   [N_max + T_max, H]           expert outputs (unweighted), same rows;
+//                                     bf16 | fp32
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace afd {
+
+enum Dtype : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+constexpr int kPanelCols = 32;         // output columns per panel
+constexpr int kStepBytes = 128;        // bytes of K per super-step and row
+constexpr int kStepPanelBytes = 4096;  // one super-step of one panel
+constexpr int kWaves = 4;              // waves per GEMM workgroup
+constexpr int kDispatchThreads = 1024;
+constexpr int kDispatchLdsInts = 12288;  // chunk x expert counters held in LDS (48 KiB)
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 32;
+
+struct DispatchParams {
+  const int32_t* ids;      // [n_flat]
+  int32_t n_flat;          // T * K
+  int32_t num_experts;     // E
+  int32_t chunk_shift;     // chunk = 1 << chunk_shift flat slots (>= 10)
+  int32_t n_chunks;
+  int32_t* counts;         // [E]
+  int32_t* offsets;        // [E+1]
+  int32_t* chunk_base;     // [n_chunks][E]
+  int32_t* err;            // [1] ids outside [-1, E)
+  int32_t* sorted_assign;  // [n_flat]
+  int32_t* row_of;         // [n_flat]
+  int32_t bm;              // rows per routed m-tile
+  int32_t shared_rows;     // T when a shared expert exists, else 0
+  int32_t shared_row0;     // first shared row (N_max)
+  int4* mtiles;            // tile list
+  int32_t* num_mtiles;     // [1]
+};
+
+struct GemmParams {
+  const int4* mtiles;
+  const int32_t* num_mtiles;
+  const int32_t* sorted_assign;  // row -> flat slot (gate/up gather)
+  int32_t top_k;
+  int32_t shared_row0;           // rows >= this are shared-expert rows (token = row - shared_row0)
+  int32_t gather;                // 1: A row = hidden[token of row]; 0: A row = a[row]
+  const uint8_t* a;              // activation rows
+  int64_t a_row_bytes;
+  const float* a_scales;         // fp8: [rows, K/128]
+  int32_t a_scale_ld;
+  const uint8_t* b;              // packed weights
+  int64_t b_expert_bytes;
+  int64_t b_panel_bytes;
+  const float* b_scales0;        // fp8: gate (gate/up) or down scales
+  const float* b_scales1;        // fp8: up scales (gate/up only)
+  int32_t b_scale_rows;          // K / 128
+  int32_t b_scale_cols;          // N / 128 of one matrix
+  int32_t k_steps;               // K / super-step
+  int32_t n_groups;              // workgroup tasks per m-tile along N
+  int32_t n_panels;              // panels of one output matrix (I/32 or H/32)
+  uint8_t* c;                    // output rows
+  int64_t c_row_bytes;
+  float* c_scales;               // fp8 gate/up: h scales [rows, I/128]
+  int32_t c_scale_ld;
+};
+
+struct CombineParams {
+  const uint8_t* y;        // [rows, H] bf16 | f32
+  const int32_t* row_of;   // [T, K]
+  const float* weights;    // [T, K]
+  int32_t top_k;
+  int32_t hidden;
+  int32_t shared_row0;     // -1 when no shared expert
+  uint8_t* out;            // [T, H]
+};
+
+struct F32Params {
+  const int4* mtiles;
+  const int32_t* num_mtiles;
+  const int32_t* sorted_assign;
+  int32_t top_k;
+  int32_t shared_row0;
+  int32_t gather;
+  const float* a;           // [*, K] rows
+  const float* w0;          // gate (gate/up) or down: [E+S][K][N]
+  const float* w1;          // up
+  int32_t kdim, ndim;
+  float* c;                 // [rows, N]
+};
+
+// launchers (return hipError_t of the launch)
+hipError_t launch_dispatch_count_scan(const DispatchParams& p, hipStream_t s);
+hipError_t launch_dispatch_scatter(const DispatchParams& p, hipStream_t s);
+hipError_t launch_gemm(int dtype, bool gate_up, int mr, const GemmParams& p, int grid,
+                       hipStream_t s);
+hipError_t launch_gemm_f32(bool gate_up, const F32Params& p, int grid, hipStream_t s);
+hipError_t launch_combine(int dtype, const CombineParams& p, int tokens, hipStream_t s);
+hipError_t launch_pack(int dtype, bool gate_up, const void* w_first, const void* w_second,
+                       int64_t expert_in_stride_elems, int experts, int kdim, int ndim,
+                       uint8_t* dst, int64_t dst_expert_bytes, hipStream_t s);
+
+}  // namespace afd

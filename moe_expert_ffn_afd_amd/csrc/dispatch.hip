@@ -1,0 +1,201 @@
+// dispatch.hip -- expert dispatch of the routed (token, slot) assignments.
+//
+// The FFN side receives tokens with their top-k expert ids and must group the
+// assignments by expert for the grouped GEMMs ("FastAFD" structured summary,
+// legend of Eq. (3): the FFN stage covers dispatch of the routed tokens and
+// the grouped GEMM over them).  The grouping is the stable counting sort of
+// the flat slots f = t*K + k by expert id:
+//   counts[e]            = #{f : ids[f] == e}
+//   offsets[e]           = sum_{e' < e} counts[e'],  offsets[E] = N
+//   sorted_assign[r]     = the flat slots of expert 0, then expert 1, ...,
+//                          each expert's in ascending f
+//   row_of[f]            = r with sorted_assign[r] == f, or -1
+// Being a pure function of the ids, it is reproduced bit for bit.
+//
+// Two kernels.  count_scan (one workgroup): per-(chunk, expert) counts with
+// LDS atomics (counts do not depend on order), per-expert prefix over chunks,
+// exclusive scan over experts, first sorted row of every (chunk, expert), and
+// the GEMM m-tile list.  scatter (one workgroup per chunk): each wave ranks its
+// 64 slots among equal ids with ballots over the id bits (match mask, popcount
+// of the lower lanes), waves are ordered through per-wave counts in LDS, and
+// rounds of 1024 slots advance per-expert cursors, so every slot lands at its
+// stable position with no order-dependent atomics.
+#include "afd_internal.h"
+
+namespace afd {
+
+namespace {
+
+__device__ inline int block_exclusive_scan_1024(int v, int* lds_waves, int* total) {
+  // 1024 threads = 16 waves of 64.
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) lds_waves[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < 16 ? lds_waves[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      int y = __shfl_up(w, d, 64);
+      if (lane >= d) w += y;
+    }
+    if (lane < 16) lds_waves[16 + lane] = w;  // inclusive wave sums
+  }
+  __syncthreads();
+  int base = wave > 0 ? lds_waves[16 + wave - 1] : 0;
+  *total = lds_waves[16 + 15];
+  int r = base + x - v;
+  __syncthreads();  // lds_waves may be reused by the caller
+  return r;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(DispatchParams p) {
+  extern __shared__ int cc[];  // [n_chunks][E] counts, then chunk-local prefixes
+  __shared__ int total[kMaxExperts];
+  __shared__ int excl[kMaxExperts];
+  __shared__ int scan_tmp[32];
+  __shared__ int bad;
+  const int E = p.num_experts;
+  const int tid = threadIdx.x;
+  const int ncc = p.n_chunks * E;
+
+  for (int i = tid; i < ncc; i += kDispatchThreads) cc[i] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+
+  for (int f = tid; f < p.n_flat; f += kDispatchThreads) {
+    int e = p.ids[f];
+    if (e >= 0 && e < E)
+      atomicAdd(&cc[(f >> p.chunk_shift) * E + e], 1);
+    else if (e != -1)
+      atomicAdd(&bad, 1);
+  }
+  __syncthreads();
+
+  // per expert: chunk-local exclusive prefix over chunks, total count
+  for (int e = tid; e < E; e += kDispatchThreads) {
+    int run = 0;
+    for (int c = 0; c < p.n_chunks; ++c) {
+      int v = cc[c * E + e];
+      cc[c * E + e] = run;
+      run += v;
+    }
+    total[e] = run;
+  }
+  __syncthreads();
+
+  // exclusive scan over experts (E <= 1024: one expert per thread)
+  int n_routed = 0;
+  {
+    int v = tid < E ? total[tid] : 0;
+    int x = block_exclusive_scan_1024(v, scan_tmp, &n_routed);
+    if (tid < E) {
+      excl[tid] = x;
+      p.counts[tid] = v;
+      p.offsets[tid] = x;
+    }
+    if (tid == 0) {
+      p.offsets[E] = n_routed;
+      p.err[0] = bad;
+    }
+  }
+  __syncthreads();
+
+  for (int i = tid; i < ncc; i += kDispatchThreads) p.chunk_base[i] = excl[i % E] + cc[i];
+
+  // m-tile list: routed experts in expert order, then the shared expert
+  {
+    int v = tid < E ? (total[tid] + p.bm - 1) / p.bm : 0;
+    int n_tiles = 0;
+    int toff = block_exclusive_scan_1024(v, scan_tmp, &n_tiles);
+    if (tid < E) {
+      for (int j = 0; j < v; ++j) {
+        int r0 = j * p.bm;
+        int rows = min(p.bm, total[tid] - r0);
+        p.mtiles[toff + j] = make_int4(tid, excl[tid] + r0, rows, 0);
+      }
+    }
+    int n_shared = (p.shared_rows + p.bm - 1) / p.bm;
+    for (int j = tid; j < n_shared; j += kDispatchThreads) {
+      int r0 = j * p.bm;
+      p.mtiles[n_tiles + j] = make_int4(E, p.shared_row0 + r0, min(p.bm, p.shared_rows - r0), 0);
+    }
+    if (tid == 0) p.num_mtiles[0] = n_tiles + n_shared;
+  }
+}
+
+__global__ __launch_bounds__(kDispatchThreads) void dispatch_scatter_kernel(DispatchParams p) {
+  extern __shared__ int lds[];
+  const int E = p.num_experts;
+  int* cursor = lds;          // [E]
+  int* wcnt = lds + E;        // [16][E] per-wave counts of the current round
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int chunk = blockIdx.x;
+  const int chunk_len = 1 << p.chunk_shift;
+  const int f0 = chunk * chunk_len;
+  const int f_end = min(f0 + chunk_len, p.n_flat);
+
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  for (int e = tid; e < E; e += kDispatchThreads) cursor[e] = p.chunk_base[chunk * E + e];
+  for (int i = tid; i < 16 * E; i += kDispatchThreads) wcnt[i] = 0;
+  __syncthreads();
+
+  for (int base = f0; base < f_end; base += kDispatchThreads) {
+    const int f = base + tid;
+    const int e = f < f_end ? p.ids[f] : -1;
+    const bool valid = e >= 0 && e < E;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      match &= bit ? m : ~m;
+    }
+    const int rank = __popcll(match & lt_mask);
+    if (valid && rank == 0) wcnt[wave * E + e] = __popcll(match);
+    __syncthreads();
+    if (valid) {
+      int prefix = 0;
+      for (int w = 0; w < wave; ++w) prefix += wcnt[w * E + e];
+      const int pos = cursor[e] + prefix + rank;
+      p.sorted_assign[pos] = f;
+      p.row_of[f] = pos;
+    } else if (f < f_end) {
+      p.row_of[f] = -1;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += kDispatchThreads) {
+      int s = 0;
+      for (int w = 0; w < 16; ++w) s += wcnt[w * E + x];
+      cursor[x] += s;
+    }
+    __syncthreads();
+    if (valid && rank == 0) wcnt[wave * E + e] = 0;
+    __syncthreads();
+  }
+}
+
+hipError_t launch_dispatch_count_scan(const DispatchParams& p, hipStream_t s) {
+  size_t lds = sizeof(int) * (size_t)p.n_chunks * p.num_experts;
+  hipLaunchKernelGGL(dispatch_count_scan_kernel, dim3(1), dim3(kDispatchThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_scatter(const DispatchParams& p, hipStream_t s) {
+  if (p.n_chunks == 0) return hipSuccess;
+  size_t lds = sizeof(int) * (size_t)17 * p.num_experts;
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(p.n_chunks), dim3(kDispatchThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace afd

@@ -1,0 +1,152 @@
+"""Edge cases and invariants of the HIP layer on the GPU (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import check_dispatch, compare, oracle_out, problem, run_layer, say, to_host_problem
+from moe_expert_ffn_afd_amd import afd
+
+pytestmark = pytest.mark.gpu
+
+
+def cfg(dtype="bf16", T=64, H=256, I=256, E=8, K=2, shared=0):
+    return dict(dtype=dtype, T=T, H=H, I=I, E=E, K=K, routing="uniform", shared_inter=shared)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_adversarial_routing(dtype):
+    """All tokens on one expert (many m-tiles), duplicate ids, -1 slots, nothing local."""
+    T, E, K = 130, 6, 3
+    rng = np.random.default_rng(1)
+    cases = {
+        "one_hot_expert": np.full((T, K), 4, np.int32),
+        "duplicates_and_minus1": rng.choice(np.array([-1, 0, 0, 2, 5], np.int32), size=(T, K)).astype(np.int32),
+        "nothing_local": np.full((T, K), -1, np.int32),
+    }
+    for name, ids in cases.items():
+        say("case", dtype, name)
+        w = rng.uniform(0.0, 1.0, size=(T, K)).astype(np.float32)
+        p = problem(cfg(dtype, T=T, E=E, K=K), seed=3, routing=(ids, w))
+        layer, out = run_layer(p)
+        check_dispatch(layer, p)
+        ref = oracle_out(to_host_problem(p))
+        if name == "nothing_local":
+            assert torch.all(out == 0)
+        else:
+            compare(out, ref, dtype, what=name)
+        layer.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_empty_and_tiny_batches(dtype):
+    p = problem(cfg(dtype, T=40, shared=256 if dtype == "fp8" else 0), seed=2)
+    layer = afd.Layer(p, max_tokens=40)
+    for T in (0, 1, 2, 40):
+        say("case", dtype, "T =", T)
+        q = {k: v for k, v in p.items()}
+        for k in ("hidden", "hidden_scales", "ids", "weights"):
+            if q[k] is not None:
+                q[k] = p[k][:T].contiguous()
+        q["T"] = T
+        out = layer.forward(q["hidden"], q["hidden_scales"], q["ids"], q["weights"])
+        torch.cuda.synchronize()
+        assert out.shape == (T, 256)
+        if T:
+            check_dispatch(layer, q)
+            compare(out, oracle_out(to_host_problem(q)), dtype, what="T=%d" % T)
+    layer.close()
+
+
+def test_unused_experts_poisoned_with_nan():
+    T, E, K = 50, 8, 2
+    rng = np.random.default_rng(4)
+    ids = rng.choice(np.array([1, 3, 6], np.int32), size=(T, K)).astype(np.int32)
+    w = rng.uniform(0.1, 1.0, size=(T, K)).astype(np.float32)
+    p = problem(cfg("bf16", T=T, E=E, K=K), seed=5, routing=(ids, w))
+    _, base = run_layer(p)
+    for name in ("w_gate", "w_up", "w_down"):
+        t = p[name].clone()
+        for e in (0, 2, 4, 5, 7):
+            t[e] = float("nan")
+        p[name] = t
+    layer, out = run_layer(p)
+    assert torch.all(torch.isfinite(out.float()))
+    assert torch.equal(out, base)
+    layer.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_deterministic_and_permutation_equivariant(dtype):
+    p = problem(cfg(dtype, T=96, E=8, K=2, shared=256 if dtype == "fp8" else 0), seed=6)
+    layer, a = run_layer(p)
+    b = layer.forward(p["hidden"], p["hidden_scales"], p["ids"], p["weights"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "run twice differs"
+    perm = torch.from_numpy(np.random.default_rng(0).permutation(96)).cuda()
+    q = dict(p)
+    for k in ("hidden", "hidden_scales", "ids", "weights"):
+        if q[k] is not None:
+            q[k] = p[k][perm].contiguous()
+    c = layer.forward(q["hidden"], q["hidden_scales"], q["ids"], q["weights"])
+    torch.cuda.synchronize()
+    assert torch.equal(c, a[perm]), "token permutation is not equivariant"
+    layer.close()
+
+
+def test_identical_experts_equal_dense_ffn():
+    T, E, K = 64, 6, 3
+    p = problem(cfg("bf16", T=T, E=E, K=K), seed=7)
+    for name in ("w_gate", "w_up", "w_down"):
+        p[name] = p[name][:1].expand_as(p[name]).contiguous()
+    layer, out = run_layer(p)
+    x = p["hidden"].double().cpu()
+    wg, wu, wd = (p[n][0].double().cpu() for n in ("w_gate", "w_up", "w_down"))
+    dense = ((torch.nn.functional.silu(x @ wg) * (x @ wu)) @ wd) * p["weights"].double().cpu().sum(1, keepdim=True)
+    compare(out, dense.numpy(), "bf16", what="identical experts")
+    layer.close()
+
+
+def test_out_of_range_ids_are_counted_and_ignored():
+    T, E, K = 20, 4, 2
+    ids = np.zeros((T, K), np.int32)
+    ids[3, 1] = 9
+    ids[5, 0] = -5
+    w = np.ones((T, K), np.float32) * 0.5
+    p = problem(cfg("bf16", T=T, E=E, K=K), seed=8, routing=(ids, w))
+    layer, out = run_layer(p)
+    assert afd.afd_ffn_routing_errors(layer.handle) == 2
+    ids2 = ids.copy()
+    ids2[3, 1] = -1
+    ids2[5, 0] = -1
+    q = dict(p)
+    q["ids"] = torch.from_numpy(ids2).cuda()
+    _, ref = run_layer(q)
+    assert torch.equal(out, ref)
+    layer.close()
+
+
+def test_forward_rejects_bad_shapes_on_host():
+    p = problem(cfg("bf16", T=16), seed=9)
+    layer = afd.Layer(p, max_tokens=16)
+    with pytest.raises(ValueError):
+        layer.forward(p["hidden"][:, :128].contiguous(), None, p["ids"], p["weights"])
+    with pytest.raises(ValueError):
+        layer.forward(p["hidden"], None, p["ids"].long(), p["weights"])
+    big = torch.zeros((17, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        layer.forward(big, None, torch.zeros((17, 2), dtype=torch.int32, device="cuda"),
+                      torch.zeros((17, 2), device="cuda"))
+    st = afd.load().afd_ffn_forward(layer.handle, 17, None, None, None, None, None, None)
+    assert st == afd.AFD_ERR_INVALID_ARG
+    layer.close()
+
+
+def test_timing_records_every_stage():
+    p = problem(cfg("bf16", T=64), seed=10)
+    layer = afd.Layer(p)
+    afd.afd_ffn_set_timing(layer.handle, True)
+    for _ in range(3):
+        layer.forward(p["hidden"], None, p["ids"], p["weights"])
+    ms, n = afd.afd_ffn_get_timing(layer.handle)
+    assert n == 3 and all(t > 0 for t in ms), ms
+    layer.close()

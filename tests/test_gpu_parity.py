@@ -1,0 +1,101 @@
+"""HIP layer vs the fp64 oracle, through the C ABI (needs an MI355X).
+
+Dispatch (counts, offsets, permutation, row map) must match bit for bit;
+outputs within max|err| <= tol * max|ref| (bf16 2e-2, block-FP8 6e-2, fp32
+1e-5).  Small cases run the whole batch through the oracle; the full-size
+workloads compare a seeded sample of tokens (the oracle computes tokens
+independently) plus the full dispatch.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import TOL, check_dispatch, compare, oracle_out, problem, run_layer, say, to_host_problem
+from moe_expert_ffn_afd_amd import afd, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def small(dtype, T, H, I, E, K, routing="uniform", shared=0, global_experts=None):
+    return dict(dtype=dtype, T=T, H=H, I=I, E=E, K=K, routing=routing, shared_inter=shared,
+                global_experts=global_experts)
+
+
+SMALL_CASES = {
+    # name: (cfg, seed)
+    "f32_tiny_full": (inputs.workload("tiny"), 0),
+    "f32_ragged_shared": (small("f32", 45, 256, 384, 5, 3, shared=384), 1),
+    "bf16_mr1_ragged": (small("bf16", 37, 256, 384, 16, 2), 2),
+    "bf16_mr2_multi_tile": (small("bf16", 150, 512, 384, 6, 3), 3),
+    "bf16_zipf_empty_experts": (small("bf16", 300, 256, 256, 16, 4, routing="zipf"), 4),
+    "fp8_mr1": (small("fp8", 33, 512, 256, 16, 2), 5),
+    "fp8_shared_multi_tile": (small("fp8", 70, 512, 384, 5, 3, shared=384), 6),
+    "fp8_local_shard": (small("fp8", 200, 256, 384, 4, 8, routing="local_shard", global_experts=32), 7),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_CASES))
+def test_small_full_batch(name):
+    cfg, seed = SMALL_CASES[name]
+    say("case", name, cfg, "seed", seed)
+    p = problem(cfg, seed)
+    layer, out = run_layer(p)
+    check_dispatch(layer, p)
+    ref = oracle_out(to_host_problem(p))
+    compare(out, ref, cfg["dtype"], what=name)
+    layer.close()
+
+
+FULL = ["tiny", "decode", "aggregated", "fp8_shared"]
+SAMPLES = {"tiny": None, "decode": 48, "aggregated": 40, "fp8_shared": 12}
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(name):
+    cfg = inputs.workload(name)
+    say("workload", name, inputs.WORKLOAD_TITLES[name])
+    p = problem(cfg, 0)
+    layer, out = run_layer(p)
+    check_dispatch(layer, p)
+    n = SAMPLES[name]
+    tokens = None if n is None else np.sort(np.random.default_rng(123).choice(cfg["T"], n, replace=False))
+    ref = oracle_out(to_host_problem(p), tokens)
+    compare(out, ref, cfg["dtype"], tokens=tokens, what=name)
+    # rows with no local expert and no shared expert are exactly zero
+    ids = p["ids"].cpu().numpy()
+    empty = np.where((ids < 0).all(axis=1))[0]
+    if len(empty) and not cfg.get("shared_inter"):
+        assert torch.all(out[torch.from_numpy(empty).cuda()] == 0)
+    layer.close()
+
+
+def test_verify_shard_two_streams_ping_pong():
+    """Two microbatches of 2048 on two streams (clone shares weights) equal the
+    one-call result bit for bit, and match the oracle on sampled tokens."""
+    cfg = inputs.workload("verify_shard")
+    say("workload verify_shard", inputs.WORKLOAD_TITLES["verify_shard"])
+    p = problem(cfg, 0)
+    T = cfg["T"]
+    half = T // 2
+    l0 = afd.Layer(p, max_tokens=T)
+    l1 = l0.clone()
+    single = l0.forward(p["hidden"], p["hidden_scales"], p["ids"], p["weights"])
+    torch.cuda.synchronize()
+    mbs = [inputs.slice_tokens(p, 0, half), inputs.slice_tokens(p, half, T)]
+    s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = [l0.out_like(half), l1.out_like(half)]
+    torch.cuda.synchronize()
+    for layer, mb, st, o in ((l0, mbs[0], s0, outs[0]), (l1, mbs[1], s1, outs[1])):
+        with torch.cuda.stream(st):
+            layer.forward(mb["hidden"], mb["hidden_scales"], mb["ids"], mb["weights"], out=o, stream=st)
+    torch.cuda.synchronize()
+    pp = torch.cat(outs)
+    assert torch.equal(pp, single), "ping-pong microbatches differ from the single call"
+    local = (p["ids"] >= 0).float().mean().item()
+    say("  local hit fraction %.3f" % local)
+    tokens = np.sort(np.random.default_rng(5).choice(T, 12, replace=False))
+    ref = oracle_out(to_host_problem(p), tokens)
+    compare(single, ref, "fp8", tokens=tokens, what="verify_shard")
+    check_dispatch(l1, mbs[1])
+    l1.close()
+    l0.close()

@@ -1,0 +1,245 @@
+"""Benchmark of the FFN-side MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+A step is one forward of the whole layer (dispatch count+scan, scatter,
+grouped GEMM gate/up + SwiGLU, grouped GEMM down, combine) over one batch of
+seeded synthetic tokens already resident in HBM; the verify_shard workload
+runs its two microbatches on two streams per step.  Prints one JSON line with
+routed tokens/s, the roofline of the dominant kernel (timed with HIP events
+on its own stream inside the timed region) and the oracle's CPU baseline.
+
+Other modes: --copy-calibration runs a plain device copy of known size (the
+reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters);
+--no-cpu-baseline skips the oracle timing.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}
+METRIC = "routed tokens/s per MoE layer on 1 MI355X; % of MFMA/HBM roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("gemm.hip",)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "moe_expert_ffn_afd_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_units(cfg: dict, ids) -> dict:
+    """Bytes and flops each kernel must move / do at minimum for this routing."""
+    import numpy as np
+
+    T, H, I, E, K = cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["K"]
+    dt = cfg["dtype"]
+    bw = {"f32": 4, "bf16": 2, "fp8": 1}[dt]
+    by = 4 if dt == "f32" else 2
+    S = 1 if cfg.get("shared_inter") else 0
+    ids = np.asarray(ids)
+    counts = np.bincount(ids[ids >= 0].reshape(-1), minlength=E)
+    N = int(counts.sum())
+    Ns = N + S * T
+    ne = int((counts > 0).sum()) + S
+    sc = 4.0 / (128 * 128) if dt == "fp8" else 0.0          # weight block scales per weight
+    xs = 4.0 / 128 if dt == "fp8" else 0.0                  # activation scales per element
+    gu_bytes = ne * 2 * H * I * (bw + sc) + T * H * (bw + xs) + Ns * I * (bw + xs)
+    dn_bytes = ne * I * H * (bw + sc) + Ns * I * (bw + xs) + Ns * H * by
+    layer_bytes = ne * 3 * H * I * (bw + sc) + T * H * (bw + xs) + T * H * by + T * K * 8
+    return dict(N=N, Ns=Ns, nonempty=ne, gu_bytes=gu_bytes, dn_bytes=dn_bytes, layer_bytes=layer_bytes,
+                gu_flops=4.0 * H * I * Ns, dn_flops=2.0 * H * I * Ns, layer_flops=6.0 * H * I * Ns)
+
+
+def cpu_baseline(p: dict, cfg: dict, budget_s: float = 12.0) -> dict:
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same batch."""
+    import numpy as np
+    import torch
+
+    from oracle import oracle as orc
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    host = {k: (v.detach().cpu() if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+    T = cfg["T"]
+    n = min(T, cores)
+    t0 = time.perf_counter()
+    orc.forward(host, tokens=np.arange(n, dtype=np.int32), nthreads=cores)
+    t1 = time.perf_counter() - t0
+    total_t, total_n = t1, n
+    if t1 < budget_s and n < T:
+        n2 = int(min(T - n, max(cores, (budget_s - t1) / max(t1, 1e-3) * n)))
+        n2 = max(cores, n2 // cores * cores) if n2 >= cores else n2
+        t0 = time.perf_counter()
+        orc.forward(host, tokens=np.arange(n, n + n2, dtype=np.int32), nthreads=cores)
+        total_t += time.perf_counter() - t0
+        total_n += n2
+    return {"value": total_n / total_t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "first %d of the %d tokens of the same seeded batch, fp64, %.1f s" % (total_n, T, total_t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode",
+                    choices=["tiny", "decode", "aggregated", "fp8_shared", "verify_shard"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer is built for one MI355X; "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        return
+
+    from moe_expert_ffn_afd_amd import afd, inputs
+
+    cfg = inputs.workload(args.workload)
+    p = inputs.make_problem(cfg, seed=args.seed, device="cuda")
+    T = cfg["T"]
+    units = algorithmic_units(cfg, p["ids"].cpu().numpy())
+    mbs = cfg.get("microbatches", 1)
+
+    layers = [afd.Layer(p, max_tokens=T // mbs)]
+    while len(layers) < mbs:
+        layers.append(layers[0].clone())
+    if mbs == 1:
+        parts = [p]
+        streams = [torch.cuda.current_stream()]
+    else:
+        step = T // mbs
+        parts = [inputs.slice_tokens(p, i * step, (i + 1) * step) for i in range(mbs)]
+        streams = [torch.cuda.Stream() for _ in range(mbs)]
+    outs = [layers[i].out_like(parts[i]["T"]) for i in range(mbs)]
+
+    main_stream = torch.cuda.current_stream()
+
+    def step_fn():
+        if mbs == 1:
+            layers[0].forward(p["hidden"], p["hidden_scales"], p["ids"], p["weights"], out=outs[0],
+                              stream=main_stream)
+            return
+        ev = torch.cuda.Event()
+        ev.record(main_stream)
+        for i in range(mbs):
+            streams[i].wait_event(ev)
+            q = parts[i]
+            layers[i].forward(q["hidden"], q["hidden_scales"], q["ids"], q["weights"], out=outs[i],
+                              stream=streams[i])
+        for i in range(mbs):
+            done = torch.cuda.Event()
+            done.record(streams[i])
+            main_stream.wait_event(done)
+
+    for _ in range(args.warmup):
+        step_fn()
+    torch.cuda.synchronize()
+    for layer in layers:
+        afd.afd_ffn_set_timing(layer.handle, True)
+        afd.afd_ffn_get_timing(layer.handle)  # reset
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_fn()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = [0.0] * afd.AFD_NUM_STAGES
+    nfwd = 0
+    for layer in layers:
+        ms, n = afd.afd_ffn_get_timing(layer.handle)
+        stage_ms = [a + b for a, b in zip(stage_ms, ms)]
+        nfwd += n
+    per_launch = [m / max(nfwd, 1) for m in stage_ms]  # average launch duration per stage (ms)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = T / (ms_per_step * 1e-3)
+    dt = cfg["dtype"]
+    # dominant kernel: grouped GEMM gate/up + SwiGLU (two thirds of the weight bytes and flops)
+    gu_launch_s = per_launch[2] * 1e-3
+    launches_per_step = mbs
+    gu_bytes = units["gu_bytes"] / launches_per_step
+    gu_flops = units["gu_flops"] / launches_per_step
+    ai = units["layer_flops"] / units["layer_bytes"]
+    ridge = PEAK_TFLOPS[dt] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if ai < ridge:
+        ach = gu_bytes / gu_launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    else:
+        ach = gu_flops / gu_launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_TFLOPS[dt], 4)}
+    roof["kernel"] = "gemm_grouped_kernel (gate/up + SwiGLU)"
+    roof["launch_ms"] = round(per_launch[2], 4)
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f).get(args.workload)
+        if tr and tr.get("kernel_hash") == kernel_source_hash():
+            traffic = tr.get("bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    roof["traffic"] = traffic
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3_block128", "f32": "f32"}[dt],
+        "data": "synthetic (seeded; random-init expert weights N(0,0.02), hidden N(0,1))",
+        "config": {"workload": inputs.WORKLOAD_TITLES[args.workload], "T": T, "H": cfg["H"], "I": cfg["I"],
+                   "E": cfg["E"], "top_k": cfg["K"], "shared_inter": cfg.get("shared_inter", 0),
+                   "routing": cfg["routing"], "microbatches": mbs, "routed_rows": units["N"],
+                   "nonempty_experts": units["nonempty"], "seed": args.seed},
+        "layer": {"tflops": round(units["layer_flops"] / (ms_per_step * 1e-3) / 1e12, 2),
+                  "hbm_gbs": round(units["layer_bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
+                  "roofline_frac": round(max(units["layer_flops"] / (PEAK_TFLOPS[dt] * 1e12),
+                                             units["layer_bytes"] / (PEAK_HBM_GBS * 1e9)) /
+                                         (ms_per_step * 1e-3), 4),
+                  "stage_ms": {n: round(v, 4) for n, v in zip(afd.STAGE_NAMES, per_launch)}},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(p, cfg)
+    print(json.dumps(result), flush=True)
+    for layer in layers[::-1]:
+        layer.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -16,7 +16,8 @@ import os
 
 import torch  # noqa: F401  (must precede loading the library: one HIP runtime)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libafd_ffn.so")
+# AFD_FFN_LIB may name another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("AFD_FFN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libafd_ffn.so")
 
 AFD_OK, AFD_ERR_INVALID_ARG, AFD_ERR_UNSUPPORTED, AFD_ERR_OUT_OF_MEMORY, AFD_ERR_HIP, AFD_ERR_BAD_ROUTING = range(6)
 AFD_DTYPE_F32, AFD_DTYPE_BF16, AFD_DTYPE_FP8_BLOCK = 0, 1, 2

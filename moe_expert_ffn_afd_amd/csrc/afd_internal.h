@@ -52,6 +52,7 @@ constexpr int kPanelCols = 32;         // output columns per panel
 constexpr int kStepBytes = 128;        // bytes of K per super-step and row
 constexpr int kStepPanelBytes = 4096;  // one super-step of one panel
 constexpr int kWaves = 4;              // waves per GEMM workgroup
+constexpr int kXcds = 8;               // accelerator complex dies of an MI355X (one L2 each)
 constexpr int kDispatchThreads = 1024;
 constexpr int kDispatchLdsInts = 12288;  // chunk x expert counters held in LDS (48 KiB)
 constexpr int kMaxExperts = 512;
@@ -84,8 +85,10 @@ struct GemmParams {
   int32_t shared_row0;           // rows >= this are shared-expert rows (token = row - shared_row0)
   int32_t gather;                // 1: A row = hidden[token of row]; 0: A row = a[row]
   const uint8_t* a;              // activation rows
+  int64_t a_bytes;               // size of the activation buffer (< 2^31)
   int64_t a_row_bytes;
   const float* a_scales;         // fp8: [rows, K/128]
+  int64_t a_scale_bytes;
   int32_t a_scale_ld;
   const uint8_t* b;              // packed weights
   int64_t b_expert_bytes;
@@ -130,8 +133,8 @@ struct F32Params {
 // launchers (return hipError_t of the launch)
 hipError_t launch_dispatch_count_scan(const DispatchParams& p, hipStream_t s);
 hipError_t launch_dispatch_scatter(const DispatchParams& p, hipStream_t s);
-hipError_t launch_gemm(int dtype, bool gate_up, int mr, const GemmParams& p, int grid,
-                       hipStream_t s);
+hipError_t launch_gemm(int dtype, bool gate_up, int mr, const GemmParams& p, int64_t max_tasks,
+                       int num_cus, hipStream_t s);
 hipError_t launch_gemm_f32(bool gate_up, const F32Params& p, int grid, hipStream_t s);
 hipError_t launch_combine(int dtype, const CombineParams& p, int tokens, hipStream_t s);
 hipError_t launch_pack(int dtype, bool gate_up, const void* w_first, const void* w_second,

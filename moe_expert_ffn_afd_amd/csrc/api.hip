@@ -404,6 +404,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   // upper bound of the routed + shared m-tiles of this call
   const int64_t mt_bound = n_flat / bm + std::min<int64_t>(E, n_flat) + (a->S ? (T + bm - 1) / bm : 0) + 1;
   const int64_t rows_ld_h = (int64_t)I * esize_of(dt);
+  const int64_t h_rows = nmax + (a->S ? a->Tmax : 0);
   const int occupancy_wgs = 4;  // resident workgroups per CU the persistent grids aim for
 
   if (dt == kF32) {
@@ -444,8 +445,10 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     // gate/up: A = hidden rows gathered by token
     g.gather = 1;
     g.a = (const uint8_t*)hidden;
+    g.a_bytes = (int64_t)T * H * es;
     g.a_row_bytes = (int64_t)H * es;
     g.a_scales = hidden_scales;
+    g.a_scale_bytes = dt == kFP8 ? (int64_t)T * (H / 128) * 4 : 0;
     g.a_scale_ld = H / 128;
     g.b = a->w->gu;
     g.b_expert_bytes = a->w->gu_expert_bytes;
@@ -461,14 +464,15 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.c_row_bytes = rows_ld_h;
     g.c_scales = a->h_scales;
     g.c_scale_ld = I / 128;
-    int grid = (int)std::min<int64_t>(mt_bound * g.n_groups, (int64_t)a->num_cus * occupancy_wgs);
-    AFD_HIP(launch_gemm(dt, true, mr, g, grid, s));
+    AFD_HIP(launch_gemm(dt, true, mr, g, mt_bound * g.n_groups, a->num_cus, s));
     if ((st = mark())) return st;
     // down: A = h rows in sorted order
     g.gather = 0;
     g.a = a->h;
+    g.a_bytes = h_rows * rows_ld_h;
     g.a_row_bytes = rows_ld_h;
     g.a_scales = a->h_scales;
+    g.a_scale_bytes = dt == kFP8 ? h_rows * (I / 128) * 4 : 0;
     g.a_scale_ld = I / 128;
     g.b = a->w->dn;
     g.b_expert_bytes = a->w->dn_expert_bytes;
@@ -484,8 +488,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.c_row_bytes = (int64_t)H * 2;
     g.c_scales = nullptr;
     g.c_scale_ld = 0;
-    grid = (int)std::min<int64_t>(mt_bound * g.n_groups, (int64_t)a->num_cus * occupancy_wgs);
-    AFD_HIP(launch_gemm(dt, false, mr, g, grid, s));
+    AFD_HIP(launch_gemm(dt, false, mr, g, mt_bound * g.n_groups, a->num_cus, s));
     if ((st = mark())) return st;
   }
 

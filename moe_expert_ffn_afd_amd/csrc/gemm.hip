@@ -32,6 +32,8 @@
 // 128 h columns (amax / 448), the plain reading of running both expert GEMMs
 // in block-FP8.  The rows outside an m-tile's count are computed on a
 // duplicate of its first row and never stored.
+#include <algorithm>
+
 #include "afd_internal.h"
 
 namespace afd {
@@ -70,6 +72,42 @@ __device__ inline uint32_t pack_fp8x4(float a, float b, float c, float d) {
   return (uint32_t)v;
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+#ifndef AFD_XCD_REMAP
+#define AFD_XCD_REMAP 0
+#endif
+#ifndef AFD_STAGES
+#define AFD_STAGES 2
+#endif
+// cache policy of weight loads: 2 = non-temporal (streamed once; bf16),
+// 0 = default (FP8 tiles of one expert re-read their panels from L2)
+#ifndef AFD_B_AUX_BF16
+#define AFD_B_AUX_BF16 2
+#endif
+#ifndef AFD_B_AUX_FP8
+#define AFD_B_AUX_FP8 0
+#endif
+#ifndef AFD_PIPE_SCHED
+#define AFD_PIPE_SCHED 1
+#endif
+#if AFD_PIPE_SCHED
+#define AFD_PIPE_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define AFD_PIPE_FENCE() ((void)0)
+#endif
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  // raw buffer: stride 0, byte-addressed, out-of-range reads return zero
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+template <int AUX = 0>
+__device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
+}
+
 template <int DT, int MR>
 struct Stage {
   uint4 a[MR][4];
@@ -91,7 +129,16 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
   const int num_tasks = num_mt * p.n_groups;
   const int ks = p.k_steps;
 
-  for (int task = blockIdx.x; task < num_tasks; task += gridDim.x) {
+  // Optional XCD-aware schedule (AFD_XCD_REMAP): workgroups are dealt
+  // round-robin to the 8 XCDs; renumbering them so each XCD owns a contiguous
+  // block of ranks puts consecutive tasks (sibling m-tiles of one expert) under
+  // one L2.  Measured: it does not remove the sibling re-reads (the streams
+  // drift apart further than their share of L2) and slows skewed batches, so
+  // it is off.
+  const int G = gridDim.x;
+  const int rank = (AFD_XCD_REMAP && G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds
+                                                     : blockIdx.x;
+  for (int task = rank; task < num_tasks; task += G) {
     const int mt = task % num_mt;
     const int q = task / num_mt;
     const int4 tile = p.mtiles[mt];
@@ -101,20 +148,24 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
     const int unit = q * kWaves + wave;
     const bool active = GATEUP ? (unit < p.n_panels) : (2 * unit < p.n_panels);
 
-    // activation row pointers (rows past the tile's count repeat its first row)
-    const uint8_t* arow[MR];
-    const float* srow[MR];
+    // activation rows (rows past the tile's count repeat its first row): one
+    // 32-bit buffer offset per lane and row fragment; weights: SGPR offsets only
+    int aoff[MR], soffA[MR];
 #pragma unroll
     for (int mr = 0; mr < MR; ++mr) {
       int m = mr * 32 + col;
       int r = row0 + (m < rows ? m : 0);
-      int64_t src = r;
+      int src = r;
       if (p.gather) src = r >= p.shared_row0 ? (r - p.shared_row0) : (p.sorted_assign[r] / p.top_k);
-      arow[mr] = p.a + src * p.a_row_bytes + g * 64;
-      srow[mr] = DT == kFP8 ? p.a_scales + src * p.a_scale_ld : nullptr;
+      aoff[mr] = (int)(src * p.a_row_bytes) + g * 64;
+      soffA[mr] = src * p.a_scale_ld * 4;
     }
-    const uint8_t* bbase = p.b + (int64_t)expert * p.b_expert_bytes +
-                           (int64_t)(2 * unit) * p.b_panel_bytes + lane * 16;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.a_scales, p.a_scale_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b + (int64_t)expert * p.b_expert_bytes, p.b_expert_bytes);
+    const int boff = uniform((int)((int64_t)(2 * unit) * p.b_panel_bytes));
+    const int bpanel = (int)p.b_panel_bytes;
+    const int voffB = lane * 16;
     // FP8 weight block scales of this wave's two panels
     const float* sb0 = nullptr;
     const float* sb1 = nullptr;
@@ -138,17 +189,28 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
         for (int r = 0; r < 16; ++r) acc[mr][pp][r] = 0.0f;
 
     if (active) {
+      // Loads of step c >= ks use an offset past the end of the buffer, which
+      // the buffer unit returns as zeros: the loop body stays branch-free (so
+      // the compiler's waits only cover the stage being multiplied) and the
+      // phantom step adds exact zeros.
+      const int oobA = (int)(p.a_bytes > 0x7fffffff ? 0x7fffffff : p.a_bytes);
+      const int oobS = (int)(p.a_scale_bytes > 0x7fffffff ? 0x7fffffff : p.a_scale_bytes);
+      const int oobB = (int)p.b_expert_bytes;
       auto load = [&](Stage<DT, MR>& s, int c) {
+        const bool in = c < ks;
+        const int sb = in ? boff + c * kStepPanelBytes : oobB;
+        const int sa = in ? c * kStepBytes : oobA;
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            s.b[pp][j] = ld16(bbase + (int64_t)pp * p.b_panel_bytes + (int64_t)c * kStepPanelBytes + j * 1024);
+          for (int j = 0; j < 4; ++j) s.b[pp][j] = bload16<DT == kBF16 ? AFD_B_AUX_BF16 : AFD_B_AUX_FP8>(rb, voffB, sb + pp * bpanel + j * 1024);
 #pragma unroll
         for (int mr = 0; mr < MR; ++mr) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) s.a[mr][j] = ld16(arow[mr] + (int64_t)c * kStepBytes + j * 16);
-          if (DT == kFP8) s.sa[mr] = srow[mr][c];
+          for (int j = 0; j < 4; ++j) s.a[mr][j] = bload16(ra, aoff[mr], sa + j * 16);
+          if (DT == kFP8)
+            s.sa[mr] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rsa, soffA[mr], in ? c * 4 : oobS, 0));
         }
       };
       auto compute = [&](const Stage<DT, MR>& s, int c) {
@@ -162,8 +224,9 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
                 acc[mr][pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     as_bf16x8(s.b[pp][j]), as_bf16x8(s.a[mr][j]), acc[mr][pp], 0, 0, 0);
         } else {
-          const float b0 = sb0[(int64_t)c * p.b_scale_cols];
-          const float b1 = sb1[(int64_t)c * p.b_scale_cols];
+          const int cs = c < ks ? c : ks - 1;
+          const float b0 = sb0[(int64_t)cs * p.b_scale_cols];
+          const float b1 = sb1[(int64_t)cs * p.b_scale_cols];
 #pragma unroll
           for (int mr = 0; mr < MR; ++mr) {
 #pragma unroll
@@ -183,13 +246,20 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
         }
       };
 
-      Stage<DT, MR> s0, s1;
-      load(s0, 0);
-      for (int c = 0; c < ks; c += 2) {
-        if (c + 1 < ks) load(s1, c + 1);
-        compute(s0, c);
-        if (c + 2 < ks) load(s0, c + 2);
-        if (c + 1 < ks) compute(s1, c + 1);
+      // AFD_STAGES register stages: the loads of step c + AFD_STAGES - 1 are
+      // issued, kept together by scheduling fences, ahead of step c's
+      // multiplies, so AFD_STAGES - 1 super-steps stay in flight per wave.
+      Stage<DT, MR> st[AFD_STAGES];
+#pragma unroll
+      for (int i = 0; i + 1 < AFD_STAGES; ++i) load(st[i], i);
+      for (int c0 = 0; c0 < ks; c0 += AFD_STAGES) {
+#pragma unroll
+        for (int i = 0; i < AFD_STAGES; ++i) {
+          load(st[(i + AFD_STAGES - 1) % AFD_STAGES], c0 + i + AFD_STAGES - 1);
+          AFD_PIPE_FENCE();
+          compute(st[i], c0 + i);
+          AFD_PIPE_FENCE();
+        }
       }
     }
 
@@ -275,15 +345,27 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
 }
 
 template <int DT, bool GATEUP, int MR>
-static hipError_t launch_one(const GemmParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_grouped_kernel<DT, GATEUP, MR>), dim3(grid), dim3(256), 0, s, p);
+static hipError_t launch_one(const GemmParams& p, int64_t max_tasks, int num_cus, hipStream_t s) {
+  // persistent grid: never more workgroups than can be resident at once
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_grouped_kernel<DT, GATEUP, MR>, 256, 0) !=
+            hipSuccess ||
+        occ <= 0)
+      occ = 1;
+    per_cu = occ;
+  }
+  const int64_t grid = std::min<int64_t>(max_tasks, (int64_t)num_cus * per_cu);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_grouped_kernel<DT, GATEUP, MR>), dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int dtype, bool gate_up, int mr, const GemmParams& p, int grid, hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
+hipError_t launch_gemm(int dtype, bool gate_up, int mr, const GemmParams& p, int64_t max_tasks, int num_cus,
+                       hipStream_t s) {
 #define AFD_CASE(DT, GU, MRV) \
-  if (dtype == DT && gate_up == GU && mr == MRV) return launch_one<DT, GU, MRV>(p, grid, s);
+  if (dtype == DT && gate_up == GU && mr == MRV) return launch_one<DT, GU, MRV>(p, max_tasks, num_cus, s);
   AFD_CASE(kBF16, true, 1) AFD_CASE(kBF16, true, 2) AFD_CASE(kBF16, false, 1) AFD_CASE(kBF16, false, 2)
   AFD_CASE(kFP8, true, 1) AFD_CASE(kFP8, true, 2) AFD_CASE(kFP8, false, 1) AFD_CASE(kFP8, false, 2)
 #undef AFD_CASE

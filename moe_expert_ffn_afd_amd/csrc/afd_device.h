@@ -1,0 +1,84 @@
+// afd_device.h -- device helpers shared by the GEMM kernels (gfx950).
+#pragma once
+
+#include "afd_internal.h"
+
+namespace afd {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ inline i32x8 cat32(uint4 a, uint4 b) {
+  i32x8 r;
+  r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
+  r[4] = (int)b.x; r[5] = (int)b.y; r[6] = (int)b.z; r[7] = (int)b.w;
+  return r;
+}
+
+__device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)a);
+  uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)b);
+  return lo | (hi << 16);
+}
+
+// 4 floats -> 4 e4m3 codes (round to nearest even; inputs already within +-448)
+__device__ inline uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return (uint32_t)v;
+}
+
+// Raw buffer resource: stride 0, byte-addressed; reads at offsets >= the
+// record count return zero without touching memory.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+template <int AUX = 0>
+__device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
+}
+
+// Buffer loads straight into LDS: lane i's 16 (or 4) bytes land at
+// lds + 16 i (or 4 i); the LDS base must be wave-uniform.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, voff, soff, 0, 0);
+}
+__device__ inline void dma16_nt(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, voff, soff, 0, 2);
+}
+__device__ inline void dma4(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 4, voff, soff, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the memory-model fence __syncthreads adds (which
+// would wait for every in-flight load); the empty asm keeps the compiler from
+// moving memory operations across it.
+__device__ inline void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+}  // namespace dev
+}  // namespace afd

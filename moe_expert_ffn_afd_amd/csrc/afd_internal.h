@@ -32,7 +32,7 @@
 //    counts[E], offsets[E+1], err[1], num_mtiles[1]
 //    chunk_base[n_chunks][E]          first sorted row of each (chunk, expert)
 //    sorted_assign[N_max], row_of[N_max]
-//    mtiles[max_mtiles] (int4)        {expert, first row, rows, 0}
+//    mtiles[max_mtiles] (int4) x 2    light and heavy lists {expert, first row, rows, 0}
 //    h   [N_max + T_max, I]           routed rows in sorted order, then the
 //                                     shared expert's rows (token order) at
 //                                     row N_max; bf16 | e4m3 (+ scales
@@ -70,11 +70,14 @@ struct DispatchParams {
   int32_t* err;            // [1] ids outside [-1, E)
   int32_t* sorted_assign;  // [n_flat]
   int32_t* row_of;         // [n_flat]
-  int32_t bm;              // rows per routed m-tile
+  int32_t bm_light;        // rows per m-tile of light experts (streaming GEMM)
+  int32_t bm_heavy;        // rows per m-tile of heavy experts (LDS-tiled GEMM)
+  int32_t heavy_min_rows;  // experts with at least this many rows are heavy
   int32_t shared_rows;     // T when a shared expert exists, else 0
   int32_t shared_row0;     // first shared row (N_max)
-  int4* mtiles;            // tile list
-  int32_t* num_mtiles;     // [1]
+  int4* mtiles;            // light tile list
+  int4* mtiles_heavy;      // heavy tile list
+  int32_t* num_mtiles;     // [2]: light, heavy
 };
 
 struct GemmParams {
@@ -135,6 +138,9 @@ hipError_t launch_dispatch_count_scan(const DispatchParams& p, hipStream_t s);
 hipError_t launch_dispatch_scatter(const DispatchParams& p, hipStream_t s);
 hipError_t launch_gemm(int dtype, bool gate_up, int mr, const GemmParams& p, int64_t max_tasks,
                        int num_cus, hipStream_t s);
+hipError_t launch_gemm_tiled(int dtype, bool gate_up, const GemmParams& p, int64_t max_tasks, int num_cus,
+                             hipStream_t s);
+int tiled_rows(int dtype);  // m-tile rows of the LDS-tiled GEMM
 hipError_t launch_gemm_f32(bool gate_up, const F32Params& p, int grid, hipStream_t s);
 hipError_t launch_combine(int dtype, const CombineParams& p, int tokens, hipStream_t s);
 hipError_t launch_pack(int dtype, bool gate_up, const void* w_first, const void* w_second,

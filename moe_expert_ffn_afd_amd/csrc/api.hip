@@ -85,6 +85,7 @@ struct afd_ffn {
   int32_t *counts = nullptr, *offsets = nullptr, *err = nullptr, *num_mtiles = nullptr;
   int32_t *chunk_base = nullptr, *sorted_assign = nullptr, *row_of = nullptr;
   int4* mtiles = nullptr;
+  int4* mtiles_heavy = nullptr;
   uint8_t* h = nullptr;
   float* h_scales = nullptr;
   uint8_t* y = nullptr;
@@ -142,8 +143,9 @@ afd_status alloc_workspace(afd_ffn* a) {
   int64_t off = 0;
   auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + bytes, 256); return o; };
   const int64_t o_counts = take(4ll * a->E), o_offsets = take(4ll * (a->E + 1)), o_err = take(4),
-                o_nmt = take(4), o_cb = take(4ll * a->max_chunks * a->E), o_sa = take(4 * nmax),
-                o_ro = take(4 * nmax), o_mt = take(16ll * a->max_mtiles), o_h = take(rows * a->I * es),
+                o_nmt = take(8), o_cb = take(4ll * a->max_chunks * a->E), o_sa = take(4 * nmax),
+                o_ro = take(4 * nmax), o_mt = take(16ll * a->max_mtiles), o_mth = take(16ll * a->max_mtiles),
+                o_h = take(rows * a->I * es),
                 o_hs = take(a->dtype == kFP8 ? rows * (a->I / 128) * 4 : 0), o_y = take(rows * a->H * ys);
   if (hipMalloc((void**)&a->ws, off) != hipSuccess) {
     (void)hipGetLastError();
@@ -158,6 +160,7 @@ afd_status alloc_workspace(afd_ffn* a) {
   a->sorted_assign = (int32_t*)(a->ws + o_sa);
   a->row_of = (int32_t*)(a->ws + o_ro);
   a->mtiles = (int4*)(a->ws + o_mt);
+  a->mtiles_heavy = (int4*)(a->ws + o_mth);
   a->h = a->ws + o_h;
   a->h_scales = a->dtype == kFP8 ? (float*)(a->ws + o_hs) : nullptr;
   a->y = a->ws + o_y;
@@ -355,9 +358,14 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   const int E = a->E, K = a->K, H = a->H, I = a->I, dt = a->dtype;
   const int64_t n_flat = (int64_t)T * K;
   const int64_t nmax = (int64_t)a->Tmax * K;
+  // Light experts (rows <= bm_light, one m-tile) stream their weights through
+  // registers (gemm.hip); heavier experts (and the shared expert) take the
+  // LDS-tiled GEMM (gemm_tiled.hip), which fetches each weight panel once per
+  // tile of tiled_rows() rows.  fp32 uses light tiles of 32 rows only.
   const int mr = dt == kF32 ? 1 : (n_flat <= 32ll * E ? 1 : 2);
   const int bm = 32 * mr;
-
+  const int bm_heavy = dt == kF32 ? bm : tiled_rows(dt);
+  const int heavy_min = dt == kF32 ? 0x7fffffff : bm + 1;
   std::vector<hipEvent_t> ev;
   auto mark = [&]() -> afd_status {
     if (!a->timing) return AFD_OK;
@@ -381,10 +389,13 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   d.err = a->err;
   d.sorted_assign = a->sorted_assign;
   d.row_of = a->row_of;
-  d.bm = bm;
+  d.bm_light = bm;
+  d.bm_heavy = bm_heavy;
+  d.heavy_min_rows = heavy_min;
   d.shared_rows = a->S ? T : 0;
   d.shared_row0 = (int32_t)nmax;
   d.mtiles = a->mtiles;
+  d.mtiles_heavy = a->mtiles_heavy;
   d.num_mtiles = a->num_mtiles;
   a->last_T = T;
 
@@ -401,8 +412,9 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   AFD_HIP(launch_dispatch_scatter(d, s));
   if ((st = mark())) return st;
 
-  // upper bound of the routed + shared m-tiles of this call
+  // upper bounds of the routed + shared m-tiles of this call, per list
   const int64_t mt_bound = n_flat / bm + std::min<int64_t>(E, n_flat) + (a->S ? (T + bm - 1) / bm : 0) + 1;
+  const int64_t mth_bound = dt == kF32 ? 0 : n_flat / heavy_min + (a->S ? (T + bm_heavy - 1) / bm_heavy : 0) + 1;
   const int64_t rows_ld_h = (int64_t)I * esize_of(dt);
   const int64_t h_rows = nmax + (a->S ? a->Tmax : 0);
   const int occupancy_wgs = 4;  // resident workgroups per CU the persistent grids aim for
@@ -464,6 +476,13 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.c_row_bytes = rows_ld_h;
     g.c_scales = a->h_scales;
     g.c_scale_ld = I / 128;
+    {
+      GemmParams gh = g;
+      gh.mtiles = a->mtiles_heavy;
+      gh.num_mtiles = a->num_mtiles + 1;
+      gh.n_groups = (2 * I / 32) / 8;
+      AFD_HIP(launch_gemm_tiled(dt, true, gh, mth_bound * gh.n_groups, a->num_cus, s));
+    }
     AFD_HIP(launch_gemm(dt, true, mr, g, mt_bound * g.n_groups, a->num_cus, s));
     if ((st = mark())) return st;
     // down: A = h rows in sorted order
@@ -488,6 +507,13 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.c_row_bytes = (int64_t)H * 2;
     g.c_scales = nullptr;
     g.c_scale_ld = 0;
+    {
+      GemmParams gh = g;
+      gh.mtiles = a->mtiles_heavy;
+      gh.num_mtiles = a->num_mtiles + 1;
+      gh.n_groups = (H / 32 + 7) / 8;
+      AFD_HIP(launch_gemm_tiled(dt, false, gh, mth_bound * gh.n_groups, a->num_cus, s));
+    }
     AFD_HIP(launch_gemm(dt, false, mr, g, mt_bound * g.n_groups, a->num_cus, s));
     if ((st = mark())) return st;
   }

@@ -110,24 +110,40 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
 
   for (int i = tid; i < ncc; i += kDispatchThreads) p.chunk_base[i] = excl[i % E] + cc[i];
 
-  // m-tile list: routed experts in expert order, then the shared expert
+  // m-tile lists: experts with at least heavy_min_rows rows go to the heavy
+  // list (tiles of bm_heavy rows), the others to the light list (bm_light);
+  // routed experts in expert order, then the shared expert.
   {
-    int v = tid < E ? (total[tid] + p.bm - 1) / p.bm : 0;
-    int n_tiles = 0;
-    int toff = block_exclusive_scan_1024(v, scan_tmp, &n_tiles);
+    const int n = tid < E ? total[tid] : 0;
+    const bool heavy = n >= p.heavy_min_rows;
+    const int vl = heavy ? 0 : (n + p.bm_light - 1) / p.bm_light;
+    const int vh = heavy ? (n + p.bm_heavy - 1) / p.bm_heavy : 0;
+    int n_light = 0, n_heavy = 0;
+    const int offl = block_exclusive_scan_1024(vl, scan_tmp, &n_light);
+    const int offh = block_exclusive_scan_1024(vh, scan_tmp, &n_heavy);
     if (tid < E) {
-      for (int j = 0; j < v; ++j) {
-        int r0 = j * p.bm;
-        int rows = min(p.bm, total[tid] - r0);
-        p.mtiles[toff + j] = make_int4(tid, excl[tid] + r0, rows, 0);
+      for (int j = 0; j < vl; ++j) {
+        const int r0 = j * p.bm_light;
+        p.mtiles[offl + j] = make_int4(tid, excl[tid] + r0, min(p.bm_light, n - r0), 0);
+      }
+      for (int j = 0; j < vh; ++j) {
+        const int r0 = j * p.bm_heavy;
+        p.mtiles_heavy[offh + j] = make_int4(tid, excl[tid] + r0, min(p.bm_heavy, n - r0), 0);
       }
     }
-    int n_shared = (p.shared_rows + p.bm - 1) / p.bm;
+    const bool sh_heavy = p.shared_rows >= p.heavy_min_rows;
+    const int bms = sh_heavy ? p.bm_heavy : p.bm_light;
+    const int n_shared = (p.shared_rows + bms - 1) / bms;
+    int4* list = sh_heavy ? p.mtiles_heavy : p.mtiles;
+    const int base = sh_heavy ? n_heavy : n_light;
     for (int j = tid; j < n_shared; j += kDispatchThreads) {
-      int r0 = j * p.bm;
-      p.mtiles[n_tiles + j] = make_int4(E, p.shared_row0 + r0, min(p.bm, p.shared_rows - r0), 0);
+      const int r0 = j * bms;
+      list[base + j] = make_int4(E, p.shared_row0 + r0, min(bms, p.shared_rows - r0), 0);
     }
-    if (tid == 0) p.num_mtiles[0] = n_tiles + n_shared;
+    if (tid == 0) {
+      p.num_mtiles[0] = n_light + (sh_heavy ? 0 : n_shared);
+      p.num_mtiles[1] = n_heavy + (sh_heavy ? n_shared : 0);
+    }
   }
 }
 

@@ -34,45 +34,11 @@
 // duplicate of its first row and never stored.
 #include <algorithm>
 
-#include "afd_internal.h"
+#include "afd_device.h"
 
 namespace afd {
 
-namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-__device__ inline uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
-__device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-__device__ inline i32x8 cat32(uint4 a, uint4 b) {
-  i32x8 r;
-  r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
-  r[4] = (int)b.x; r[5] = (int)b.y; r[6] = (int)b.z; r[7] = (int)b.w;
-  return r;
-}
-
-__device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
-
-__device__ inline uint32_t pack_bf16x2(float a, float b) {
-  uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)a);
-  uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)b);
-  return lo | (hi << 16);
-}
-
-// 4 floats -> 4 e4m3 codes (round to nearest even; inputs already within +-448)
-__device__ inline uint32_t pack_fp8x4(float a, float b, float c, float d) {
-  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
-  return (uint32_t)v;
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
+using namespace dev;
 
 #ifndef AFD_XCD_REMAP
 #define AFD_XCD_REMAP 0
@@ -97,16 +63,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define AFD_PIPE_FENCE() ((void)0)
 #endif
 
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  // raw buffer: stride 0, byte-addressed, out-of-range reads return zero
-  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
-}
-
-template <int AUX = 0>
-__device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
-}
+namespace {
 
 template <int DT, int MR>
 struct Stage {

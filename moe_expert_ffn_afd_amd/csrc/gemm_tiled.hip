@@ -1,0 +1,374 @@
+// gemm_tiled.hip -- LDS-tiled grouped expert GEMMs for experts with many rows.
+//
+// Same two GEMMs as gemm.hip (gate/up with SwiGLU and, for block-FP8, the
+// 1x128 re-quantisation of h; then down), for the m-tiles of "heavy" experts
+// (rows >= a threshold): aggregated AFD batches concentrate tokens on popular
+// experts ("FastAFD" summary, speculative decoding multiplies routed expert
+// work; design-space study: expert FFNs are compute-intensive), where each
+// weight panel must feed many rows and the MFMA pipes, not HBM, set the pace.
+//
+// A workgroup task is one m-tile of BM rows times 8 weight panels (256 GEMM
+// columns: 128 h columns of gate+up, or 256 output columns of down).  Each
+// super-step (128 bytes of K) of the task's weight panels and activation rows
+// is copied HBM -> LDS by the buffer unit directly (no registers), into a ring
+// of NS stages; the four waves then read their MFMA fragments from LDS, so a
+// weight byte is fetched once per tile and shared by every row of it.  The
+// copy engine's LDS writes are invisible to the compiler, so the kernel
+// orders them itself: it waits until only the younger stages are outstanding
+// (s_waitcnt vmcnt) and then barriers, before any wave reads the stage.
+//
+// LDS layout of a stage: weight panels exactly as packed in HBM (fragment
+// order: conflict-free 16-byte reads), then activation rows of 128 bytes with
+// the eight 16-byte slots of row r permuted by slot ^ (r & 7) (so the 32 rows
+// of an MFMA fragment read spread over all banks), then (FP8) the per-row
+// activation scale of the super-step.
+//
+// bf16: tile 256 x 256, waves 2 x 2 of 128 rows x 4 panels, MFMA 32x32x16,
+//       256 fp32 accumulators per lane, 2 LDS stages (128 KiB).
+// FP8:  tile 128 x 256, waves 1 x 4 of 128 rows x 2 panels, MFMA 16x16x128 --
+//       one MFMA spans a whole 128-deep scale block, so each product is added
+//       straight into the accumulators times (token scale x block scale);
+//       3 LDS stages (147 KiB) keep two super-steps in flight per CU.
+#include <algorithm>
+#include <type_traits>
+
+#include "afd_device.h"
+
+namespace afd {
+
+using namespace dev;
+
+namespace {
+
+template <int DT>
+struct Tiled;
+template <>
+struct Tiled<kBF16> {
+  static constexpr int WM = 2, WN = 2, BM = 256, NS = 2;
+  static constexpr int A_DMA = 8, B_DMA = 8, S_DMA = 0;  // copies per wave and stage
+};
+template <>
+struct Tiled<kFP8> {
+  static constexpr int WM = 1, WN = 4, BM = 128, NS = 3;
+  static constexpr int A_DMA = 4, B_DMA = 8, S_DMA = 1;
+};
+
+constexpr int kBNP = 8;        // panels per task
+constexpr int kSSlots = 256;   // scale slots per stage (one per lane of the 4 waves)
+
+template <int DT>
+constexpr int stage_bytes() {
+  return kBNP * kStepPanelBytes + Tiled<DT>::BM * kStepBytes + (DT == kFP8 ? kSSlots * 4 : 0);
+}
+
+__device__ inline int clamp31(int64_t v) { return v > 0x7fffffff ? 0x7fffffff : (int)v; }
+
+}  // namespace
+
+template <int DT, bool GATEUP>
+__global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
+  using C = Tiled<DT>;
+  constexpr int BM = C::BM, NS = C::NS;
+  constexpr int B_OFF = 0, A_OFF = kBNP * kStepPanelBytes, S_OFF = A_OFF + BM * kStepBytes;
+  constexpr int STAGE = stage_bytes<DT>();
+  constexpr int PER_STAGE = C::A_DMA + C::B_DMA + C::S_DMA;
+  constexpr int ROWS_PER_WAVE = BM / 4;  // activation rows each wave copies
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ float red[4][128];  // FP8 epilogue: per-wave row amax
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);  // scalar: LDS copy targets must be wave-uniform
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int num_mt = uniform(p.num_mtiles[0]);
+  const int num_tasks = num_mt * p.n_groups;
+  const int ks = p.k_steps;
+  const int oobA = clamp31(p.a_bytes), oobS = clamp31(p.a_scale_bytes);
+  const int oobB = (int)p.b_expert_bytes;
+  const int bpanel = (int)p.b_panel_bytes;
+  const auto ra = make_rsrc(p.a, p.a_bytes);
+  const auto rsa = make_rsrc(p.a_scales, p.a_scale_bytes);
+
+  for (int task = blockIdx.x; task < num_tasks; task += gridDim.x) {
+    const int mt = task % num_mt;
+    const int q = task / num_mt;
+    const int4 tile = p.mtiles[mt];
+    const int expert = uniform(tile.x), row0 = uniform(tile.y), rows = uniform(tile.z);
+    const auto rb = make_rsrc(p.b + (int64_t)expert * p.b_expert_bytes, p.b_expert_bytes);
+    const int pbase = uniform((int)((int64_t)q * kBNP * p.b_panel_bytes));
+
+    auto src_row = [&](int r) -> int {  // activation row of tile row r (valid r)
+      const int rr = row0 + r;
+      if (!p.gather) return rr;
+      return rr >= p.shared_row0 ? rr - p.shared_row0 : p.sorted_assign[rr] / p.top_k;
+    };
+    // activation copies: wave copies rows [wave*RPW, +RPW), 8 rows per copy;
+    // lane i -> row +i/8, LDS slot i%8, which holds 16-byte part slot^(row&7)
+    int avoff[C::A_DMA];
+#pragma unroll
+    for (int k = 0; k < C::A_DMA; ++k) {
+      const int r = wave * ROWS_PER_WAVE + 8 * k + (lane >> 3);
+      const int part = (lane & 7) ^ (r & 7);
+      avoff[k] = r < rows ? (int)((int64_t)src_row(r) * p.a_row_bytes) + part * 16 : oobA;
+    }
+    int svoff = oobS;
+    if (DT == kFP8) {
+      const int r = wave * 64 + lane;
+      if (r < rows && r < BM) svoff = src_row(r) * p.a_scale_ld * 4;
+    }
+
+    // copy super-step c of the task into ring slot c % NS; `in` false (only in
+    // the prologue of very short reductions) copies zeros from past the end
+    auto issue = [&](int c, bool in) {
+      uint8_t* st = smem + (c % NS) * STAGE;
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int panel = 2 * wave + pl;
+          const int so = in ? pbase + panel * bpanel + c * kStepPanelBytes + j * 1024 : oobB;
+          if (DT == kBF16)
+            dma16_nt(rb, st + B_OFF + panel * kStepPanelBytes + j * 1024, lane * 16, so);
+          else
+            dma16(rb, st + B_OFF + panel * kStepPanelBytes + j * 1024, lane * 16, so);
+        }
+#pragma unroll
+      for (int k = 0; k < C::A_DMA; ++k)
+        dma16(ra, st + A_OFF + (wave * ROWS_PER_WAVE + 8 * k) * kStepBytes, avoff[k], in ? c * kStepBytes : oobA);
+      if (DT == kFP8) dma4(rsa, st + S_OFF + wave * 256, svoff, in ? c * 4 : oobS);
+    };
+
+    // accumulators: bf16 [4 row frags][4 panels] of 32x32; FP8 [8 token
+    // sub-tiles][4 weight sub-panels] of 16x16
+    constexpr int NA = DT == kBF16 ? 4 : 8;
+    constexpr int NB = 4;
+    typedef typename std::conditional<DT == kBF16, f32x16, f32x4>::type acc_t;
+    constexpr int NR = DT == kBF16 ? 16 : 4;
+    acc_t acc[NA][NB];
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[a][b][r] = 0.0f;
+
+    // FP8 weight block scales: gate/up -> block q of gate (panel 2wn) and up
+    // (panel 2wn+1); down -> block (8q + 2wn) / 4 for both panels
+    const float* sb0 = nullptr;
+    const float* sb1 = nullptr;
+    if (DT == kFP8) {
+      const int64_t eoff = (int64_t)expert * p.b_scale_rows * p.b_scale_cols;
+      if (GATEUP) {
+        sb0 = p.b_scales0 + eoff + q;
+        sb1 = p.b_scales1 + eoff + q;
+      } else {
+        sb0 = p.b_scales0 + eoff + (8 * q + 2 * wn) / 4;
+        sb1 = sb0;
+      }
+    }
+
+    auto compute = [&](const uint8_t* st, int c) {
+      const uint8_t* Bs = st + B_OFF;
+      const uint8_t* As = st + A_OFF;
+      if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x8 af[4], bfr[4];
+#pragma unroll
+          for (int mr = 0; mr < 4; ++mr) {
+            const int r = wm * 128 + mr * 32 + (lane & 31);
+            const int slot = ((lane >> 5) * 4 + j) ^ (r & 7);
+            af[mr] = *reinterpret_cast<const bf16x8*>(As + r * kStepBytes + slot * 16);
+          }
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp)
+            bfr[pp] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 4 + pp) * kStepPanelBytes + j * 1024 + lane * 16);
+#pragma unroll
+          for (int mr = 0; mr < 4; ++mr)
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp)
+              acc[mr][pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[pp], af[mr], acc[mr][pp], 0, 0, 0);
+        }
+      } else {
+        const float* S = reinterpret_cast<const float*>(st + S_OFF);
+        const int cs = c < ks ? c : ks - 1;
+        const float sbv[2] = {sb0[(int64_t)cs * p.b_scale_cols], sb1[(int64_t)cs * p.b_scale_cols]};
+        const int kg = lane >> 4;  // which 32 bytes of the 128-deep block this lane carries
+        const int g = kg >> 1, j0 = (kg & 1) * 2;
+        i32x8 w[2][2];
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const uint8_t* lo = Bs + (2 * wn + pl) * kStepPanelBytes + j0 * 1024 + (16 * s + (lane & 15) + 32 * g) * 16;
+            w[pl][s] = cat32(*reinterpret_cast<const uint4*>(lo), *reinterpret_cast<const uint4*>(lo + 1024));
+          }
+#pragma unroll
+        for (int ts = 0; ts < 8; ++ts) {
+          const int r = ts * 16 + (lane & 15);
+          const int s0 = (2 * kg) ^ (r & 7), s1 = (2 * kg + 1) ^ (r & 7);
+          const i32x8 x = cat32(*reinterpret_cast<const uint4*>(As + r * kStepBytes + s0 * 16),
+                                *reinterpret_cast<const uint4*>(As + r * kStepBytes + s1 * 16));
+          const float sa = S[r];
+#pragma unroll
+          for (int pl = 0; pl < 2; ++pl) {
+            const float sc = sa * sbv[pl];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+              t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[pl][s], x, t, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+              for (int r4 = 0; r4 < 4; ++r4) acc[ts][pl * 2 + s][r4] += t[r4] * sc;
+            }
+          }
+        }
+      }
+    };
+
+    // Prologue fills NS-1 slots; the steady loop (branch-free, so the
+    // accumulators stay put) waits for its slot, barriers, refills the slot
+    // freed by the previous step and multiplies; the last NS-1 steps drain.
+#pragma unroll
+    for (int s = 0; s + 1 < NS; ++s) issue(s, s < ks);
+    int c = 0;
+    for (; c + NS - 1 < ks; ++c) {
+      wait_vmcnt<(NS - 2) * PER_STAGE>();  // this wave's copies of step c have landed
+      raw_barrier();                        // ... and every wave's; slot of c-1 is free
+      issue(c + NS - 1, true);
+      compute(smem + (c % NS) * STAGE, c);
+    }
+    if (NS == 3 && c + 1 < ks) {            // two steps left: the younger is in flight
+      wait_vmcnt<PER_STAGE>();
+      raw_barrier();
+      compute(smem + (c % NS) * STAGE, c);
+      ++c;
+    }
+    if (c < ks) {
+      wait_vmcnt<0>();
+      raw_barrier();
+      compute(smem + (c % NS) * STAGE, c);
+    }
+    wait_vmcnt<0>();  // prologue copies past the end (very short reductions)
+    raw_barrier();    // every wave is done with the ring before the next task refills it
+
+    // ------------------------------------------------------------- epilogue
+    if constexpr (DT == kBF16) {
+#pragma unroll
+      for (int mr = 0; mr < 4; ++mr) {
+        const int m = wm * 128 + mr * 32 + (lane & 31);
+        if (m >= rows) continue;
+        uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes;
+#pragma unroll
+        for (int pp = 0; pp < 4; pp += (GATEUP ? 2 : 1)) {
+          const int P = q * kBNP + wn * 4 + pp;  // packed panel index (gate/up: 2 per unit)
+          if (P >= (GATEUP ? 2 * p.n_panels : p.n_panels)) continue;
+          const int col0 = GATEUP ? 32 * (P / 2) : 32 * P;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int n = 8 * r4 + 4 * (lane >> 5);
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              v[e] = GATEUP ? silu_mul(acc[mr][pp][4 * r4 + e], acc[mr][pp + 1][4 * r4 + e]) : acc[mr][pp][4 * r4 + e];
+            uint2 o;
+            o.x = pack_bf16x2(v[0], v[1]);
+            o.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(orow + (int64_t)(col0 + n) * 2) = o;
+          }
+        }
+      }
+    } else if constexpr (GATEUP) {
+      // h for unit u = 4q + wn: gate sub-panels 0,1 and up sub-panels 2,3
+      const int kg = lane >> 4;
+      float h[8][2][4];
+#pragma unroll
+      for (int ts = 0; ts < 8; ++ts) {
+        float a = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            h[ts][s][r4] = silu_mul(acc[ts][s][r4], acc[ts][2 + s][r4]);
+            a = fmaxf(a, fabsf(h[ts][s][r4]));
+          }
+        a = fmaxf(a, __shfl_xor(a, 16, 64));
+        a = fmaxf(a, __shfl_xor(a, 32, 64));
+        if (kg == 0) red[wave][ts * 16 + (lane & 15)] = a;
+      }
+      __syncthreads();
+      const int u = 4 * q + wn;
+#pragma unroll
+      for (int ts = 0; ts < 8; ++ts) {
+        const int m = ts * 16 + (lane & 15);
+        const float amax = fmaxf(fmaxf(red[0][m], red[1][m]), fmaxf(red[2][m], red[3][m]));
+        const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+        const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
+        if (m < rows) {
+          uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes + 32 * u;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = fminf(fmaxf(h[ts][s][e] * inv, -448.0f), 448.0f);
+            *reinterpret_cast<uint32_t*>(orow + 16 * s + 4 * kg) = pack_fp8x4(v[0], v[1], v[2], v[3]);
+          }
+          if (wave == 0 && kg == 0) p.c_scales[(int64_t)(row0 + m) * p.c_scale_ld + q] = scale;
+        }
+      }
+      __syncthreads();  // red[] is rewritten by the next task
+    } else {
+      const int kg = lane >> 4;
+#pragma unroll
+      for (int ts = 0; ts < 8; ++ts) {
+        const int m = ts * 16 + (lane & 15);
+        if (m >= rows) continue;
+        uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes;
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) {
+          const int P = q * kBNP + 2 * wn + pl;
+          if (P >= p.n_panels) continue;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const int col = 32 * P + 16 * s + 4 * kg;
+            uint2 o;
+            o.x = pack_bf16x2(acc[ts][pl * 2 + s][0], acc[ts][pl * 2 + s][1]);
+            o.y = pack_bf16x2(acc[ts][pl * 2 + s][2], acc[ts][pl * 2 + s][3]);
+            *reinterpret_cast<uint2*>(orow + (int64_t)col * 2) = o;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int DT, bool GATEUP>
+static hipError_t launch_tiled_one(const GemmParams& p, int64_t max_tasks, int num_cus, hipStream_t s) {
+  constexpr int lds = Tiled<DT>::NS * stage_bytes<DT>();
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled_kernel<DT, GATEUP>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_tiled_kernel<DT, GATEUP>, 256, lds) != hipSuccess ||
+        occ <= 0)
+      occ = 1;
+    per_cu = occ;
+  }
+  const int64_t grid = std::min<int64_t>(max_tasks, (int64_t)num_cus * per_cu);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_tiled_kernel<DT, GATEUP>), dim3((unsigned)grid), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+int tiled_rows(int dtype) { return dtype == kFP8 ? Tiled<kFP8>::BM : Tiled<kBF16>::BM; }
+
+hipError_t launch_gemm_tiled(int dtype, bool gate_up, const GemmParams& p, int64_t max_tasks, int num_cus,
+                             hipStream_t s) {
+  if (dtype == kBF16) return gate_up ? launch_tiled_one<kBF16, true>(p, max_tasks, num_cus, s)
+                                     : launch_tiled_one<kBF16, false>(p, max_tasks, num_cus, s);
+  if (dtype == kFP8) return gate_up ? launch_tiled_one<kFP8, true>(p, max_tasks, num_cus, s)
+                                    : launch_tiled_one<kFP8, false>(p, max_tasks, num_cus, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace afd

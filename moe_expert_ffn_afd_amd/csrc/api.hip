@@ -112,6 +112,8 @@ afd_status check_config(const afd_ffn_config* c) {
     return fail(AFD_ERR_INVALID_ARG, "hidden, inter, num_experts, top_k and max_tokens must be positive");
   if (c->hidden % 128 || c->inter % 128)
     return fail(AFD_ERR_UNSUPPORTED, "hidden (%d) and inter (%d) must be multiples of 128", c->hidden, c->inter);
+  if (c->dtype == kFP8 && (c->hidden > 16384 || c->inter > 16384))
+    return fail(AFD_ERR_UNSUPPORTED, "block-FP8 reductions are limited to 128 blocks (hidden, inter <= 16384)");
   if (c->num_experts > kMaxExperts) return fail(AFD_ERR_UNSUPPORTED, "num_experts %d > %d", c->num_experts, kMaxExperts);
   if (c->top_k > kMaxTopK) return fail(AFD_ERR_UNSUPPORTED, "top_k %d > %d", c->top_k, kMaxTopK);
   if ((int64_t)c->max_tokens * c->top_k >= (1ll << 26))

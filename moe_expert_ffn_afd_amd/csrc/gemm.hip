@@ -123,18 +123,14 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
     const int boff = uniform((int)((int64_t)(2 * unit) * p.b_panel_bytes));
     const int bpanel = (int)p.b_panel_bytes;
     const int voffB = lane * 16;
-    // FP8 weight block scales of this wave's two panels
-    const float* sb0 = nullptr;
-    const float* sb1 = nullptr;
+    // FP8 weight block scales of this wave's two panels, one per super-step:
+    // lane l holds those of super-steps l and l + 64, read in the loop with
+    // readlane (no memory operation inside the load pipeline)
+    BlockScales sbs;
     if (DT == kFP8) {
-      int64_t eoff = (int64_t)expert * p.b_scale_rows * p.b_scale_cols;
-      if (GATEUP) {
-        sb0 = p.b_scales0 + eoff + unit / 4;
-        sb1 = p.b_scales1 + eoff + unit / 4;
-      } else {
-        sb0 = p.b_scales0 + eoff + unit / 2;
-        sb1 = sb0;
-      }
+      const int64_t eoff = (int64_t)expert * p.b_scale_rows * p.b_scale_cols;
+      const int nb = GATEUP ? unit / 4 : unit / 2;
+      sbs.load(p.b_scales0 + eoff + nb, (GATEUP ? p.b_scales1 : p.b_scales0) + eoff + nb, p.b_scale_cols, ks, lane);
     }
 
     f32x16 acc[MR][2];
@@ -182,8 +178,7 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
                     as_bf16x8(s.b[pp][j]), as_bf16x8(s.a[mr][j]), acc[mr][pp], 0, 0, 0);
         } else {
           const int cs = c < ks ? c : ks - 1;
-          const float b0 = sb0[(int64_t)cs * p.b_scale_cols];
-          const float b1 = sb1[(int64_t)cs * p.b_scale_cols];
+          const float b0 = sbs.get0(cs), b1 = sbs.get1(cs);
 #pragma unroll
           for (int mr = 0; mr < MR; ++mr) {
 #pragma unroll

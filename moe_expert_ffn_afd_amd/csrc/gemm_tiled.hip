@@ -17,10 +17,13 @@
 // orders them itself: it waits until only the younger stages are outstanding
 // (s_waitcnt vmcnt) and then barriers, before any wave reads the stage.
 //
+// LDS fragments are read as ext_vector types: reading them through HIP's
+// struct uint4 makes the compiler drain every in-flight copy before the read.
+//
 // LDS layout of a stage: weight panels exactly as packed in HBM (fragment
 // order: conflict-free 16-byte reads), then activation rows of 128 bytes with
-// the eight 16-byte slots of row r permuted by slot ^ (r & 7) (so the 32 rows
-// of an MFMA fragment read spread over all banks), then (FP8) the per-row
+// the eight 16-byte slots of row r permuted by slot ^ ((r >> 1) & 7) (so the
+// rows of an MFMA fragment read spread over all banks), then (FP8) the per-row
 // activation scale of the super-step.
 //
 // bf16: tile 256 x 256, waves 2 x 2 of 128 rows x 4 panels, MFMA 32x32x16,
@@ -28,7 +31,7 @@
 // FP8:  tile 128 x 256, waves 1 x 4 of 128 rows x 2 panels, MFMA 16x16x128 --
 //       one MFMA spans a whole 128-deep scale block, so each product is added
 //       straight into the accumulators times (token scale x block scale);
-//       3 LDS stages (147 KiB) keep two super-steps in flight per CU.
+//       3 LDS stages (156 KiB) keep two super-steps in flight per CU.
 #include <algorithm>
 #include <type_traits>
 
@@ -42,26 +45,46 @@ namespace {
 
 template <int DT>
 struct Tiled;
+// SUB = ring slots per super-step (a slot holds 128/SUB bytes of K per row)
 template <>
 struct Tiled<kBF16> {
-  static constexpr int WM = 2, WN = 2, BM = 256, NS = 2;
-  static constexpr int A_DMA = 8, B_DMA = 8, S_DMA = 0;  // copies per wave and stage
+  static constexpr int WM = 2, WN = 2, BM = 256, NS = 4, SUB = 2;
+  static constexpr int A_DMA = 4, B_DMA = 4, S_DMA = 0;  // copies per wave and slot
 };
 template <>
 struct Tiled<kFP8> {
-  static constexpr int WM = 1, WN = 4, BM = 128, NS = 3;
+  static constexpr int WM = 1, WN = 4, BM = 128, NS = 3, SUB = 1;
   static constexpr int A_DMA = 4, B_DMA = 8, S_DMA = 1;
 };
 
+#ifndef AFD_TILED_B_NT
+#define AFD_TILED_B_NT 0  // 1: bf16 weight copies non-temporal (panels are re-read by sibling m-tiles)
+#endif
+#ifndef AFD_TILED_XCD_REMAP
+#define AFD_TILED_XCD_REMAP 1
+#endif
+#ifndef AFD_TILED_MB
+#define AFD_TILED_MB 4  // m-tiles per rasterisation block
+#endif
+
 constexpr int kBNP = 8;        // panels per task
-constexpr int kSSlots = 256;   // scale slots per stage (one per lane of the 4 waves)
+constexpr int kMB = AFD_TILED_MB;
+constexpr int kSSlots = 256;   // scale rows per stage (one per lane of the 4 waves), 16 B each
 
 template <int DT>
 constexpr int stage_bytes() {
-  return kBNP * kStepPanelBytes + Tiled<DT>::BM * kStepBytes + (DT == kFP8 ? kSSlots * 4 : 0);
+  return (kBNP * kStepPanelBytes + Tiled<DT>::BM * kStepBytes) / Tiled<DT>::SUB + (DT == kFP8 ? kSSlots * 16 : 0);
 }
 
 __device__ inline int clamp31(int64_t v) { return v > 0x7fffffff ? 0x7fffffff : (int)v; }
+
+// LDS slot permutation of activation row r (rows of RB bytes, RB/16 slots):
+// 16 consecutive rows reading the same 16-byte part hit 16 distinct
+// (row, slot) bank groups, i.e. all 64 banks.
+template <int RB>
+__device__ inline int swz(int r) {
+  return RB == 128 ? (r >> 1) & 7 : (r >> 2) & 3;
+}
 
 }  // namespace
 
@@ -69,10 +92,15 @@ template <int DT, bool GATEUP>
 __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
   using C = Tiled<DT>;
   constexpr int BM = C::BM, NS = C::NS;
-  constexpr int B_OFF = 0, A_OFF = kBNP * kStepPanelBytes, S_OFF = A_OFF + BM * kStepBytes;
+  constexpr int SUB = C::SUB;
+  constexpr int RB = kStepBytes / SUB;              // activation bytes per row and slot
+  constexpr int PB = kStepPanelBytes / SUB;         // weight bytes per panel and slot
+  constexpr int B_OFF = 0, A_OFF = kBNP * PB, S_OFF = A_OFF + BM * RB;
   constexpr int STAGE = stage_bytes<DT>();
   constexpr int PER_STAGE = C::A_DMA + C::B_DMA + C::S_DMA;
   constexpr int ROWS_PER_WAVE = BM / 4;  // activation rows each wave copies
+  constexpr int ROWS_PER_COPY = 1024 / RB;
+  constexpr int SLOTS = RB / 16;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ float red[4][128];  // FP8 epilogue: per-wave row amax
 
@@ -88,9 +116,27 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
   const auto ra = make_rsrc(p.a, p.a_bytes);
   const auto rsa = make_rsrc(p.a_scales, p.a_scale_bytes);
 
-  for (int task = blockIdx.x; task < num_tasks; task += gridDim.x) {
-    const int mt = task % num_mt;
-    const int q = task / num_mt;
+  // Task order: blocks of kMB m-tiles x all column groups, column group
+  // outer within a block, and workgroup ranks renumbered so each XCD owns a
+  // contiguous run of tasks.  The ~32 tiles an XCD runs at once then share a
+  // few activation chunks and weight panels through its L2.
+  const int G = gridDim.x;
+  const int rank = (AFD_TILED_XCD_REMAP && G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds
+                                                           : blockIdx.x;
+  const int nq = p.n_groups;
+  const int full = (num_mt / kMB) * kMB * nq;  // tasks in complete blocks
+  const int rem = num_mt % kMB;
+  for (int task = rank; task < num_tasks; task += G) {
+    int mt, q;
+    if (task < full) {
+      const int blk = task / (kMB * nq), w = task % (kMB * nq);
+      q = w / kMB;
+      mt = blk * kMB + w % kMB;
+    } else {
+      const int t = task - full;
+      q = t / rem;
+      mt = (num_mt / kMB) * kMB + t % rem;
+    }
     const int4 tile = p.mtiles[mt];
     const int expert = uniform(tile.x), row0 = uniform(tile.y), rows = uniform(tile.z);
     const auto rb = make_rsrc(p.b + (int64_t)expert * p.b_expert_bytes, p.b_expert_bytes);
@@ -101,13 +147,16 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
       if (!p.gather) return rr;
       return rr >= p.shared_row0 ? rr - p.shared_row0 : p.sorted_assign[rr] / p.top_k;
     };
-    // activation copies: wave copies rows [wave*RPW, +RPW), 8 rows per copy;
-    // lane i -> row +i/8, LDS slot i%8, which holds 16-byte part slot^(row&7)
+    // activation copies: wave copies rows [wave*RPW, +RPW), ROWS_PER_COPY rows
+    // per copy; lane i -> row +i/SLOTS, LDS slot i%SLOTS holding 16-byte
+    // part index pi = slot ^ swz(row); with two slots per super-step, index pi
+    // of slot h is part (pi&1) + 2h + 4(pi>>1) (the +32h bytes ride in soffset)
     int avoff[C::A_DMA];
 #pragma unroll
     for (int k = 0; k < C::A_DMA; ++k) {
-      const int r = wave * ROWS_PER_WAVE + 8 * k + (lane >> 3);
-      const int part = (lane & 7) ^ (r & 7);
+      const int r = wave * ROWS_PER_WAVE + ROWS_PER_COPY * k + lane / SLOTS;
+      const int pi = (lane % SLOTS) ^ swz<RB>(r);
+      const int part = SUB == 1 ? pi : (pi & 1) + 4 * (pi >> 1);
       avoff[k] = r < rows ? (int)((int64_t)src_row(r) * p.a_row_bytes) + part * 16 : oobA;
     }
     int svoff = oobS;
@@ -116,25 +165,30 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
       if (r < rows && r < BM) svoff = src_row(r) * p.a_scale_ld * 4;
     }
 
-    // copy super-step c of the task into ring slot c % NS; `in` false (only in
-    // the prologue of very short reductions) copies zeros from past the end
-    auto issue = [&](int c, bool in) {
-      uint8_t* st = smem + (c % NS) * STAGE;
+    // copy ring step t (super-step t / SUB, part t % SUB) into slot t % NS;
+    // `in` false (prologue of very short reductions only) copies zeros
+    auto issue = [&](int t, bool in) {
+      uint8_t* st = smem + (t % NS) * STAGE;
+      const int c = t / SUB, h = t % SUB;
 #pragma unroll
       for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4 / SUB; ++j) {
           const int panel = 2 * wave + pl;
-          const int so = in ? pbase + panel * bpanel + c * kStepPanelBytes + j * 1024 : oobB;
-          if (DT == kBF16)
-            dma16_nt(rb, st + B_OFF + panel * kStepPanelBytes + j * 1024, lane * 16, so);
+          const int so = in ? pbase + panel * bpanel + c * kStepPanelBytes + (h * (4 / SUB) + j) * 1024 : oobB;
+          if (DT == kBF16 && AFD_TILED_B_NT)
+            dma16_nt(rb, st + B_OFF + panel * PB + j * 1024, lane * 16, so);
           else
-            dma16(rb, st + B_OFF + panel * kStepPanelBytes + j * 1024, lane * 16, so);
+            dma16(rb, st + B_OFF + panel * PB + j * 1024, lane * 16, so);
         }
 #pragma unroll
       for (int k = 0; k < C::A_DMA; ++k)
-        dma16(ra, st + A_OFF + (wave * ROWS_PER_WAVE + 8 * k) * kStepBytes, avoff[k], in ? c * kStepBytes : oobA);
-      if (DT == kFP8) dma4(rsa, st + S_OFF + wave * 256, svoff, in ? c * 4 : oobS);
+        dma16(ra, st + A_OFF + (wave * ROWS_PER_WAVE + ROWS_PER_COPY * k) * RB, avoff[k],
+              in ? c * kStepBytes + 32 * h : oobA);
+      // activation scales: 16-byte copies (scales of super-steps c..c+3 of a
+      // row; only the first is used) -- the compiler tracks 4-byte LDS copies
+      // and would drain every in-flight load before the next LDS read
+      if (DT == kFP8) dma16(rsa, st + S_OFF + wave * 1024, svoff, in ? c * 4 : oobS);
     };
 
     // accumulators: bf16 [4 row frags][4 panels] of 32x32; FP8 [8 token
@@ -151,37 +205,36 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) acc[a][b][r] = 0.0f;
 
-    // FP8 weight block scales: gate/up -> block q of gate (panel 2wn) and up
-    // (panel 2wn+1); down -> block (8q + 2wn) / 4 for both panels
-    const float* sb0 = nullptr;
-    const float* sb1 = nullptr;
+    // FP8 weight block scales, one per super-step (see BlockScales): gate/up
+    // -> block q of gate (panel 2wn) and up (panel 2wn+1); down -> block
+    // (8q + 2wn) / 4 for both panels
+    BlockScales sbs;
     if (DT == kFP8) {
       const int64_t eoff = (int64_t)expert * p.b_scale_rows * p.b_scale_cols;
-      if (GATEUP) {
-        sb0 = p.b_scales0 + eoff + q;
-        sb1 = p.b_scales1 + eoff + q;
-      } else {
-        sb0 = p.b_scales0 + eoff + (8 * q + 2 * wn) / 4;
-        sb1 = sb0;
-      }
+      if (GATEUP)
+        sbs.load(p.b_scales0 + eoff + q, p.b_scales1 + eoff + q, p.b_scale_cols, ks, lane);
+      else
+        sbs.load(p.b_scales0 + eoff + (8 * q + 2 * wn) / 4, p.b_scales0 + eoff + (8 * q + 2 * wn) / 4,
+                 p.b_scale_cols, ks, lane);
     }
 
-    auto compute = [&](const uint8_t* st, int c) {
+    auto compute = [&](const uint8_t* st, int t) {
       const uint8_t* Bs = st + B_OFF;
       const uint8_t* As = st + A_OFF;
       if constexpr (DT == kBF16) {
+        // slot t holds MFMAs j = 2(t%2) + jj of its super-step
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int jj = 0; jj < 4 / SUB; ++jj) {
           bf16x8 af[4], bfr[4];
 #pragma unroll
           for (int mr = 0; mr < 4; ++mr) {
             const int r = wm * 128 + mr * 32 + (lane & 31);
-            const int slot = ((lane >> 5) * 4 + j) ^ (r & 7);
-            af[mr] = *reinterpret_cast<const bf16x8*>(As + r * kStepBytes + slot * 16);
+            const int pi = SUB == 1 ? (lane >> 5) * 4 + jj : jj + 2 * (lane >> 5);
+            af[mr] = *reinterpret_cast<const bf16x8*>(As + r * RB + (pi ^ swz<RB>(r)) * 16);
           }
 #pragma unroll
           for (int pp = 0; pp < 4; ++pp)
-            bfr[pp] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 4 + pp) * kStepPanelBytes + j * 1024 + lane * 16);
+            bfr[pp] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 4 + pp) * PB + jj * 1024 + lane * 16);
 #pragma unroll
           for (int mr = 0; mr < 4; ++mr)
 #pragma unroll
@@ -190,8 +243,9 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
         }
       } else {
         const float* S = reinterpret_cast<const float*>(st + S_OFF);
+        const int c = t;  // one slot per super-step
         const int cs = c < ks ? c : ks - 1;
-        const float sbv[2] = {sb0[(int64_t)cs * p.b_scale_cols], sb1[(int64_t)cs * p.b_scale_cols]};
+        const float sbv[2] = {sbs.get0(cs), sbs.get1(cs)};
         const int kg = lane >> 4;  // which 32 bytes of the 128-deep block this lane carries
         const int g = kg >> 1, j0 = (kg & 1) * 2;
         i32x8 w[2][2];
@@ -199,16 +253,16 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
         for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            const uint8_t* lo = Bs + (2 * wn + pl) * kStepPanelBytes + j0 * 1024 + (16 * s + (lane & 15) + 32 * g) * 16;
-            w[pl][s] = cat32(*reinterpret_cast<const uint4*>(lo), *reinterpret_cast<const uint4*>(lo + 1024));
+            const uint8_t* lo = Bs + (2 * wn + pl) * PB + j0 * 1024 + (16 * s + (lane & 15) + 32 * g) * 16;
+            w[pl][s] = cat32v(*reinterpret_cast<const i32x4*>(lo), *reinterpret_cast<const i32x4*>(lo + 1024));
           }
 #pragma unroll
         for (int ts = 0; ts < 8; ++ts) {
           const int r = ts * 16 + (lane & 15);
-          const int s0 = (2 * kg) ^ (r & 7), s1 = (2 * kg + 1) ^ (r & 7);
-          const i32x8 x = cat32(*reinterpret_cast<const uint4*>(As + r * kStepBytes + s0 * 16),
-                                *reinterpret_cast<const uint4*>(As + r * kStepBytes + s1 * 16));
-          const float sa = S[r];
+          const int s0 = (2 * kg) ^ swz<RB>(r), s1 = (2 * kg + 1) ^ swz<RB>(r);
+          const i32x8 x = cat32v(*reinterpret_cast<const i32x4*>(As + r * RB + s0 * 16),
+                                 *reinterpret_cast<const i32x4*>(As + r * RB + s1 * 16));
+          const float sa = S[4 * r];
 #pragma unroll
           for (int pl = 0; pl < 2; ++pl) {
             const float sc = sa * sbv[pl];
@@ -226,26 +280,28 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
 
     // Prologue fills NS-1 slots; the steady loop (branch-free, so the
     // accumulators stay put) waits for its slot, barriers, refills the slot
-    // freed by the previous step and multiplies; the last NS-1 steps drain.
+    // freed by the previous step and multiplies; the last NS-1 steps drain
+    // with shrinking waits.
+    const int nsteps = ks * SUB;
 #pragma unroll
-    for (int s = 0; s + 1 < NS; ++s) issue(s, s < ks);
-    int c = 0;
-    for (; c + NS - 1 < ks; ++c) {
-      wait_vmcnt<(NS - 2) * PER_STAGE>();  // this wave's copies of step c have landed
-      raw_barrier();                        // ... and every wave's; slot of c-1 is free
-      issue(c + NS - 1, true);
-      compute(smem + (c % NS) * STAGE, c);
+    for (int i = 0; i + 1 < NS; ++i) issue(i, i < nsteps);
+    int t = 0;
+    for (; t + NS - 1 < nsteps; ++t) {
+      wait_vmcnt<(NS - 2) * PER_STAGE>();  // this wave's copies of step t have landed
+      raw_barrier();                        // ... and every wave's; slot of t-1 is free
+      issue(t + NS - 1, true);
+      compute(smem + (t % NS) * STAGE, t);
     }
-    if (NS == 3 && c + 1 < ks) {            // two steps left: the younger is in flight
-      wait_vmcnt<PER_STAGE>();
+    for (; t < nsteps; ++t) {  // drain: steps t+1 .. nsteps-1 are still in flight
+      const int younger = nsteps - 1 - t;
+      if (NS > 3 && younger >= 2)
+        wait_vmcnt<(NS > 3 ? 2 : 0) * PER_STAGE>();
+      else if (younger == 1)
+        wait_vmcnt<PER_STAGE>();
+      else
+        wait_vmcnt<0>();
       raw_barrier();
-      compute(smem + (c % NS) * STAGE, c);
-      ++c;
-    }
-    if (c < ks) {
-      wait_vmcnt<0>();
-      raw_barrier();
-      compute(smem + (c % NS) * STAGE, c);
+      compute(smem + (t % NS) * STAGE, t);
     }
     wait_vmcnt<0>();  // prologue copies past the end (very short reductions)
     raw_barrier();    // every wave is done with the ring before the next task refills it

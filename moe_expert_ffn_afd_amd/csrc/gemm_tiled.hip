@@ -26,12 +26,13 @@
 // rows of an MFMA fragment read spread over all banks), then (FP8) the per-row
 // activation scale of the super-step.
 //
-// bf16: tile 256 x 256, waves 2 x 2 of 128 rows x 4 panels, MFMA 32x32x16,
-//       256 fp32 accumulators per lane, 2 LDS stages (128 KiB).
-// FP8:  tile 128 x 256, waves 1 x 4 of 128 rows x 2 panels, MFMA 16x16x128 --
-//       one MFMA spans a whole 128-deep scale block, so each product is added
-//       straight into the accumulators times (token scale x block scale);
-//       3 LDS stages (156 KiB) keep two super-steps in flight per CU.
+// bf16: tile 256 x 256, 4 waves as 2 x 2 of 128 rows x 4 panels, MFMA
+//       32x32x16, 256 fp32 accumulators per lane; ring of 4 half-super-step
+//       slots (128 KiB), three in flight while one is multiplied.
+// FP8:  tile 128 x 256, 8 waves (two per SIMD) as 2 x 4 of 64 rows x 2
+//       panels, MFMA 16x16x128 -- one MFMA spans a whole 128-deep scale block,
+//       so each product is added straight into the accumulators times (token
+//       scale x block scale); ring of 3 super-step slots (150 KiB).
 #include <algorithm>
 #include <type_traits>
 
@@ -43,18 +44,17 @@ using namespace dev;
 
 namespace {
 
+// Tile configuration.  NW waves form a WM x WN grid over BM rows x 8 panels;
+// SUB = ring slots per super-step (a slot holds 128/SUB bytes of K per row).
 template <int DT>
 struct Tiled;
-// SUB = ring slots per super-step (a slot holds 128/SUB bytes of K per row)
 template <>
 struct Tiled<kBF16> {
-  static constexpr int WM = 2, WN = 2, BM = 256, NS = 4, SUB = 2;
-  static constexpr int A_DMA = 4, B_DMA = 4, S_DMA = 0;  // copies per wave and slot
+  static constexpr int NW = 4, WM = 2, WN = 2, BM = 256, NS = 4, SUB = 2;
 };
 template <>
 struct Tiled<kFP8> {
-  static constexpr int WM = 1, WN = 4, BM = 128, NS = 3, SUB = 1;
-  static constexpr int A_DMA = 4, B_DMA = 8, S_DMA = 1;
+  static constexpr int NW = 8, WM = 2, WN = 4, BM = 128, NS = 3, SUB = 1;
 };
 
 #ifndef AFD_TILED_B_NT
@@ -67,13 +67,16 @@ struct Tiled<kFP8> {
 #define AFD_TILED_MB 4  // m-tiles per rasterisation block
 #endif
 
-constexpr int kBNP = 8;        // panels per task
+constexpr int kBNP = 8;  // panels per task
 constexpr int kMB = AFD_TILED_MB;
-constexpr int kSSlots = 256;   // scale rows per stage (one per lane of the 4 waves), 16 B each
 
 template <int DT>
 constexpr int stage_bytes() {
-  return (kBNP * kStepPanelBytes + Tiled<DT>::BM * kStepBytes) / Tiled<DT>::SUB + (DT == kFP8 ? kSSlots * 16 : 0);
+  return (kBNP * kStepPanelBytes + Tiled<DT>::BM * kStepBytes) / Tiled<DT>::SUB + (DT == kFP8 ? Tiled<DT>::BM * 16 : 0);
+}
+template <int DT>
+constexpr int lds_bytes() {
+  return Tiled<DT>::NS * stage_bytes<DT>() + (DT == kFP8 ? 1024 : 0);  // + sink of idle scale copies
 }
 
 __device__ inline int clamp31(int64_t v) { return v > 0x7fffffff ? 0x7fffffff : (int)v; }
@@ -89,24 +92,32 @@ __device__ inline int swz(int r) {
 }  // namespace
 
 template <int DT, bool GATEUP>
-__global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
+__global__ __launch_bounds__(Tiled<DT>::NW * 64, 1) void gemm_tiled_kernel(GemmParams p) {
   using C = Tiled<DT>;
-  constexpr int BM = C::BM, NS = C::NS;
-  constexpr int SUB = C::SUB;
-  constexpr int RB = kStepBytes / SUB;              // activation bytes per row and slot
-  constexpr int PB = kStepPanelBytes / SUB;         // weight bytes per panel and slot
+  constexpr int NW = C::NW, WM = C::WM, WN = C::WN, BM = C::BM, NS = C::NS, SUB = C::SUB;
+  constexpr int RB = kStepBytes / SUB;        // activation bytes per row and slot
+  constexpr int PB = kStepPanelBytes / SUB;   // weight bytes per panel and slot
+  constexpr int JJ = 4 / SUB;                 // 1 KiB chunks per panel and slot
   constexpr int B_OFF = 0, A_OFF = kBNP * PB, S_OFF = A_OFF + BM * RB;
   constexpr int STAGE = stage_bytes<DT>();
-  constexpr int PER_STAGE = C::A_DMA + C::B_DMA + C::S_DMA;
-  constexpr int ROWS_PER_WAVE = BM / 4;  // activation rows each wave copies
+  constexpr int SINK = NS * STAGE;
   constexpr int ROWS_PER_COPY = 1024 / RB;
   constexpr int SLOTS = RB / 16;
+  constexpr int B_DMA = kBNP * JJ / NW;                 // copies per wave and slot
+  constexpr int A_DMA = BM * RB / 1024 / NW;
+  constexpr int S_DMA = DT == kFP8 ? 1 : 0;
+  constexpr int S_COPIES = BM / 64;                     // waves holding real scale rows
+  constexpr int PER_STAGE = B_DMA + A_DMA + S_DMA;
+  constexpr int WR = BM / WM;                           // rows per wave
+  constexpr int NPW = kBNP / WN;                        // panels per wave
+  static_assert(B_DMA * NW == kBNP * JJ && A_DMA * NW * 1024 == BM * RB, "copy split");
+  static_assert(DT != kFP8 || (NPW == 2 && S_COPIES <= NW), "FP8 wave holds one gate/up unit");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ float red[4][128];  // FP8 epilogue: per-wave row amax
+  __shared__ float red[WM][WN][64];  // FP8 epilogue: per-wave row amax
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);  // scalar: LDS copy targets must be wave-uniform
-  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int wm = wave / WN, wn = wave % WN;
   const int num_mt = uniform(p.num_mtiles[0]);
   const int num_tasks = num_mt * p.n_groups;
   const int ks = p.k_steps;
@@ -147,22 +158,25 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
       if (!p.gather) return rr;
       return rr >= p.shared_row0 ? rr - p.shared_row0 : p.sorted_assign[rr] / p.top_k;
     };
-    // activation copies: wave copies rows [wave*RPW, +RPW), ROWS_PER_COPY rows
-    // per copy; lane i -> row +i/SLOTS, LDS slot i%SLOTS holding 16-byte
-    // part index pi = slot ^ swz(row); with two slots per super-step, index pi
-    // of slot h is part (pi&1) + 2h + 4(pi>>1) (the +32h bytes ride in soffset)
-    int avoff[C::A_DMA];
+    // Activation copy k of a wave covers rows (wave*A_DMA + k)*ROWS_PER_COPY
+    // + [0, ROWS_PER_COPY); lane i -> row +i/SLOTS, LDS slot i%SLOTS holding
+    // 16-byte part index pi = slot ^ swz(row); with two slots per super-step,
+    // index pi of slot h is part (pi&1) + 2h + 4(pi>>1) (+32h rides in soffset).
+    int avoff[A_DMA];
 #pragma unroll
-    for (int k = 0; k < C::A_DMA; ++k) {
-      const int r = wave * ROWS_PER_WAVE + ROWS_PER_COPY * k + lane / SLOTS;
+    for (int k = 0; k < A_DMA; ++k) {
+      const int r = (wave * A_DMA + k) * ROWS_PER_COPY + lane / SLOTS;
       const int pi = (lane % SLOTS) ^ swz<RB>(r);
       const int part = SUB == 1 ? pi : (pi & 1) + 4 * (pi >> 1);
       avoff[k] = r < rows ? (int)((int64_t)src_row(r) * p.a_row_bytes) + part * 16 : oobA;
     }
+    // FP8 activation scales: waves below S_COPIES copy 64 rows each (16 bytes
+    // = the scales of 4 super-steps per row, the first used); the others copy
+    // zeros into a sink so every wave issues the same number of copies
     int svoff = oobS;
     if (DT == kFP8) {
       const int r = wave * 64 + lane;
-      if (r < rows && r < BM) svoff = src_row(r) * p.a_scale_ld * 4;
+      if (wave < S_COPIES && r < rows) svoff = src_row(r) * p.a_scale_ld * 4;
     }
 
     // copy ring step t (super-step t / SUB, part t % SUB) into slot t % NS;
@@ -171,30 +185,27 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
       uint8_t* st = smem + (t % NS) * STAGE;
       const int c = t / SUB, h = t % SUB;
 #pragma unroll
-      for (int pl = 0; pl < 2; ++pl)
+      for (int k = 0; k < B_DMA; ++k) {
+        const int i = wave * B_DMA + k, panel = i / JJ, j = i % JJ;
+        const int so = in ? pbase + panel * bpanel + c * kStepPanelBytes + (h * JJ + j) * 1024 : oobB;
+        if (DT == kBF16 && AFD_TILED_B_NT)
+          dma16_nt(rb, st + B_OFF + panel * PB + j * 1024, lane * 16, so);
+        else
+          dma16(rb, st + B_OFF + panel * PB + j * 1024, lane * 16, so);
+      }
 #pragma unroll
-        for (int j = 0; j < 4 / SUB; ++j) {
-          const int panel = 2 * wave + pl;
-          const int so = in ? pbase + panel * bpanel + c * kStepPanelBytes + (h * (4 / SUB) + j) * 1024 : oobB;
-          if (DT == kBF16 && AFD_TILED_B_NT)
-            dma16_nt(rb, st + B_OFF + panel * PB + j * 1024, lane * 16, so);
-          else
-            dma16(rb, st + B_OFF + panel * PB + j * 1024, lane * 16, so);
-        }
-#pragma unroll
-      for (int k = 0; k < C::A_DMA; ++k)
-        dma16(ra, st + A_OFF + (wave * ROWS_PER_WAVE + ROWS_PER_COPY * k) * RB, avoff[k],
-              in ? c * kStepBytes + 32 * h : oobA);
-      // activation scales: 16-byte copies (scales of super-steps c..c+3 of a
-      // row; only the first is used) -- the compiler tracks 4-byte LDS copies
-      // and would drain every in-flight load before the next LDS read
-      if (DT == kFP8) dma16(rsa, st + S_OFF + wave * 1024, svoff, in ? c * 4 : oobS);
+      for (int k = 0; k < A_DMA; ++k)
+        dma16(ra, st + A_OFF + (wave * A_DMA + k) * 1024, avoff[k], in ? c * kStepBytes + 32 * h : oobA);
+      // 16-byte copies: the compiler tracks 4-byte LDS copies and would drain
+      // every in-flight load before the next LDS read
+      if (DT == kFP8)
+        dma16(rsa, wave < S_COPIES ? st + S_OFF + wave * 1024 : smem + SINK, svoff, in ? c * 4 : oobS);
     };
 
-    // accumulators: bf16 [4 row frags][4 panels] of 32x32; FP8 [8 token
-    // sub-tiles][4 weight sub-panels] of 16x16
-    constexpr int NA = DT == kBF16 ? 4 : 8;
-    constexpr int NB = 4;
+    // accumulators: bf16 [WR/32 row frags][NPW panels] of 32x32; FP8 [WR/16
+    // token sub-tiles][2 panels x 2 halves] of 16x16
+    constexpr int NA = DT == kBF16 ? WR / 32 : WR / 16;
+    constexpr int NB = DT == kBF16 ? NPW : 2 * NPW;
     typedef typename std::conditional<DT == kBF16, f32x16, f32x4>::type acc_t;
     constexpr int NR = DT == kBF16 ? 16 : 4;
     acc_t acc[NA][NB];
@@ -222,23 +233,23 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
       const uint8_t* Bs = st + B_OFF;
       const uint8_t* As = st + A_OFF;
       if constexpr (DT == kBF16) {
-        // slot t holds MFMAs j = 2(t%2) + jj of its super-step
+        // slot t holds MFMAs j = JJ(t%SUB) + jj of its super-step
 #pragma unroll
-        for (int jj = 0; jj < 4 / SUB; ++jj) {
-          bf16x8 af[4], bfr[4];
+        for (int jj = 0; jj < JJ; ++jj) {
+          bf16x8 af[NA], bfr[NPW];
 #pragma unroll
-          for (int mr = 0; mr < 4; ++mr) {
-            const int r = wm * 128 + mr * 32 + (lane & 31);
+          for (int mr = 0; mr < NA; ++mr) {
+            const int r = wm * WR + mr * 32 + (lane & 31);
             const int pi = SUB == 1 ? (lane >> 5) * 4 + jj : jj + 2 * (lane >> 5);
             af[mr] = *reinterpret_cast<const bf16x8*>(As + r * RB + (pi ^ swz<RB>(r)) * 16);
           }
 #pragma unroll
-          for (int pp = 0; pp < 4; ++pp)
-            bfr[pp] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 4 + pp) * PB + jj * 1024 + lane * 16);
+          for (int pp = 0; pp < NPW; ++pp)
+            bfr[pp] = *reinterpret_cast<const bf16x8*>(Bs + (wn * NPW + pp) * PB + jj * 1024 + lane * 16);
 #pragma unroll
-          for (int mr = 0; mr < 4; ++mr)
+          for (int mr = 0; mr < NA; ++mr)
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp)
+            for (int pp = 0; pp < NPW; ++pp)
               acc[mr][pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[pp], af[mr], acc[mr][pp], 0, 0, 0);
         }
       } else {
@@ -257,8 +268,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
             w[pl][s] = cat32v(*reinterpret_cast<const i32x4*>(lo), *reinterpret_cast<const i32x4*>(lo + 1024));
           }
 #pragma unroll
-        for (int ts = 0; ts < 8; ++ts) {
-          const int r = ts * 16 + (lane & 15);
+        for (int ts = 0; ts < NA; ++ts) {
+          const int r = wm * WR + ts * 16 + (lane & 15);
           const int s0 = (2 * kg) ^ swz<RB>(r), s1 = (2 * kg + 1) ^ swz<RB>(r);
           const i32x8 x = cat32v(*reinterpret_cast<const i32x4*>(As + r * RB + s0 * 16),
                                  *reinterpret_cast<const i32x4*>(As + r * RB + s1 * 16));
@@ -268,10 +279,10 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
             const float sc = sa * sbv[pl];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-              f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
-              t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[pl][s], x, t, 0, 0, 0, 0, 0, 0);
+              f32x4 tt = {0.0f, 0.0f, 0.0f, 0.0f};
+              tt = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[pl][s], x, tt, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-              for (int r4 = 0; r4 < 4; ++r4) acc[ts][pl * 2 + s][r4] += t[r4] * sc;
+              for (int r4 = 0; r4 < 4; ++r4) acc[ts][pl * 2 + s][r4] += tt[r4] * sc;
             }
           }
         }
@@ -309,13 +320,13 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
     // ------------------------------------------------------------- epilogue
     if constexpr (DT == kBF16) {
 #pragma unroll
-      for (int mr = 0; mr < 4; ++mr) {
-        const int m = wm * 128 + mr * 32 + (lane & 31);
+      for (int mr = 0; mr < NA; ++mr) {
+        const int m = wm * WR + mr * 32 + (lane & 31);
         if (m >= rows) continue;
         uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes;
 #pragma unroll
-        for (int pp = 0; pp < 4; pp += (GATEUP ? 2 : 1)) {
-          const int P = q * kBNP + wn * 4 + pp;  // packed panel index (gate/up: 2 per unit)
+        for (int pp = 0; pp < NPW; pp += (GATEUP ? 2 : 1)) {
+          const int P = q * kBNP + wn * NPW + pp;  // packed panel index (gate/up: 2 per unit)
           if (P >= (GATEUP ? 2 * p.n_panels : p.n_panels)) continue;
           const int col0 = GATEUP ? 32 * (P / 2) : 32 * P;
 #pragma unroll
@@ -333,11 +344,12 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
         }
       }
     } else if constexpr (GATEUP) {
-      // h for unit u = 4q + wn: gate sub-panels 0,1 and up sub-panels 2,3
+      // h for unit u = 4q + wn: gate sub-panels 0,1 and up sub-panels 2,3;
+      // row amax over the task's 128 h columns = over the WN waves of a row half
       const int kg = lane >> 4;
-      float h[8][2][4];
+      float h[NA][2][4];
 #pragma unroll
-      for (int ts = 0; ts < 8; ++ts) {
+      for (int ts = 0; ts < NA; ++ts) {
         float a = 0.0f;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
@@ -348,14 +360,17 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
           }
         a = fmaxf(a, __shfl_xor(a, 16, 64));
         a = fmaxf(a, __shfl_xor(a, 32, 64));
-        if (kg == 0) red[wave][ts * 16 + (lane & 15)] = a;
+        if (kg == 0) red[wm][wn][ts * 16 + (lane & 15)] = a;
       }
       __syncthreads();
       const int u = 4 * q + wn;
 #pragma unroll
-      for (int ts = 0; ts < 8; ++ts) {
-        const int m = ts * 16 + (lane & 15);
-        const float amax = fmaxf(fmaxf(red[0][m], red[1][m]), fmaxf(red[2][m], red[3][m]));
+      for (int ts = 0; ts < NA; ++ts) {
+        const int mi = ts * 16 + (lane & 15);
+        const int m = wm * WR + mi;
+        float amax = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, red[wm][w2][mi]);
         const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
         const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
         if (m < rows) {
@@ -367,15 +382,15 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
             for (int e = 0; e < 4; ++e) v[e] = fminf(fmaxf(h[ts][s][e] * inv, -448.0f), 448.0f);
             *reinterpret_cast<uint32_t*>(orow + 16 * s + 4 * kg) = pack_fp8x4(v[0], v[1], v[2], v[3]);
           }
-          if (wave == 0 && kg == 0) p.c_scales[(int64_t)(row0 + m) * p.c_scale_ld + q] = scale;
+          if (wn == 0 && kg == 0) p.c_scales[(int64_t)(row0 + m) * p.c_scale_ld + q] = scale;
         }
       }
       __syncthreads();  // red[] is rewritten by the next task
     } else {
       const int kg = lane >> 4;
 #pragma unroll
-      for (int ts = 0; ts < 8; ++ts) {
-        const int m = ts * 16 + (lane & 15);
+      for (int ts = 0; ts < NA; ++ts) {
+        const int m = wm * WR + ts * 16 + (lane & 15);
         if (m >= rows) continue;
         uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes;
 #pragma unroll
@@ -398,21 +413,23 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
 
 template <int DT, bool GATEUP>
 static hipError_t launch_tiled_one(const GemmParams& p, int64_t max_tasks, int num_cus, hipStream_t s) {
-  constexpr int lds = Tiled<DT>::NS * stage_bytes<DT>();
+  constexpr int lds = lds_bytes<DT>();
+  constexpr int threads = Tiled<DT>::NW * 64;
   static int per_cu = 0;
   if (per_cu == 0) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled_kernel<DT, GATEUP>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_tiled_kernel<DT, GATEUP>, 256, lds) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_tiled_kernel<DT, GATEUP>, threads, lds) !=
+            hipSuccess ||
         occ <= 0)
       occ = 1;
     per_cu = occ;
   }
   const int64_t grid = std::min<int64_t>(max_tasks, (int64_t)num_cus * per_cu);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_tiled_kernel<DT, GATEUP>), dim3((unsigned)grid), dim3(256), lds, s, p);
+  hipLaunchKernelGGL((gemm_tiled_kernel<DT, GATEUP>), dim3((unsigned)grid), dim3(threads), lds, s, p);
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@
 // columns: 128 h columns of gate+up, or 256 output columns of down).  Each
 // super-step (128 bytes of K) of the task's weight panels and activation rows
 // is copied HBM -> LDS by the buffer unit directly (no registers), into a ring
-// of NS stages; the four waves then read their MFMA fragments from LDS, so a
+// of NS stages; the waves then read their MFMA fragments from LDS, so a
 // weight byte is fetched once per tile and shared by every row of it.  The
 // copy engine's LDS writes are invisible to the compiler, so the kernel
 // orders them itself: it waits until only the younger stages are outstanding
@@ -26,9 +26,10 @@
 // rows of an MFMA fragment read spread over all banks), then (FP8) the per-row
 // activation scale of the super-step.
 //
-// bf16: tile 256 x 256, 4 waves as 2 x 2 of 128 rows x 4 panels, MFMA
-//       32x32x16, 256 fp32 accumulators per lane; ring of 4 half-super-step
-//       slots (128 KiB), three in flight while one is multiplied.
+// bf16: tile 256 x 256, 8 waves (two per SIMD) as 4 x 2 of 64 rows x 4
+//       panels, MFMA 32x32x16, 128 fp32 accumulators per lane; ring of 4
+//       half-super-step slots (128 KiB), three in flight while one is
+//       multiplied.
 // FP8:  tile 128 x 256, 8 waves (two per SIMD) as 2 x 4 of 64 rows x 2
 //       panels, MFMA 16x16x128 -- one MFMA spans a whole 128-deep scale block,
 //       so each product is added straight into the accumulators times (token
@@ -48,9 +49,19 @@ namespace {
 // SUB = ring slots per super-step (a slot holds 128/SUB bytes of K per row).
 template <int DT>
 struct Tiled;
+#ifndef AFD_TILED_BF16_NW
+#define AFD_TILED_BF16_NW 8
+#endif
+#ifndef AFD_TILED_BF16_WM
+#define AFD_TILED_BF16_WM 4
+#endif
+#ifndef AFD_TILED_BF16_NS
+#define AFD_TILED_BF16_NS 4
+#endif
 template <>
 struct Tiled<kBF16> {
-  static constexpr int NW = 4, WM = 2, WN = 2, BM = 256, NS = 4, SUB = 2;
+  static constexpr int NW = AFD_TILED_BF16_NW, WM = AFD_TILED_BF16_WM, WN = NW / WM, BM = 256,
+                       NS = AFD_TILED_BF16_NS, SUB = 2;
 };
 template <>
 struct Tiled<kFP8> {

@@ -1,0 +1,44 @@
+"""Host-side checks of bench.py: the one-GPU guard and the algorithmic units."""
+import importlib.util
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_units_hand_counted():
+    b = _bench()
+    # 3 tokens, top-2 over 4 experts; expert 3 empty, one dropped slot (-1)
+    ids = np.array([[0, 1], [1, -1], [2, 0]], dtype=np.int32)
+    T, H, I, E, K = 3, 8, 16, 4, 2
+    cfg = dict(T=T, H=H, I=I, E=E, K=K, dtype="bf16")
+    u = b.algorithmic_units(cfg, ids)
+    assert u["N"] == 5 and u["Ns"] == 5 and u["nonempty"] == 3
+    assert u["gu_bytes"] == 3 * 2 * H * I * 2 + T * H * 2 + 5 * I * 2
+    assert u["dn_bytes"] == 3 * I * H * 2 + 5 * I * 2 + 5 * H * 2
+    assert u["layer_bytes"] == 3 * 3 * H * I * 2 + T * H * 2 + T * H * 2 + T * K * 8
+    assert u["gu_flops"] == 4.0 * H * I * 5 and u["layer_flops"] == 6.0 * H * I * 5
+
+    # a shared expert adds T rows and one always-read expert; FP8 adds scales
+    cfg = dict(T=T, H=128, I=128, E=E, K=K, dtype="fp8", shared_inter=128)
+    u = b.algorithmic_units(cfg, ids)
+    assert u["Ns"] == 5 + T and u["nonempty"] == 4
+    w = 128 * 128 * (1 + 4.0 / (128 * 128))
+    assert abs(u["gu_bytes"] - (4 * 2 * w + T * 128 * (1 + 4.0 / 128) + 8 * 128 * (1 + 4.0 / 128))) < 1e-6

@@ -80,7 +80,10 @@ typedef enum {
  *   sh_s_gate, sh_s_up [H/128, shared_inter/128], sh_s_down [shared_inter/128, H/128].
  *
  * Limits: 1 <= E <= 512, 1 <= K <= 32, 1 <= max_tokens, max_tokens*K < 2^26;
- * H and I multiples of 128 for every dtype.
+ * H and I multiples of 128 for every dtype (block-FP8: at most 16384); the
+ * activation buffers (max_tokens*K (+ max_tokens with a shared expert) rows of
+ * max(H, I) elements, and max_tokens rows of H) below 2^31 - 2^24 bytes each.
+ * A configuration outside these limits is rejected with AFD_ERR_UNSUPPORTED.
  */
 typedef struct {
     int32_t hidden;        /* H                                                */

@@ -75,6 +75,11 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until this wave's LDS reads have returned (lgkmcnt(0); vmcnt and
+// expcnt left at their no-wait maxima): a slot may be refilled by another
+// wave's copy once every wave has passed the next barrier.
+__device__ inline void lds_reads_done() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
 // Workgroup barrier without the memory-model fence __syncthreads adds (which
 // would wait for every in-flight load); the empty asm keeps the compiler from
 // moving memory operations across it.

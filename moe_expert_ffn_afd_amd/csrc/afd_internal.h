@@ -29,14 +29,18 @@
 //  128-deep scale block and one panel lies inside one 128-column block.
 //
 //  Workspace (per handle, sized for max_tokens T_max; N_max = T_max * K):
-//    counts[E], offsets[E+1], err[1], num_mtiles[1]
+//    counts[E], offsets[E+1], err[1], num_mtiles[2]
 //    chunk_base[n_chunks][E]          first sorted row of each (chunk, expert)
 //    sorted_assign[N_max], row_of[N_max]
 //    mtiles[max_mtiles] (int4) x 2    light and heavy lists {expert, first row, rows, 0}
 //    h   [N_max + T_max, I]           routed rows in sorted order, then the
 //                                     shared expert's rows (token order) at
-//                                     row N_max; bf16 | e4m3 (+ scales
-//                                     [rows, I/128] fp32) | fp32
+//                                     row N_max; bf16 | e4m3 | fp32
+//    FP8 activation scales, step-major over the same rows (one 128-deep
+//    block per "step", so a tile's scales of one step are contiguous):
+//    xs  [H/128][N_max + T_max]       the caller's 1x128 hidden scales,
+//                                     gathered into sorted-row order
+//    hs  [I/128][N_max + T_max]       h's 1x128 scales
 //    y   [N_max + T_max, H]           expert outputs (unweighted), same rows;
 //                                     bf16 | fp32
 #pragma once
@@ -90,9 +94,9 @@ struct GemmParams {
   const uint8_t* a;              // activation rows
   int64_t a_bytes;               // size of the activation buffer (< 2^31)
   int64_t a_row_bytes;
-  const float* a_scales;         // fp8: [rows, K/128]
+  const float* a_scales;         // fp8: step-major [K/128][a_scale_ld], sorted-row order
   int64_t a_scale_bytes;
-  int32_t a_scale_ld;
+  int32_t a_scale_ld;            // rows per step of a_scales
   const uint8_t* b;              // packed weights
   int64_t b_expert_bytes;
   int64_t b_panel_bytes;
@@ -105,8 +109,22 @@ struct GemmParams {
   int32_t n_panels;              // panels of one output matrix (I/32 or H/32)
   uint8_t* c;                    // output rows
   int64_t c_row_bytes;
-  float* c_scales;               // fp8 gate/up: h scales [rows, I/128]
+  float* c_scales;               // fp8 gate/up: h scales, step-major [I/128][c_scale_ld]
   int32_t c_scale_ld;
+};
+
+struct ScaleGatherParams {
+  const float* src;              // caller's hidden scales [T][ks]
+  int32_t ks;                    // H / 128
+  int32_t tokens;                // T
+  int32_t top_k;
+  const int32_t* sorted_assign;  // row -> flat slot
+  const int32_t* offsets;        // offsets[E] = routed rows
+  int32_t num_experts;
+  int32_t routed_max;            // T * K of this call (upper bound of the routed rows)
+  int32_t shared_row0;           // N_max with a shared expert, else -1
+  float* dst;                    // [ks][ld]
+  int32_t ld;
 };
 
 struct CombineParams {
@@ -136,11 +154,18 @@ struct F32Params {
 // launchers (return hipError_t of the launch)
 hipError_t launch_dispatch_count_scan(const DispatchParams& p, hipStream_t s);
 hipError_t launch_dispatch_scatter(const DispatchParams& p, hipStream_t s);
+hipError_t launch_gather_scales(const ScaleGatherParams& p, hipStream_t s);
+// bf16 only: streaming (gemm.hip) and LDS-tiled (gemm_tiled.hip) GEMMs
 hipError_t launch_gemm(int dtype, bool gate_up, int mr, const GemmParams& p, int64_t max_tasks,
                        int num_cus, hipStream_t s);
 hipError_t launch_gemm_tiled(int dtype, bool gate_up, const GemmParams& p, int64_t max_tasks, int num_cus,
                              hipStream_t s);
 int tiled_rows(int dtype);  // m-tile rows of the LDS-tiled GEMM
+// Block-FP8 GEMM with a weight ring in LDS (gemm_ring.hip): heavy = m-tiles of
+// up to ring_rows(true) rows, else up to ring_rows(false)
+hipError_t launch_gemm_ring(bool gate_up, bool heavy, const GemmParams& p, int64_t max_tasks, int num_cus,
+                            hipStream_t s);
+int ring_rows(bool heavy);
 hipError_t launch_gemm_f32(bool gate_up, const F32Params& p, int grid, hipStream_t s);
 hipError_t launch_combine(int dtype, const CombineParams& p, int tokens, hipStream_t s);
 hipError_t launch_pack(int dtype, bool gate_up, const void* w_first, const void* w_second,

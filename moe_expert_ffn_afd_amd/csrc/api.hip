@@ -87,7 +87,9 @@ struct afd_ffn {
   int4* mtiles = nullptr;
   int4* mtiles_heavy = nullptr;
   uint8_t* h = nullptr;
-  float* h_scales = nullptr;
+  float* h_scales = nullptr;   // FP8: [I/128][h_rows] step-major
+  float* x_scales = nullptr;   // FP8: [H/128][h_rows] hidden scales in sorted-row order
+  int64_t h_rows = 0;
   uint8_t* y = nullptr;
   int max_chunks = 0, max_mtiles = 0;
   int last_T = 0;
@@ -120,6 +122,14 @@ afd_status check_config(const afd_ffn_config* c) {
     return fail(AFD_ERR_UNSUPPORTED, "max_tokens * top_k must stay below 2^26");
   if (c->shared_inter < 0 || (c->shared_inter > 0 && c->shared_inter != c->inter))
     return fail(AFD_ERR_UNSUPPORTED, "shared_inter must be 0 or equal to inter");
+  {
+    // the GEMMs address activation rows (hidden, h) with 32-bit buffer offsets
+    const int64_t es = c->dtype == kF32 ? 4 : c->dtype == kBF16 ? 2 : 1;
+    const int64_t rows = (int64_t)c->max_tokens * c->top_k + (c->shared_inter > 0 ? c->max_tokens : 0);
+    const int64_t lim = (1ll << 31) - (1ll << 24);
+    if (rows * std::max(c->hidden, c->inter) * es > lim || (int64_t)c->max_tokens * c->hidden * es > lim)
+      return fail(AFD_ERR_UNSUPPORTED, "activation buffers of max_tokens=%d exceed 2 GiB", c->max_tokens);
+  }
   if (c->device < 0) return fail(AFD_ERR_INVALID_ARG, "device must be >= 0");
   if (!c->w_gate || !c->w_up || !c->w_down) return fail(AFD_ERR_INVALID_ARG, "weight pointer is NULL");
   const bool fp8 = c->dtype == kFP8;
@@ -148,7 +158,8 @@ afd_status alloc_workspace(afd_ffn* a) {
                 o_nmt = take(8), o_cb = take(4ll * a->max_chunks * a->E), o_sa = take(4 * nmax),
                 o_ro = take(4 * nmax), o_mt = take(16ll * a->max_mtiles), o_mth = take(16ll * a->max_mtiles),
                 o_h = take(rows * a->I * es),
-                o_hs = take(a->dtype == kFP8 ? rows * (a->I / 128) * 4 : 0), o_y = take(rows * a->H * ys);
+                o_hs = take(a->dtype == kFP8 ? rows * (a->I / 128) * 4 : 0),
+                o_xs = take(a->dtype == kFP8 ? rows * (a->H / 128) * 4 : 0), o_y = take(rows * a->H * ys);
   if (hipMalloc((void**)&a->ws, off) != hipSuccess) {
     (void)hipGetLastError();
     a->ws = nullptr;
@@ -165,6 +176,8 @@ afd_status alloc_workspace(afd_ffn* a) {
   a->mtiles_heavy = (int4*)(a->ws + o_mth);
   a->h = a->ws + o_h;
   a->h_scales = a->dtype == kFP8 ? (float*)(a->ws + o_hs) : nullptr;
+  a->x_scales = a->dtype == kFP8 ? (float*)(a->ws + o_xs) : nullptr;
+  a->h_rows = rows;
   a->y = a->ws + o_y;
   AFD_HIP(hipMemset(a->ws, 0, off));
   return AFD_OK;
@@ -360,13 +373,17 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   const int E = a->E, K = a->K, H = a->H, I = a->I, dt = a->dtype;
   const int64_t n_flat = (int64_t)T * K;
   const int64_t nmax = (int64_t)a->Tmax * K;
-  // Light experts (rows <= bm_light, one m-tile) stream their weights through
-  // registers (gemm.hip); heavier experts (and the shared expert) take the
-  // LDS-tiled GEMM (gemm_tiled.hip), which fetches each weight panel once per
-  // tile of tiled_rows() rows.  fp32 uses light tiles of 32 rows only.
+  // Light experts (rows <= bm_light, one m-tile) and heavier ones (and the
+  // shared expert) go to two tile lists.  bf16: light experts stream their
+  // weights through registers (gemm.hip), heavy ones take the LDS-tiled GEMM
+  // (gemm_tiled.hip), which fetches each weight panel once per tile of
+  // tiled_rows() rows.  Block-FP8: both lists run the weight-ring GEMM
+  // (gemm_ring.hip), light tiles (<= 64 rows) and heavy tiles of
+  // ring_rows(true) rows.  fp32 uses light tiles of 32 rows only.
   const int mr = dt == kF32 ? 1 : (n_flat <= 32ll * E ? 1 : 2);
   const int bm = 32 * mr;
-  const int bm_heavy = dt == kF32 ? bm : tiled_rows(dt);
+  const bool fp8 = dt == kFP8;
+  const int bm_heavy = dt == kF32 ? bm : fp8 ? ring_rows(true) : tiled_rows(dt);
   const int heavy_min = dt == kF32 ? 0x7fffffff : bm + 1;
   std::vector<hipEvent_t> ev;
   auto mark = [&]() -> afd_status {
@@ -412,6 +429,21 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     return AFD_OK;
   }
   AFD_HIP(launch_dispatch_scatter(d, s));
+  if (dt == kFP8) {
+    ScaleGatherParams sg{};
+    sg.src = hidden_scales;
+    sg.ks = H / 128;
+    sg.tokens = T;
+    sg.top_k = K;
+    sg.sorted_assign = a->sorted_assign;
+    sg.offsets = a->offsets;
+    sg.num_experts = E;
+    sg.routed_max = (int32_t)n_flat;
+    sg.shared_row0 = a->S ? (int32_t)nmax : -1;
+    sg.dst = a->x_scales;
+    sg.ld = (int32_t)a->h_rows;
+    AFD_HIP(launch_gather_scales(sg, s));
+  }
   if ((st = mark())) return st;
 
   // upper bounds of the routed + shared m-tiles of this call, per list
@@ -461,9 +493,9 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.a = (const uint8_t*)hidden;
     g.a_bytes = (int64_t)T * H * es;
     g.a_row_bytes = (int64_t)H * es;
-    g.a_scales = hidden_scales;
-    g.a_scale_bytes = dt == kFP8 ? (int64_t)T * (H / 128) * 4 : 0;
-    g.a_scale_ld = H / 128;
+    g.a_scales = a->x_scales;  // gathered by gather_scales_kernel
+    g.a_scale_bytes = fp8 ? (int64_t)(H / 128) * a->h_rows * 4 : 0;
+    g.a_scale_ld = (int32_t)a->h_rows;
     g.b = a->w->gu;
     g.b_expert_bytes = a->w->gu_expert_bytes;
     g.b_panel_bytes = a->w->gu_panel_bytes;
@@ -477,15 +509,21 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.c = a->h;
     g.c_row_bytes = rows_ld_h;
     g.c_scales = a->h_scales;
-    g.c_scale_ld = I / 128;
+    g.c_scale_ld = (int32_t)a->h_rows;
     {
       GemmParams gh = g;
       gh.mtiles = a->mtiles_heavy;
       gh.num_mtiles = a->num_mtiles + 1;
       gh.n_groups = (2 * I / 32) / 8;
-      AFD_HIP(launch_gemm_tiled(dt, true, gh, mth_bound * gh.n_groups, a->num_cus, s));
+      if (fp8)
+        AFD_HIP(launch_gemm_ring(true, true, gh, mth_bound * gh.n_groups, a->num_cus, s));
+      else
+        AFD_HIP(launch_gemm_tiled(dt, true, gh, mth_bound * gh.n_groups, a->num_cus, s));
     }
-    AFD_HIP(launch_gemm(dt, true, mr, g, mt_bound * g.n_groups, a->num_cus, s));
+    if (fp8)
+      AFD_HIP(launch_gemm_ring(true, false, g, mt_bound * g.n_groups, a->num_cus, s));
+    else
+      AFD_HIP(launch_gemm(dt, true, mr, g, mt_bound * g.n_groups, a->num_cus, s));
     if ((st = mark())) return st;
     // down: A = h rows in sorted order
     g.gather = 0;
@@ -493,8 +531,8 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.a_bytes = h_rows * rows_ld_h;
     g.a_row_bytes = rows_ld_h;
     g.a_scales = a->h_scales;
-    g.a_scale_bytes = dt == kFP8 ? h_rows * (I / 128) * 4 : 0;
-    g.a_scale_ld = I / 128;
+    g.a_scale_bytes = fp8 ? h_rows * (I / 128) * 4 : 0;
+    g.a_scale_ld = (int32_t)a->h_rows;
     g.b = a->w->dn;
     g.b_expert_bytes = a->w->dn_expert_bytes;
     g.b_panel_bytes = a->w->dn_panel_bytes;
@@ -514,9 +552,15 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
       gh.mtiles = a->mtiles_heavy;
       gh.num_mtiles = a->num_mtiles + 1;
       gh.n_groups = (H / 32 + 7) / 8;
-      AFD_HIP(launch_gemm_tiled(dt, false, gh, mth_bound * gh.n_groups, a->num_cus, s));
+      if (fp8)
+        AFD_HIP(launch_gemm_ring(false, true, gh, mth_bound * gh.n_groups, a->num_cus, s));
+      else
+        AFD_HIP(launch_gemm_tiled(dt, false, gh, mth_bound * gh.n_groups, a->num_cus, s));
     }
-    AFD_HIP(launch_gemm(dt, false, mr, g, mt_bound * g.n_groups, a->num_cus, s));
+    if (fp8)
+      AFD_HIP(launch_gemm_ring(false, false, g, mt_bound * g.n_groups, a->num_cus, s));
+    else
+      AFD_HIP(launch_gemm(dt, false, mr, g, mt_bound * g.n_groups, a->num_cus, s));
     if ((st = mark())) return st;
   }
 

@@ -20,6 +20,8 @@
 // of the lower lanes), waves are ordered through per-wave counts in LDS, and
 // rounds of 1024 slots advance per-expert cursors, so every slot lands at its
 // stable position with no order-dependent atomics.
+#include <algorithm>
+
 #include "afd_internal.h"
 
 namespace afd {
@@ -199,6 +201,36 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_scatter_kernel(Disp
     if (valid && rank == 0) wcnt[wave * E + e] = 0;
     __syncthreads();
   }
+}
+
+// Block-FP8 only: the caller's 1x128 activation scales [T][H/128], gathered
+// into the sorted rows of the gate/up GEMM and stored step-major
+// (dst[c][row]), so that one GEMM step reads a tile's scales as one contiguous
+// run.  One thread per (row, step c = blockIdx.y): coalesced stores, reads
+// from the small, cache-resident source.  blockIdx.z = 0: routed rows (token
+// of row r = sorted_assign[r] / K); 1: the shared expert's rows (token order).
+__global__ __launch_bounds__(256) void gather_scales_kernel(ScaleGatherParams p) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int c = blockIdx.y;
+  int row, token;
+  if (blockIdx.z == 0) {
+    if (i >= p.offsets[p.num_experts]) return;
+    row = i;
+    token = p.sorted_assign[i] / p.top_k;
+  } else {
+    if (i >= p.tokens) return;
+    row = p.shared_row0 + i;
+    token = i;
+  }
+  p.dst[(int64_t)c * p.ld + row] = p.src[(int64_t)token * p.ks + c];
+}
+
+hipError_t launch_gather_scales(const ScaleGatherParams& p, hipStream_t s) {
+  const int n = std::max(p.routed_max, p.shared_row0 >= 0 ? p.tokens : 0);
+  if (n <= 0 || p.ks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_scales_kernel, dim3((n + 255) / 256, p.ks, p.shared_row0 >= 0 ? 2 : 1), dim3(256), 0, s,
+                     p);
+  return hipGetLastError();
 }
 
 hipError_t launch_dispatch_count_scan(const DispatchParams& p, hipStream_t s) {

@@ -29,7 +29,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}
 METRIC = "routed tokens/s per MoE layer on 1 MI355X; % of MFMA/HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ("gemm.hip", "gemm_tiled.hip")
+KERNEL_SOURCES = ("gemm.hip", "gemm_tiled.hip", "gemm_ring.hip", "afd_device.h", "afd_internal.h")
 
 
 def kernel_source_hash() -> str:

@@ -63,6 +63,10 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int 
 __device__ inline void dma16_nt(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, voff, soff, 0, 2);
 }
+template <int AUX>
+__device__ inline void dma16_aux(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, voff, soff, 0, AUX);
+}
 __device__ inline void dma4(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 4, voff, soff, 0, 0);
 }

@@ -510,21 +510,11 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.c_row_bytes = rows_ld_h;
     g.c_scales = a->h_scales;
     g.c_scale_ld = (int32_t)a->h_rows;
-    {
-      GemmParams gh = g;
-      gh.mtiles = a->mtiles_heavy;
-      gh.num_mtiles = a->num_mtiles + 1;
-      gh.n_groups = (2 * I / 32) / 8;
-      if (fp8)
-        AFD_HIP(launch_gemm_ring(true, true, gh, mth_bound * gh.n_groups, a->num_cus, s));
-      else
-        AFD_HIP(launch_gemm_tiled(dt, true, gh, mth_bound * gh.n_groups, a->num_cus, s));
-    }
-    if (fp8)
-      AFD_HIP(launch_gemm_ring(true, false, g, mt_bound * g.n_groups, a->num_cus, s));
-    else
-      AFD_HIP(launch_gemm(dt, true, mr, g, mt_bound * g.n_groups, a->num_cus, s));
-    if ((st = mark())) return st;
+    GemmParams gu_light = g;
+    GemmParams gu_heavy = g;
+    gu_heavy.mtiles = a->mtiles_heavy;
+    gu_heavy.num_mtiles = a->num_mtiles + 1;
+    gu_heavy.n_groups = (2 * I / 32) / 8;
     // down: A = h rows in sorted order
     g.gather = 0;
     g.a = a->h;
@@ -547,20 +537,29 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.c_row_bytes = (int64_t)H * 2;
     g.c_scales = nullptr;
     g.c_scale_ld = 0;
-    {
-      GemmParams gh = g;
-      gh.mtiles = a->mtiles_heavy;
-      gh.num_mtiles = a->num_mtiles + 1;
-      gh.n_groups = (H / 32 + 7) / 8;
-      if (fp8)
-        AFD_HIP(launch_gemm_ring(false, true, gh, mth_bound * gh.n_groups, a->num_cus, s));
-      else
-        AFD_HIP(launch_gemm_tiled(dt, false, gh, mth_bound * gh.n_groups, a->num_cus, s));
-    }
-    if (fp8)
-      AFD_HIP(launch_gemm_ring(false, false, g, mt_bound * g.n_groups, a->num_cus, s));
-    else
-      AFD_HIP(launch_gemm(dt, false, mr, g, mt_bound * g.n_groups, a->num_cus, s));
+    GemmParams dn_light = g;
+    GemmParams dn_heavy = g;
+    dn_heavy.mtiles = a->mtiles_heavy;
+    dn_heavy.num_mtiles = a->num_mtiles + 1;
+    dn_heavy.n_groups = (H / 32 + 7) / 8;
+
+    auto heavy = [&](bool gate_up, const GemmParams& q, hipStream_t st_) -> hipError_t {
+      return fp8 ? launch_gemm_ring(gate_up, true, q, mth_bound * q.n_groups, a->num_cus, st_)
+                 : launch_gemm_tiled(dt, gate_up, q, mth_bound * q.n_groups, a->num_cus, st_);
+    };
+    auto light = [&](bool gate_up, const GemmParams& q, hipStream_t st_) -> hipError_t {
+      return fp8 ? launch_gemm_ring(gate_up, false, q, mt_bound * q.n_groups, a->num_cus, st_)
+                 : launch_gemm(dt, gate_up, mr, q, mt_bound * q.n_groups, a->num_cus, st_);
+    };
+    // Both lists on the caller's stream, heavy first.  (Running the light list
+    // on a second stream did not overlap the two: a heavy workgroup's LDS and
+    // registers leave no room for a light one on the same CU, and the mixed
+    // order only lengthened the tails.)
+    AFD_HIP(heavy(true, gu_heavy, s));
+    AFD_HIP(light(true, gu_light, s));
+    if ((st = mark())) return st;
+    AFD_HIP(heavy(false, dn_heavy, s));
+    AFD_HIP(light(false, dn_light, s));
     if ((st = mark())) return st;
   }
 

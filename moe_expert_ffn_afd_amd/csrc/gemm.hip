@@ -38,8 +38,12 @@ using namespace dev;
 #ifndef AFD_XCD_REMAP
 #define AFD_XCD_REMAP 0
 #endif
-#ifndef AFD_STAGES
-#define AFD_STAGES 2
+// register stages per wave, by row fragments per tile
+#ifndef AFD_STAGES_MR1
+#define AFD_STAGES_MR1 2
+#endif
+#ifndef AFD_STAGES_MR2
+#define AFD_STAGES_MR2 2
 #endif
 // cache policy of the weight loads: 2 = non-temporal (streamed once)
 #ifndef AFD_B_AUX
@@ -150,16 +154,20 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
                                                                     acc[mr][pp], 0, 0, 0);
       };
 
-      // AFD_STAGES register stages: the loads of step c + AFD_STAGES - 1 are
-      // issued, kept together by scheduling fences, ahead of step c's
-      // multiplies, so AFD_STAGES - 1 super-steps stay in flight per wave.
-      Stage<MR> st[AFD_STAGES];
+      // NST register stages: the loads of step c + NST - 1 are issued, kept
+      // together by scheduling fences, ahead of step c's multiplies, so
+      // NST - 1 super-steps stay in flight per wave.
+      constexpr int NST = MR == 1 ? AFD_STAGES_MR1 : AFD_STAGES_MR2;
+      Stage<MR> st[NST];
 #pragma unroll
-      for (int i = 0; i + 1 < AFD_STAGES; ++i) load(st[i], i);
-      for (int c0 = 0; c0 < ks; c0 += AFD_STAGES) {
+      for (int i = 0; i + 1 < NST; ++i) {
+        load(st[i], i);
+        AFD_PIPE_FENCE();  // a stage's loads stay together, also here (in-order wait counts)
+      }
+      for (int c0 = 0; c0 < ks; c0 += NST) {
 #pragma unroll
-        for (int i = 0; i < AFD_STAGES; ++i) {
-          load(st[(i + AFD_STAGES - 1) % AFD_STAGES], c0 + i + AFD_STAGES - 1);
+        for (int i = 0; i < NST; ++i) {
+          load(st[(i + NST - 1) % NST], c0 + i + NST - 1);
           AFD_PIPE_FENCE();
           compute(st[i]);
           AFD_PIPE_FENCE();

@@ -51,6 +51,9 @@ namespace {
 #ifndef AFD_RING_NS
 #define AFD_RING_NS 4
 #endif
+#ifndef AFD_RING_B_AUX
+#define AFD_RING_B_AUX 0  // cache policy of the weight copies
+#endif
 #ifndef AFD_RING_XCD_REMAP
 #define AFD_RING_XCD_REMAP 1
 #endif
@@ -167,8 +170,8 @@ __global__ __launch_bounds__(kRingWaves * 64, 1) void gemm_ring_kernel(GemmParam
 #pragma unroll
       for (int k = 0; k < B_DMA; ++k) {
         const int i = wave * B_DMA + k, panel = i / 4, j = i % 4;
-        dma16(rb, st + panel * kStepPanelBytes + j * 1024, lane * 16,
-              in ? pbase + panel * bpanel + c * kStepPanelBytes + j * 1024 : oobB);
+        dma16_aux<AFD_RING_B_AUX>(rb, st + panel * kStepPanelBytes + j * 1024, lane * 16,
+                                  in ? pbase + panel * bpanel + c * kStepPanelBytes + j * 1024 : oobB);
       }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {

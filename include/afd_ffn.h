@@ -82,7 +82,8 @@ typedef enum {
  * Limits: 1 <= E <= 512, 1 <= K <= 32, 1 <= max_tokens, max_tokens*K < 2^26;
  * H and I multiples of 128 for every dtype (block-FP8: at most 16384); the
  * activation buffers (max_tokens*K (+ max_tokens with a shared expert) rows of
- * max(H, I) elements, and max_tokens rows of H) below 2^31 - 2^24 bytes each.
+ * max(H, I) elements and of H bf16/fp32 outputs, and max_tokens rows of H)
+ * below 2^31 - 2^24 bytes each.
  * A configuration outside these limits is rejected with AFD_ERR_UNSUPPORTED.
  */
 typedef struct {

@@ -129,6 +129,7 @@ struct ScaleGatherParams {
 
 struct CombineParams {
   const uint8_t* y;        // [rows, H] bf16 | f32
+  int64_t y_bytes;         // size of y (< 2^31)
   const int32_t* row_of;   // [T, K]
   const float* weights;    // [T, K]
   int32_t top_k;

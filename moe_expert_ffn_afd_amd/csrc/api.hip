@@ -123,11 +123,13 @@ afd_status check_config(const afd_ffn_config* c) {
   if (c->shared_inter < 0 || (c->shared_inter > 0 && c->shared_inter != c->inter))
     return fail(AFD_ERR_UNSUPPORTED, "shared_inter must be 0 or equal to inter");
   {
-    // the GEMMs address activation rows (hidden, h) with 32-bit buffer offsets
+    // the GEMMs and the combine address rows (hidden, h, y) with 32-bit buffer offsets
     const int64_t es = c->dtype == kF32 ? 4 : c->dtype == kBF16 ? 2 : 1;
     const int64_t rows = (int64_t)c->max_tokens * c->top_k + (c->shared_inter > 0 ? c->max_tokens : 0);
     const int64_t lim = (1ll << 31) - (1ll << 24);
-    if (rows * std::max(c->hidden, c->inter) * es > lim || (int64_t)c->max_tokens * c->hidden * es > lim)
+    const int64_t ys = c->dtype == kF32 ? 4 : 2;  // expert outputs y are bf16 | fp32
+    if (rows * std::max(c->hidden, c->inter) * es > lim || (int64_t)c->max_tokens * c->hidden * es > lim ||
+        rows * c->hidden * ys > lim)
       return fail(AFD_ERR_UNSUPPORTED, "activation buffers of max_tokens=%d exceed 2 GiB", c->max_tokens);
   }
   if (c->device < 0) return fail(AFD_ERR_INVALID_ARG, "device must be >= 0");
@@ -565,6 +567,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
 
   CombineParams cp{};
   cp.y = a->y;
+  cp.y_bytes = (nmax + (a->S ? a->Tmax : 0)) * (int64_t)H * (dt == kF32 ? 4 : 2);
   cp.row_of = a->row_of;
   cp.weights = topk_weights;
   cp.top_k = K;

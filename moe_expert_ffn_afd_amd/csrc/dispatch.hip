@@ -72,12 +72,24 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
   if (tid == 0) bad = 0;
   __syncthreads();
 
-  for (int f = tid; f < p.n_flat; f += kDispatchThreads) {
-    int e = p.ids[f];
-    if (e >= 0 && e < E)
-      atomicAdd(&cc[(f >> p.chunk_shift) * E + e], 1);
-    else if (e != -1)
-      atomicAdd(&bad, 1);
+  // 8 id loads in flight per thread, then their LDS increments
+  constexpr int kU = 8;
+  for (int f0 = 0; f0 < p.n_flat; f0 += kU * kDispatchThreads) {
+    int ev[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int f = f0 + u * kDispatchThreads + tid;
+      ev[u] = f < p.n_flat ? p.ids[f] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int f = f0 + u * kDispatchThreads + tid;
+      const int e = ev[u];
+      if (e >= 0 && e < E)
+        atomicAdd(&cc[(f >> p.chunk_shift) * E + e], 1);
+      else if (e != -1)
+        atomicAdd(&bad, 1);
+    }
   }
   __syncthreads();
 

@@ -31,6 +31,14 @@ SMALL_CASES = {
     "fp8_mr1": (small("fp8", 33, 512, 256, 16, 2), 5),
     "fp8_shared_multi_tile": (small("fp8", 70, 512, 384, 5, 3, shared=384), 6),
     "fp8_local_shard": (small("fp8", 200, 256, 384, 4, 8, routing="local_shard", global_experts=32), 7),
+    # top-k at its limit (32) plus a shared expert: 33 rows per token in the combine; H = 384
+    # leaves the last group of 8 down panels half full
+    "bf16_k32_shared_h384": (small("bf16", 40, 384, 256, 64, 32, shared=256), 8),
+    "fp8_k32_shared_h384": (small("fp8", 40, 384, 256, 64, 32, shared=256), 9),
+    # heavy experts over several m-tiles with ragged last tiles (bf16: 256-row tiles,
+    # block-FP8: 128-row tiles)
+    "bf16_heavy_ragged": (small("bf16", 600, 256, 256, 4, 2), 10),
+    "fp8_heavy_ragged": (small("fp8", 300, 256, 256, 4, 2), 11),
 }
 
 

@@ -469,7 +469,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.kdim = H;
     g.ndim = I;
     g.c = (float*)a->h;
-    int grid = (int)std::min<int64_t>(mt_bound * ((I + 255) / 256), (int64_t)a->num_cus * occupancy_wgs);
+    int grid = (int)std::min<int64_t>(mt_bound * ((I + 63) / 64), (int64_t)a->num_cus * occupancy_wgs);
     AFD_HIP(launch_gemm_f32(true, g, grid, s));
     if ((st = mark())) return st;
     g.gather = 0;
@@ -479,7 +479,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.kdim = I;
     g.ndim = H;
     g.c = (float*)a->y;
-    grid = (int)std::min<int64_t>(mt_bound * ((H + 255) / 256), (int64_t)a->num_cus * occupancy_wgs);
+    grid = (int)std::min<int64_t>(mt_bound * ((H + 63) / 64), (int64_t)a->num_cus * occupancy_wgs);
     AFD_HIP(launch_gemm_f32(false, g, grid, s));
     if ((st = mark())) return st;
   } else {

@@ -87,6 +87,8 @@ struct DispatchParams {
 struct GemmParams {
   const int4* mtiles;
   const int32_t* num_mtiles;
+  const int4* mtiles2;           // block-FP8 ring GEMM: the heavy list, run before `mtiles`
+  const int32_t* num_mtiles2;
   const int32_t* sorted_assign;  // row -> flat slot (gate/up gather)
   int32_t top_k;
   int32_t shared_row0;           // rows >= this are shared-expert rows (token = row - shared_row0)
@@ -162,10 +164,10 @@ hipError_t launch_gemm(int dtype, bool gate_up, int mr, const GemmParams& p, int
 hipError_t launch_gemm_tiled(int dtype, bool gate_up, const GemmParams& p, int64_t max_tasks, int num_cus,
                              hipStream_t s);
 int tiled_rows(int dtype);  // m-tile rows of the LDS-tiled GEMM
-// Block-FP8 GEMM with a weight ring in LDS (gemm_ring.hip): heavy = m-tiles of
-// up to ring_rows(true) rows, else up to ring_rows(false)
-hipError_t launch_gemm_ring(bool gate_up, bool heavy, const GemmParams& p, int64_t max_tasks, int num_cus,
-                            hipStream_t s);
+// Block-FP8 GEMM with a weight ring in LDS (gemm_ring.hip): one launch over
+// the heavy list (mtiles2, m-tiles of up to ring_rows(true) rows) and then the
+// light list (mtiles, up to ring_rows(false) rows)
+hipError_t launch_gemm_ring(bool gate_up, const GemmParams& p, int64_t max_tasks, int num_cus, hipStream_t s);
 int ring_rows(bool heavy);
 hipError_t launch_gemm_f32(bool gate_up, const F32Params& p, int grid, hipStream_t s);
 hipError_t launch_combine(int dtype, const CombineParams& p, int tokens, hipStream_t s);

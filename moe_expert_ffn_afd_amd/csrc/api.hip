@@ -545,23 +545,25 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     dn_heavy.num_mtiles = a->num_mtiles + 1;
     dn_heavy.n_groups = (H / 32 + 7) / 8;
 
-    auto heavy = [&](bool gate_up, const GemmParams& q, hipStream_t st_) -> hipError_t {
-      return fp8 ? launch_gemm_ring(gate_up, true, q, mth_bound * q.n_groups, a->num_cus, st_)
-                 : launch_gemm_tiled(dt, gate_up, q, mth_bound * q.n_groups, a->num_cus, st_);
-    };
-    auto light = [&](bool gate_up, const GemmParams& q, hipStream_t st_) -> hipError_t {
-      return fp8 ? launch_gemm_ring(gate_up, false, q, mt_bound * q.n_groups, a->num_cus, st_)
-                 : launch_gemm(dt, gate_up, mr, q, mt_bound * q.n_groups, a->num_cus, st_);
-    };
     // Both lists on the caller's stream, heavy first.  (Running the light list
     // on a second stream did not overlap the two: a heavy workgroup's LDS and
     // registers leave no room for a light one on the same CU, and the mixed
-    // order only lengthened the tails.)
-    AFD_HIP(heavy(true, gu_heavy, s));
-    AFD_HIP(light(true, gu_light, s));
+    // order only lengthened the tails.)  Block-FP8 runs both lists in one
+    // launch of the ring GEMM.
+    auto stage = [&](bool gate_up, const GemmParams& light, const GemmParams& heavy) -> hipError_t {
+      if (fp8) {
+        GemmParams both = light;
+        both.mtiles2 = heavy.mtiles;
+        both.num_mtiles2 = heavy.num_mtiles;
+        return launch_gemm_ring(gate_up, both, (mt_bound + mth_bound) * light.n_groups, a->num_cus, s);
+      }
+      hipError_t e = launch_gemm_tiled(dt, gate_up, heavy, mth_bound * heavy.n_groups, a->num_cus, s);
+      if (e != hipSuccess) return e;
+      return launch_gemm(dt, gate_up, mr, light, mt_bound * light.n_groups, a->num_cus, s);
+    };
+    AFD_HIP(stage(true, gu_light, gu_heavy));
     if ((st = mark())) return st;
-    AFD_HIP(heavy(false, dn_heavy, s));
-    AFD_HIP(light(false, dn_light, s));
+    AFD_HIP(stage(false, dn_light, dn_heavy));
     if ((st = mark())) return st;
   }
 

@@ -71,8 +71,13 @@ __device__ inline int clamp31(int64_t v) { return v > 0x7fffffff ? 0x7fffffff : 
 
 }  // namespace
 
+// One task: m-tile `tile` (at most BM rows) x column group q.  Every wave of
+// the workgroup calls it with the same arguments.
 template <bool GATEUP, int BM>
-__global__ __launch_bounds__(kRingWaves * 64, 1) void gemm_ring_kernel(GemmParams p) {
+__device__ __forceinline__ void ring_task(const GemmParams& p, const int4 tile, const int q) {
+  // declared here, not passed in: the copies need pointers known to be in LDS
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
+  __shared__ float red[kRingWaves * 32];  // gate/up: per-wave token amax
   constexpr int NS = kRingNS;
   constexpr int WM = BM / 32, WN = kRingWaves / WM, NPW = kRingPanels / WN;
   constexpr int RT = 2;                                   // 16-row token tiles per wave
@@ -82,16 +87,12 @@ __global__ __launch_bounds__(kRingWaves * 64, 1) void gemm_ring_kernel(GemmParam
   constexpr int S_OFF = kRingWeightBytes;
   constexpr int SINK = NS * SLOT;
   static_assert(WM * WN == kRingWaves && NPW % 2 == 0 && NPW <= 4 && BM <= 256, "wave grid");
-  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
-  __shared__ float red[WM][WN][32];  // gate/up: per-wave token amax
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int kg = lane >> 4;  // which 32 bytes of the 128-deep block this lane carries
   const int tok = lane & 15;
-  const int num_mt = uniform(p.num_mtiles[0]);
-  const int num_tasks = num_mt * p.n_groups;
   const int ks = p.k_steps;
   const int nsr = (ks + NS - 1) / NS * NS;  // steps run: whole unrolled rounds
   const int oobA = clamp31(p.a_bytes), oobS = clamp31(p.a_scale_bytes);
@@ -100,26 +101,7 @@ __global__ __launch_bounds__(kRingWaves * 64, 1) void gemm_ring_kernel(GemmParam
   const auto ra = make_rsrc(p.a, p.a_bytes);
   const auto rsa = make_rsrc(p.a_scales, p.a_scale_bytes);
 
-  // blocks of kRingMB m-tiles x all column groups; workgroup ranks renumbered
-  // so that each XCD owns a contiguous run of tasks (shared rows stay in its L2)
-  const int G = gridDim.x;
-  const int rank = (AFD_RING_XCD_REMAP && G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds
-                                                          : blockIdx.x;
-  const int nq = p.n_groups;
-  const int full = (num_mt / kRingMB) * kRingMB * nq;
-  const int rem = num_mt % kRingMB;
-  for (int task = rank; task < num_tasks; task += G) {
-    int mt, q;
-    if (task < full) {
-      const int blk = task / (kRingMB * nq), w = task % (kRingMB * nq);
-      q = w / kRingMB;
-      mt = blk * kRingMB + w % kRingMB;
-    } else {
-      const int t = task - full;
-      q = t / rem;
-      mt = (num_mt / kRingMB) * kRingMB + t % rem;
-    }
-    const int4 tile = p.mtiles[mt];
+  {
     const int expert = uniform(tile.x), row0 = uniform(tile.y), rows = uniform(tile.z);
     const auto rb = make_rsrc(p.b + (int64_t)expert * p.b_expert_bytes, p.b_expert_bytes);
     const int pbase = uniform((int)((int64_t)q * kRingPanels * p.b_panel_bytes));
@@ -258,7 +240,7 @@ __global__ __launch_bounds__(kRingWaves * 64, 1) void gemm_ring_kernel(GemmParam
             }
         a = fmaxf(a, __shfl_xor(a, 16, 64));
         a = fmaxf(a, __shfl_xor(a, 32, 64));
-        if (kg == 0) red[wm][wn][rt * 16 + tok] = a;
+        if (kg == 0) red[(wm * WN + wn) * 32 + rt * 16 + tok] = a;
       }
       __syncthreads();
 #pragma unroll
@@ -267,7 +249,7 @@ __global__ __launch_bounds__(kRingWaves * 64, 1) void gemm_ring_kernel(GemmParam
         const int m = wm * 32 + mi;
         float amax = 0.0f;
 #pragma unroll
-        for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, red[wm][w2][mi]);
+        for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, red[(wm * WN + w2) * 32 + mi]);
         const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
         const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
         if (m < rows) {
@@ -311,16 +293,55 @@ __global__ __launch_bounds__(kRingWaves * 64, 1) void gemm_ring_kernel(GemmParam
   }
 }
 
-template <bool GATEUP, int BM>
+// Both tile lists in one persistent launch: the heavy list's tasks (m-tiles
+// of up to 128 rows), then the light list's (up to 64 rows), so a GEMM stage
+// has one tail instead of two.  Tasks run in blocks of kRingMB m-tiles x all
+// column groups; workgroup ranks are renumbered so that each XCD owns a
+// contiguous run of tasks (shared rows stay in its L2).
+template <bool GATEUP>
+__global__ __launch_bounds__(kRingWaves * 64, 1) void gemm_ring_kernel(GemmParams p) {
+  const int nq = p.n_groups;
+  const int nh = uniform(p.num_mtiles2 ? p.num_mtiles2[0] : 0);
+  const int nl = uniform(p.num_mtiles[0]);
+  const int th = nh * nq, tl = nl * nq;
+  const int G = gridDim.x;
+  const int rank = (AFD_RING_XCD_REMAP && G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds
+                                                          : blockIdx.x;
+  // task t of a list of n m-tiles -> (m-tile, column group)
+  auto decode = [&](int t, int n, int& mt, int& q) {
+    const int full = (n / kRingMB) * kRingMB * nq;
+    if (t < full) {
+      const int blk = t / (kRingMB * nq), w = t % (kRingMB * nq);
+      q = w / kRingMB;
+      mt = blk * kRingMB + w % kRingMB;
+    } else {
+      const int rem = n % kRingMB, u = t - full;
+      q = u / rem;
+      mt = (n / kRingMB) * kRingMB + u % rem;
+    }
+  };
+  for (int task = rank; task < th + tl; task += G) {
+    int mt, q;
+    if (task < th) {
+      decode(task, nh, mt, q);
+      ring_task<GATEUP, 128>(p, p.mtiles2[mt], q);
+    } else {
+      decode(task - th, nl, mt, q);
+      ring_task<GATEUP, 64>(p, p.mtiles[mt], q);
+    }
+  }
+}
+
+template <bool GATEUP>
 static hipError_t launch_ring_one(const GemmParams& p, int64_t max_tasks, int num_cus, hipStream_t s) {
   constexpr int lds = kRingLdsBytes;
   static int per_cu = 0;
   if (per_cu == 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_ring_kernel<GATEUP, BM>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_ring_kernel<GATEUP>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_ring_kernel<GATEUP, BM>, kRingWaves * 64, lds) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_ring_kernel<GATEUP>, kRingWaves * 64, lds) !=
             hipSuccess ||
         occ <= 0)
       occ = 1;
@@ -328,18 +349,14 @@ static hipError_t launch_ring_one(const GemmParams& p, int64_t max_tasks, int nu
   }
   const int64_t grid = std::min<int64_t>(max_tasks, (int64_t)num_cus * per_cu);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_ring_kernel<GATEUP, BM>), dim3((unsigned)grid), dim3(kRingWaves * 64), lds, s, p);
+  hipLaunchKernelGGL((gemm_ring_kernel<GATEUP>), dim3((unsigned)grid), dim3(kRingWaves * 64), lds, s, p);
   return hipGetLastError();
 }
 
 int ring_rows(bool heavy) { return heavy ? 128 : 64; }
 
-hipError_t launch_gemm_ring(bool gate_up, bool heavy, const GemmParams& p, int64_t max_tasks, int num_cus,
-                            hipStream_t s) {
-  if (heavy) return gate_up ? launch_ring_one<true, 128>(p, max_tasks, num_cus, s)
-                            : launch_ring_one<false, 128>(p, max_tasks, num_cus, s);
-  return gate_up ? launch_ring_one<true, 64>(p, max_tasks, num_cus, s)
-                 : launch_ring_one<false, 64>(p, max_tasks, num_cus, s);
+hipError_t launch_gemm_ring(bool gate_up, const GemmParams& p, int64_t max_tasks, int num_cus, hipStream_t s) {
+  return gate_up ? launch_ring_one<true>(p, max_tasks, num_cus, s) : launch_ring_one<false>(p, max_tasks, num_cus, s);
 }
 
 }  // namespace afd

@@ -158,7 +158,9 @@ struct F32Params {
 hipError_t launch_dispatch_count_scan(const DispatchParams& p, hipStream_t s);
 hipError_t launch_dispatch_scatter(const DispatchParams& p, hipStream_t s);
 hipError_t launch_gather_scales(const ScaleGatherParams& p, hipStream_t s);
-// bf16 only: streaming (gemm.hip) and LDS-tiled (gemm_tiled.hip) GEMMs
+// bf16 only: streaming (gemm.hip) and LDS-tiled (gemm_tiled.hip) GEMMs;
+// down_panels_per_task(mr): H panels of one streaming down task
+int down_panels_per_task(int mr);
 hipError_t launch_gemm(int dtype, bool gate_up, int mr, const GemmParams& p, int64_t max_tasks,
                        int num_cus, hipStream_t s);
 hipError_t launch_gemm_tiled(int dtype, bool gate_up, const GemmParams& p, int64_t max_tasks, int num_cus,

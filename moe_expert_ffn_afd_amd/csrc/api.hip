@@ -534,7 +534,10 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.b_scale_cols = H / 128;
     g.k_steps = (int32_t)((int64_t)I * es / kStepBytes);
     g.n_panels = H / 32;
-    g.n_groups = (H / 32 + 2 * kWaves - 1) / (2 * kWaves);
+    // light tasks of the down GEMM: down_panels_per_task(mr) H panels (bf16
+    // streaming GEMM) or 8 (block-FP8 ring GEMM, both lists)
+    const int dn_panels = fp8 ? 8 : down_panels_per_task(mr);
+    g.n_groups = (H / 32 + dn_panels - 1) / dn_panels;
     g.c = a->y;
     g.c_row_bytes = (int64_t)H * 2;
     g.c_scales = nullptr;

@@ -60,16 +60,23 @@ using namespace dev;
 
 namespace {
 
-template <int MR>
+template <int MR, int NPW>
 struct Stage {
   uint4 a[MR][4];
-  uint4 b[2][4];
+  uint4 b[NPW][4];
 };
 
 }  // namespace
 
+#ifndef AFD_DOWN_NPW
+#define AFD_DOWN_NPW 4  // panels per wave of the single-fragment down GEMM
+#endif
+
+// NPW = panels per wave: gate/up 2 (one gate + up pair), down AFD_DOWN_NPW
+// for single-fragment tiles (registers allow it there), else 2
 template <bool GATEUP, int MR>
 __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
+  constexpr int NPW = (GATEUP || MR > 1) ? 2 : AFD_DOWN_NPW;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 5;
@@ -96,7 +103,7 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
     const int row0 = uniform(tile.y);
     const int rows = uniform(tile.z);
     const int unit = q * kWaves + wave;
-    const bool active = GATEUP ? (unit < p.n_panels) : (2 * unit < p.n_panels);
+    const bool active = GATEUP ? (unit < p.n_panels) : (NPW * unit < p.n_panels);
 
     // activation rows (rows past the tile's count repeat its first row): one
     // 32-bit buffer offset per lane and row fragment; weights: SGPR offsets only
@@ -111,15 +118,15 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
     }
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b + (int64_t)expert * p.b_expert_bytes, p.b_expert_bytes);
-    const int boff = uniform((int)((int64_t)(2 * unit) * p.b_panel_bytes));
+    const int boff = uniform((int)((int64_t)(NPW * unit) * p.b_panel_bytes));
     const int bpanel = (int)p.b_panel_bytes;
     const int voffB = lane * 16;
 
-    f32x16 acc[MR][2];
+    f32x16 acc[MR][NPW];
 #pragma unroll
     for (int mr = 0; mr < MR; ++mr)
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
+      for (int pp = 0; pp < NPW; ++pp)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mr][pp][r] = 0.0f;
 
@@ -130,12 +137,12 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
       // phantom step adds exact zeros.
       const int oobA = (int)(p.a_bytes > 0x7fffffff ? 0x7fffffff : p.a_bytes);
       const int oobB = (int)p.b_expert_bytes;
-      auto load = [&](Stage<MR>& s, int c) {
+      auto load = [&](Stage<MR, NPW>& s, int c) {
         const bool in = c < ks;
         const int sb = in ? boff + c * kStepPanelBytes : oobB;
         const int sa = in ? c * kStepBytes : oobA;
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
+        for (int pp = 0; pp < NPW; ++pp)
 #pragma unroll
           for (int j = 0; j < 4; ++j) s.b[pp][j] = bload16<AFD_B_AUX>(rb, voffB, sb + pp * bpanel + j * 1024);
 #pragma unroll
@@ -143,13 +150,13 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) s.a[mr][j] = bload16(ra, aoff[mr], sa + j * 16);
       };
-      auto compute = [&](const Stage<MR>& s) {
+      auto compute = [&](const Stage<MR, NPW>& s) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int mr = 0; mr < MR; ++mr)
 #pragma unroll
-            for (int pp = 0; pp < 2; ++pp)
+            for (int pp = 0; pp < NPW; ++pp)
               acc[mr][pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(s.b[pp][j]), as_bf16x8(s.a[mr][j]),
                                                                     acc[mr][pp], 0, 0, 0);
       };
@@ -158,7 +165,7 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
       // together by scheduling fences, ahead of step c's multiplies, so
       // NST - 1 super-steps stay in flight per wave.
       constexpr int NST = MR == 1 ? AFD_STAGES_MR1 : AFD_STAGES_MR2;
-      Stage<MR> st[NST];
+      Stage<MR, NPW> st[NST];
 #pragma unroll
       for (int i = 0; i + 1 < NST; ++i) {
         load(st[i], i);
@@ -201,8 +208,9 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
         const int m = mr * 32 + col;
         if (m >= rows) continue;
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          uint8_t* out = p.c + (int64_t)(row0 + m) * p.c_row_bytes + (int64_t)(32 * (2 * unit + pp)) * 2;
+        for (int pp = 0; pp < NPW; ++pp) {
+          if (NPW * unit + pp >= p.n_panels) continue;
+          uint8_t* out = p.c + (int64_t)(row0 + m) * p.c_row_bytes + (int64_t)(32 * (NPW * unit + pp)) * 2;
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             const int n = 8 * r4 + 4 * g;
@@ -234,6 +242,8 @@ static hipError_t launch_one(const GemmParams& p, int64_t max_tasks, int num_cus
   hipLaunchKernelGGL((gemm_grouped_kernel<GATEUP, MR>), dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
+
+int down_panels_per_task(int mr) { return kWaves * (mr == 1 ? AFD_DOWN_NPW : 2); }
 
 hipError_t launch_gemm(int dtype, bool gate_up, int mr, const GemmParams& p, int64_t max_tasks, int num_cus,
                        hipStream_t s) {

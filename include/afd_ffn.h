@@ -79,6 +79,9 @@ typedef enum {
  *   sh_gate, sh_up [H, shared_inter], sh_down [shared_inter, H], and for FP8
  *   sh_s_gate, sh_s_up [H/128, shared_inter/128], sh_s_down [shared_inter/128, H/128].
  *
+ * Alignment: bf16 and e4m3 weights 16-byte aligned, fp32 weights and all
+ * scale arrays 4-byte aligned (otherwise AFD_ERR_INVALID_ARG).
+ *
  * Limits: 1 <= E <= 512, 1 <= K <= 32, 1 <= max_tokens, max_tokens*K < 2^26;
  * H and I multiples of 128 for every dtype (block-FP8: at most 16384); the
  * activation buffers (max_tokens*K (+ max_tokens with a shared expert) rows of
@@ -129,8 +132,10 @@ afd_status afd_ffn_clone(const afd_ffn_t *src, afd_ffn_t **out_handle);
  *   out            device [T, H]: fp32 for AFD_DTYPE_F32, else bf16; every
  *                  element is written (rows with no local expert and no shared
  *                  expert are 0).  Must not alias the inputs.
- * Asynchronous on `stream`; inputs and out must stay valid until the stream
- * work completes.  The dispatch (counts, offsets, permutation) of this call
+ * hidden and out must be 16-byte aligned; hidden_scales, topk_ids and
+ * topk_weights 4-byte aligned (otherwise AFD_ERR_INVALID_ARG, checked on the
+ * host).  Asynchronous on `stream`; inputs and out must stay valid until the
+ * stream work completes.  The dispatch (counts, offsets, permutation) of this call
  * stays in the handle's workspace until the next forward on the handle.
  */
 afd_status afd_ffn_forward(afd_ffn_t *handle, int32_t num_tokens, const void *hidden,

@@ -139,6 +139,17 @@ afd_status check_config(const afd_ffn_config* c) {
     return fail(AFD_ERR_INVALID_ARG, "block-FP8 weights need s_gate, s_up and s_down");
   if (!fp8 && (c->s_gate || c->s_up || c->s_down))
     return fail(AFD_ERR_INVALID_ARG, "weight scales are only used with AFD_DTYPE_FP8_BLOCK");
+  auto mis = [](const void* q, uintptr_t a) { return q && (reinterpret_cast<uintptr_t>(q) & (a - 1)); };
+  {
+    // bf16 / e4m3 weights are packed with 16-byte vector loads; fp32 ones are copied
+    const uintptr_t wa = c->dtype == kF32 ? 4 : 16;
+    if (mis(c->w_gate, wa) || mis(c->w_up, wa) || mis(c->w_down, wa) || mis(c->sh_gate, wa) ||
+        mis(c->sh_up, wa) || mis(c->sh_down, wa))
+      return fail(AFD_ERR_INVALID_ARG, "weights must be %d-byte aligned", (int)wa);
+  }
+  if (mis(c->s_gate, 4) || mis(c->s_up, 4) || mis(c->s_down, 4) || mis(c->sh_s_gate, 4) || mis(c->sh_s_up, 4) ||
+      mis(c->sh_s_down, 4))
+    return fail(AFD_ERR_INVALID_ARG, "weight scales must be 4-byte aligned");
   if (c->shared_inter > 0) {
     if (!c->sh_gate || !c->sh_up || !c->sh_down) return fail(AFD_ERR_INVALID_ARG, "shared expert weight is NULL");
     if (fp8 && (!c->sh_s_gate || !c->sh_s_up || !c->sh_s_down))
@@ -368,6 +379,13 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     return fail(AFD_ERR_INVALID_ARG, "block-FP8 input needs hidden_scales");
   if (a->dtype != kFP8 && hidden_scales)
     return fail(AFD_ERR_INVALID_ARG, "hidden_scales is only used with AFD_DTYPE_FP8_BLOCK");
+  {
+    auto mis = [](const void* q, uintptr_t al) { return q && (reinterpret_cast<uintptr_t>(q) & (al - 1)); };
+    if (mis(hidden, 16) || mis(out, 16))
+      return fail(AFD_ERR_INVALID_ARG, "hidden and out must be 16-byte aligned");
+    if (mis(hidden_scales, 4) || mis(topk_ids, 4) || mis(topk_weights, 4))
+      return fail(AFD_ERR_INVALID_ARG, "hidden_scales, topk_ids and topk_weights must be 4-byte aligned");
+  }
   DeviceGuard dg(a->device);
   if (!dg.ok) return fail(AFD_ERR_HIP, "cannot select device %d", a->device);
   hipStream_t s = (hipStream_t)stream;

@@ -54,10 +54,11 @@ def _cfg(**kw):
 
 def test_validate_config_accepts_good(lib):
     afd.afd_ffn_validate_config(_cfg())
+    afd.afd_ffn_validate_config(_cfg(dtype=afd.AFD_DTYPE_F32, w_gate=0x1004))  # fp32: 4-byte alignment
     # (2^17 - 4096) * 8 rows of 1024 bf16 = 1.94 GiB: still within 32-bit offsets
     afd.afd_ffn_validate_config(_cfg(max_tokens=(1 << 17) - 4096, top_k=8, hidden=1024, inter=1024))
     afd.afd_ffn_validate_config(_cfg(dtype=afd.AFD_DTYPE_FP8_BLOCK, s_gate=8, s_up=8, s_down=8))
-    afd.afd_ffn_validate_config(_cfg(shared_inter=512, sh_gate=8, sh_up=8, sh_down=8))
+    afd.afd_ffn_validate_config(_cfg(shared_inter=512, sh_gate=0x4000, sh_up=0x5000, sh_down=0x6000))
 
 
 @pytest.mark.parametrize("bad, status", [
@@ -77,6 +78,9 @@ def test_validate_config_accepts_good(lib):
     (dict(shared_inter=256), afd.AFD_ERR_UNSUPPORTED),                        # != inter
     (dict(shared_inter=512), afd.AFD_ERR_INVALID_ARG),                        # shared weights missing
     (dict(device=-1), afd.AFD_ERR_INVALID_ARG),
+    (dict(w_gate=0x1008), afd.AFD_ERR_INVALID_ARG),                          # bf16 weights need 16 bytes
+    (dict(dtype=afd.AFD_DTYPE_FP8_BLOCK, s_gate=8, s_up=8, s_down=6), afd.AFD_ERR_INVALID_ARG),  # scales 4
+    (dict(dtype=afd.AFD_DTYPE_F32, w_down=0x3002), afd.AFD_ERR_INVALID_ARG),  # fp32 weights need 4
     # activation rows beyond 32-bit buffer offsets: 2^20 * 8 rows of 512 bf16
     (dict(max_tokens=1 << 20, top_k=8), afd.AFD_ERR_UNSUPPORTED),
     # hidden rows alone: 2^18 tokens of 4096 bf16 = 2 GiB

@@ -136,8 +136,18 @@ def test_forward_rejects_bad_shapes_on_host():
     with pytest.raises(ValueError):
         layer.forward(big, None, torch.zeros((17, 2), dtype=torch.int32, device="cuda"),
                       torch.zeros((17, 2), device="cuda"))
-    st = afd.load().afd_ffn_forward(layer.handle, 17, None, None, None, None, None, None)
+    lib = afd.load()
+    st = lib.afd_ffn_forward(layer.handle, 17, None, None, None, None, None, None)
     assert st == afd.AFD_ERR_INVALID_ARG
+    # misaligned device pointers are refused before anything is enqueued
+    out = layer.out_like(16)
+    h, ids, w = p["hidden"].data_ptr(), p["ids"].data_ptr(), p["weights"].data_ptr()
+    for args in [(h + 2, ids, w, out.data_ptr()), (h, ids, w, out.data_ptr() + 8),
+                 (h, ids + 2, w, out.data_ptr()), (h, ids, w + 1, out.data_ptr())]:
+        st = lib.afd_ffn_forward(layer.handle, 16, args[0], None, args[1], args[2], args[3], None)
+        assert st == afd.AFD_ERR_INVALID_ARG
+        assert b"aligned" in lib.afd_ffn_last_error()
+    torch.cuda.synchronize()
     layer.close()
 
 

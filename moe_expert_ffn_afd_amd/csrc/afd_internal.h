@@ -166,6 +166,7 @@ hipError_t launch_gemm(int dtype, bool gate_up, int mr, const GemmParams& p, int
 hipError_t launch_gemm_tiled(int dtype, bool gate_up, const GemmParams& p, int64_t max_tasks, int num_cus,
                              hipStream_t s);
 int tiled_rows(int dtype);  // m-tile rows of the LDS-tiled GEMM
+int tiled_panels();         // weight panels of one LDS-tiled task
 // Block-FP8 GEMM with a weight ring in LDS (gemm_ring.hip): one launch over
 // the heavy list (mtiles2, m-tiles of up to ring_rows(true) rows) and then the
 // light list (mtiles, up to ring_rows(false) rows)

@@ -534,7 +534,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     GemmParams gu_heavy = g;
     gu_heavy.mtiles = a->mtiles_heavy;
     gu_heavy.num_mtiles = a->num_mtiles + 1;
-    gu_heavy.n_groups = (2 * I / 32) / 8;
+    gu_heavy.n_groups = (2 * I / 32 + tiled_panels() - 1) / tiled_panels();  // bf16 only
     // down: A = h rows in sorted order
     g.gather = 0;
     g.a = a->h;
@@ -564,7 +564,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     GemmParams dn_heavy = g;
     dn_heavy.mtiles = a->mtiles_heavy;
     dn_heavy.num_mtiles = a->num_mtiles + 1;
-    dn_heavy.n_groups = (H / 32 + 7) / 8;
+    dn_heavy.n_groups = (H / 32 + tiled_panels() - 1) / tiled_panels();  // bf16 only
 
     // Both lists on the caller's stream, heavy first.  (Running the light list
     // on a second stream did not overlap the two: a heavy workgroup's LDS and

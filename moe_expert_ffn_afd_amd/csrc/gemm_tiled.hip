@@ -62,7 +62,10 @@ namespace {
 // NW waves form a WM x WN grid over BM rows x 8 panels; SUB ring slots per
 // super-step (a slot holds 128/SUB bytes of K per row).
 constexpr int kNW = AFD_TILED_NW, kWM = AFD_TILED_WM, kWN = kNW / kWM, kBM = 256, kNS = AFD_TILED_NS, kSUB = 2;
-constexpr int kBNP = 8;  // panels per task
+#ifndef AFD_TILED_BNP
+#define AFD_TILED_BNP 8
+#endif
+constexpr int kBNP = AFD_TILED_BNP;  // panels per task
 constexpr int kMB = AFD_TILED_MB;
 constexpr int kStage = (kBNP * kStepPanelBytes + kBM * kStepBytes) / kSUB;
 constexpr int kLds = kNS * kStage;
@@ -286,6 +289,7 @@ static hipError_t launch_tiled_one(const GemmParams& p, int64_t max_tasks, int n
 }
 
 int tiled_rows(int dtype) { return dtype == kBF16 ? kBM : 0; }
+int tiled_panels() { return kBNP; }
 
 hipError_t launch_gemm_tiled(int dtype, bool gate_up, const GemmParams& p, int64_t max_tasks, int num_cus,
                              hipStream_t s) {

@@ -93,36 +93,6 @@ __device__ inline void raw_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Per-super-step weight block scales of one task, kept in registers: lane l
-// holds the scales of super-steps l and l + 64 (up to 128 super-steps), and
-// get*(c) broadcasts super-step c's with readlane.  Loaded once per task,
-// before the task's load pipeline starts, so the multiply loop issues no
-// memory operation that would make its in-order load waits drain the
-// prefetched stages.
-struct BlockScales {
-  float a0 = 0.0f, a1 = 0.0f, b0 = 0.0f, b1 = 0.0f;
-  __device__ inline void load(const float* s0, const float* s1, int ld, int ks, int lane) {
-    if (lane < ks) {
-      a0 = s0[(int64_t)lane * ld];
-      b0 = s1[(int64_t)lane * ld];
-    }
-    if (lane + 64 < ks) {
-      a1 = s0[(int64_t)(lane + 64) * ld];
-      b1 = s1[(int64_t)(lane + 64) * ld];
-    }
-    // retire these loads now, before the caller's pipeline issues its own:
-    // the loop's readlanes must not wait on them behind in-flight stages
-    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
-  }
-  __device__ inline float pick(float lo, float hi, int c) const {
-    // both lanes read, then a scalar select: no branch in the caller's loop
-    const int l = __builtin_amdgcn_readlane(__builtin_bit_cast(int, lo), c & 63);
-    const int h = __builtin_amdgcn_readlane(__builtin_bit_cast(int, hi), c & 63);
-    return __builtin_bit_cast(float, c < 64 ? l : h);
-  }
-  __device__ inline float get0(int c) const { return pick(a0, a1, c); }
-  __device__ inline float get1(int c) const { return pick(b0, b1, c); }
-};
 
 }  // namespace dev
 }  // namespace afd

@@ -104,6 +104,7 @@ struct GemmParams {
   int64_t b_panel_bytes;
   const float* b_scales0;        // fp8: gate (gate/up) or down scales
   const float* b_scales1;        // fp8: up scales (gate/up only)
+  int64_t b_scale_bytes;         // fp8: bytes of each block-scale array (all experts)
   int32_t b_scale_rows;          // K / 128
   int32_t b_scale_cols;          // N / 128 of one matrix
   int32_t k_steps;               // K / super-step

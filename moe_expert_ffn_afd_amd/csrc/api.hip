@@ -66,6 +66,7 @@ struct WeightStore {
   float* sd = nullptr;
   int64_t gu_expert_bytes = 0, dn_expert_bytes = 0;
   int64_t gu_panel_bytes = 0, dn_panel_bytes = 0;
+  int64_t scale_bytes = 0;  // fp8: bytes of each of sg, su, sd
   ~WeightStore() {
     for (void* p : {(void*)gu, (void*)up, (void*)dn, (void*)sg, (void*)su, (void*)sd})
       if (p) (void)hipFree(p);
@@ -242,6 +243,7 @@ afd_status pack_weights(const afd_ffn_config* c, afd_ffn* a) {
     if ((st = mal((uint8_t**)&w->sg, sblk * ES)) || (st = mal((uint8_t**)&w->su, sblk * ES)) ||
         (st = mal((uint8_t**)&w->sd, sblk * ES)))
       return st;
+    w->scale_bytes = sblk * ES;
     AFD_HIP(hipMemcpy(w->sg, c->s_gate, sblk * E, hipMemcpyDeviceToDevice));
     AFD_HIP(hipMemcpy(w->su, c->s_up, sblk * E, hipMemcpyDeviceToDevice));
     AFD_HIP(hipMemcpy(w->sd, c->s_down, sblk * E, hipMemcpyDeviceToDevice));
@@ -520,6 +522,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.b_expert_bytes = a->w->gu_expert_bytes;
     g.b_panel_bytes = a->w->gu_panel_bytes;
     g.b_scales0 = a->w->sg;
+    g.b_scale_bytes = a->w->scale_bytes;
     g.b_scales1 = a->w->su;
     g.b_scale_rows = H / 128;
     g.b_scale_cols = I / 128;

@@ -15,22 +15,28 @@
 // into a ring of NS slots, so NS-1 super-steps (96 KiB at NS = 4) are in flight
 // per CU without holding a register.  The activation rows are small and served
 // from cache; each wave loads its own two 16-row token tiles straight into MFMA
-// operand registers, NS-1 steps ahead as well.  Their 1x128 scales are stored
-// step-major in sorted-row order (by the dispatch for the hidden rows, by the
-// gate/up epilogue for h), so one step's scales of a tile are one contiguous
-// run that a single copy brings into the ring slot.  (A scalar loaded into a
-// rotating register stage would cost a register copy, and the wait before that
-// copy would drain the younger steps; one 16-byte load per row and step would
-// spend as many cache-line requests as the activation rows themselves.)
+// operand registers, NS-1 steps ahead as well.  Every scale a step needs rides
+// in the same slot: the tile's 1x128 row scales (stored step-major in
+// sorted-row order, by the dispatch for the hidden rows and by the gate/up
+// epilogue for h, so one step's scales of a tile are one contiguous run) and
+// the two 128x128 weight block scales of the step.
+//
+// The pipeline runs across task boundaries: while a task's last steps are
+// multiplied, the first NS-1 steps of the workgroup's next task are already in
+// flight, and the task's epilogue (SwiGLU, re-quantisation, stores) runs while
+// they land.  So nothing a task needs may be fetched with a wait of its own:
+// the next task's m-tile is read with scalar loads, and the source rows of its
+// gathered activations are copied into LDS one task ahead, behind the same
+// in-order wait counts as the weights.
+//
 // The steady loop is unrolled by NS so every register stage has a static
 // index, and is branch-free: steps past the end load at out-of-range offsets,
 // which the buffer unit returns as zeros (exact zero products), so one wait
-// count serves every step.
-//
-// The copy engine's LDS writes are invisible to the compiler, so the kernel
-// orders them itself: s_waitcnt vmcnt(N), N = the loads of the younger steps
-// still allowed in flight, then a barrier; the slot refilled after the barrier
-// is the one every wave finished reading one step earlier.
+// count serves every step.  The copy engine's LDS writes are invisible to the
+// compiler, so the kernel orders them itself: s_waitcnt vmcnt(N), N = the
+// loads of the younger steps still allowed in flight, then a barrier; the slot
+// refilled after the barrier is the one every wave finished reading one step
+// earlier.
 //
 // MFMA 16x16x128 e4m3 (one instruction spans a whole scale block): weight
 // fragment first, token fragment second, so lane l holds token l % 16 and
@@ -61,20 +67,64 @@ namespace {
 constexpr int kRingWaves = 8;
 constexpr int kRingPanels = 8;
 constexpr int kRingWeightBytes = kRingPanels * kStepPanelBytes;  // 32 KiB per step
-
-constexpr int kRingSlotBytes = kRingWeightBytes + 1024;  // + the tile's row scales of the step
-constexpr int kRingLdsBytes = AFD_RING_NS * kRingSlotBytes + 1024;  // + sink of idle scale copies
+// Each slot: the step's weights, then one 1 KiB scale copy per wave 0..2:
+// the tile's row scales (wave 0), weight block scales 0 and 1 (waves 1 and 2).
+constexpr int kRingScaleCopies = 3;
+constexpr int kRingSlotBytes = kRingWeightBytes + kRingScaleCopies * 1024;
 constexpr int kRingNS = AFD_RING_NS;
-constexpr int kRingMB = 4;  // m-tiles per rasterisation block
+constexpr int kRingSinkOff = kRingNS * kRingSlotBytes;      // the other waves' (empty) scale copies
+constexpr int kRingMetaOff = kRingSinkOff + 1024;           // per wave: source rows of two tasks ahead
+constexpr int kRingMetaBytes = 256;                         // 64 lanes x 4 bytes
+constexpr int kRingLdsBytes = kRingMetaOff + kRingWaves * 2 * kRingMetaBytes;
+constexpr int kRingMB = 4;         // m-tiles per rasterisation block
+constexpr int kRingMinRounds = 1;  // unrolled rounds per task
+static_assert(kRingLdsBytes <= 160 * 1024 - 4096, "ring exceeds LDS");
 
 __device__ inline int clamp31(int64_t v) { return v > 0x7fffffff ? 0x7fffffff : (int)v; }
 
+// Task t of a list of n m-tiles -> (m-tile, column group): blocks of kRingMB
+// m-tiles x all column groups, so consecutive tasks share their rows in L2.
+__device__ inline void ring_decode(int t, int n, int nq, int& mt, int& q) {
+  const int full = (n / kRingMB) * kRingMB * nq;
+  if (t < full) {
+    const int blk = t / (kRingMB * nq), w = t % (kRingMB * nq);
+    q = w / kRingMB;
+    mt = blk * kRingMB + w % kRingMB;
+  } else {
+    const int rem = n % kRingMB, u = t - full;
+    q = u / rem;
+    mt = (n / kRingMB) * kRingMB + u % rem;
+  }
+}
+
+// m-tile mt of a list.  The lists are not written by this kernel, so the
+// read goes through the constant address space and becomes a scalar load (a
+// vector load would need a wait of its own in the middle of the pipeline).
+__device__ inline int4 load_tile(const int4* tiles, int mt) {
+  typedef const __attribute__((address_space(4))) int* cptr;
+  const cptr c = (cptr)(const void*)tiles;
+  const int i = 4 * uniform(mt);
+  return make_int4(c[i], c[i + 1], c[i + 2], c[i + 3]);
+}
+
+// One task as a wave holds it while its steps are issued: the m-tile, the
+// column group and the per-lane offsets (buffer descriptors are rebuilt per
+// step from these, which is cheaper than holding two tasks' in registers).
+struct RingDesc {
+  int expert, row0, rows, q;
+  int ks;       // steps with data (0: an empty task, every copy out of range)
+  int svoff;    // per lane: scale copy offset (out of range where unused)
+  int aoff[2];  // per lane: activation offsets of the two token tiles
+};
+
 }  // namespace
 
-// One task: m-tile `tile` (at most BM rows) x column group q.  Every wave of
-// the workgroup calls it with the same arguments.
+// Every task rank + k * stride (k = 0, 1, ...) below n_tiles x n_groups of one
+// m-tile list, in one continuous pipeline.  Every wave of the workgroup calls
+// it with the same arguments.
 template <bool GATEUP, int BM>
-__device__ __forceinline__ void ring_task(const GemmParams& p, const int4 tile, const int q) {
+__device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles, const int n_tiles,
+                                          const int first, const int stride) {
   // declared here, not passed in: the copies need pointers known to be in LDS
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   __shared__ float red[kRingWaves * 32];  // gate/up: per-wave token amax
@@ -85,8 +135,12 @@ __device__ __forceinline__ void ring_task(const GemmParams& p, const int4 tile, 
   constexpr int PER_STAGE = B_DMA + 2 * RT + 1;           // + two 16-byte row loads per tile + scales
   constexpr int SLOT = kRingSlotBytes;
   constexpr int S_OFF = kRingWeightBytes;
-  constexpr int SINK = NS * SLOT;
   static_assert(WM * WN == kRingWaves && NPW % 2 == 0 && NPW <= 4 && BM <= 256, "wave grid");
+  static_assert(NS >= 2 && (NS - 2) * PER_STAGE < 64, "wait count");
+
+  const int nq = p.n_groups;
+  const int count = n_tiles * nq;
+  if (first >= count) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -94,133 +148,142 @@ __device__ __forceinline__ void ring_task(const GemmParams& p, const int4 tile, 
   const int kg = lane >> 4;  // which 32 bytes of the 128-deep block this lane carries
   const int tok = lane & 15;
   const int ks = p.k_steps;
-  const int nsr = (ks + NS - 1) / NS * NS;  // steps run: whole unrolled rounds
+  const int nsr = max((ks + NS - 1) / NS, kRingMinRounds) * NS;  // steps run: whole unrolled rounds
   const int oobA = clamp31(p.a_bytes), oobS = clamp31(p.a_scale_bytes);
   const int oobB = (int)p.b_expert_bytes;
   const int bpanel = (int)p.b_panel_bytes;
+  const int wsb = p.b_scale_rows * p.b_scale_cols;  // block scales per expert and matrix
   const auto ra = make_rsrc(p.a, p.a_bytes);
   const auto rsa = make_rsrc(p.a_scales, p.a_scale_bytes);
+  // this wave's scale copy: 0 = the tile's row scales, 1 / 2 = weight block
+  // scale 0 / 1 of the step, -1 = none (its empty copy goes to the sink)
+  const int scopy = wave < kRingScaleCopies ? wave : -1;
+  const auto rmeta = make_rsrc(p.sorted_assign, (int64_t)p.shared_row0 * 4);
+  // the source of this wave's scale copy, its bytes per step and an
+  // out-of-range offset (expert and block enter the per-lane offset)
+  const auto rs = scopy <= 0 ? rsa : make_rsrc((GATEUP && scopy == 2) ? p.b_scales1 : p.b_scales0, p.b_scale_bytes);
+  const int sstep = scopy <= 0 ? p.a_scale_ld * 4 : p.b_scale_cols * 4;
+  const int soob = scopy <= 0 ? oobS : clamp31(p.b_scale_bytes);
+  uint8_t* const meta = ring + kRingMetaOff + wave * 2 * kRingMetaBytes;  // two buffers
+  // down: the block scale of this wave's panels
+  const bool dn_second = ((kRingPanels / WN) * wn) / 4 != 0;
 
-  {
-    const int expert = uniform(tile.x), row0 = uniform(tile.y), rows = uniform(tile.z);
-    const auto rb = make_rsrc(p.b + (int64_t)expert * p.b_expert_bytes, p.b_expert_bytes);
-    const int pbase = uniform((int)((int64_t)q * kRingPanels * p.b_panel_bytes));
+  // gate/up: copy the sorted-row -> flat-slot entries of this wave's 32 rows of
+  // a tile (lanes 0..31) and of the tile's first row (lane 32) into meta
+  // buffer `buf`
+  auto meta_copy = [&](const int4 tile, const bool valid, const int buf) {
+    const int row0 = uniform(tile.y);
+    int v = 0x7fffffff;
+    if (valid && lane < 32) v = (row0 + wm * 32 + lane) * 4;
+    if (valid && lane == 32) v = row0 * 4;
+    dma4(rmeta, meta + buf * kRingMetaBytes, v, 0);
+  };
 
-    // this lane's token of each tile (rows past the count repeat the tile's
-    // first row: computed, never stored)
-    auto src_row = [&](int r) -> int {  // activation row of sorted row r
-      return !p.gather ? r : r >= p.shared_row0 ? r - p.shared_row0 : p.sorted_assign[r] / p.top_k;
-    };
-    int aoff[RT];
+  auto make_desc = [&](const int4 tile, const int q, const bool valid, const int buf) {
+    RingDesc d;
+    d.expert = uniform(tile.x);
+    d.row0 = uniform(tile.y);
+    d.rows = valid ? uniform(tile.z) : 0;
+    d.q = q;
+    d.ks = valid ? ks : 0;
+    const int* mi = reinterpret_cast<const int*>(meta + buf * kRingMetaBytes);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
+      // rows past the tile's count repeat its first row (computed, never stored)
       const int m = wm * 32 + rt * 16 + tok;
-      aoff[rt] = (int)((int64_t)src_row(row0 + (m < rows ? m : 0)) * p.a_row_bytes) + 32 * kg;
+      const int r = d.row0 + (m < d.rows ? m : 0);
+      int src = r;
+      if (GATEUP && r < p.shared_row0) src = (m < d.rows ? mi[rt * 16 + tok] : mi[32]) / p.top_k;
+      if (GATEUP && r >= p.shared_row0) src = r - p.shared_row0;
+      d.aoff[rt] = valid ? (int)((int64_t)src * p.a_row_bytes) + 32 * kg : 0;
     }
-    // scales: wave 0 copies the step's run of the tile's rows (lane i: rows
-    // 4i .. 4i+3); the others copy zeros into a sink so every wave counts the
-    // same loads per step
-    const int svoff = (wave == 0 && 4 * lane < BM) ? (row0 + 4 * lane) * 4 : oobS;
-    const int sstep = p.a_scale_ld * 4;
+    if (scopy == 0)  // lane i: rows 4i .. 4i+3 of the tile's run in a step
+      d.svoff = (valid && 4 * lane < BM) ? (d.row0 + 4 * lane) * 4 : soob;
+    else             // lane 0: one block scale of the step (row c of the expert's block grid)
+      d.svoff = (valid && scopy > 0 && lane == 0) ? (d.expert * wsb + (GATEUP ? q : 2 * q + (scopy - 1))) * 4 : soob;
+    return d;
+  };
 
-    // weight block scales, one per super-step: gate/up -> block q of gate (even
-    // panels) and up (odd panels); down -> the block of this wave's panels
-    BlockScales sbs;
-    {
-      const int64_t eoff = (int64_t)expert * p.b_scale_rows * p.b_scale_cols;
-      if (GATEUP)
-        sbs.load(p.b_scales0 + eoff + q, p.b_scales1 + eoff + q, p.b_scale_cols, ks, lane);
-      else
-        sbs.load(p.b_scales0 + eoff + (kRingPanels * q + NPW * wn) / 4,
-                 p.b_scales0 + eoff + (kRingPanels * q + NPW * wn) / 4, p.b_scale_cols, ks, lane);
+  i32x4 areg[NS][RT][2];
+  f32x4 acc[RT][2 * NPW];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int b = 0; b < 2 * NPW; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[rt][b][r] = 0.0f;
+
+  // step s of the current task into ring slot `slot` and register stage
+  // `slot`; s >= nsr: step s - nsr of the next task
+  auto issue = [&](const RingDesc& cur, const RingDesc& nxt, int s, int slot) {
+    const bool nx = s >= nsr;
+    const int c = nx ? s - nsr : s;
+    const bool in = c < (nx ? nxt.ks : cur.ks);
+    const int expert = nx ? nxt.expert : cur.expert;
+    const int q = nx ? nxt.q : cur.q;
+    uint8_t* st = ring + slot * SLOT;
+    const auto rb = make_rsrc(p.b + (int64_t)expert * p.b_expert_bytes, p.b_expert_bytes);
+    const int pbase = q * kRingPanels * bpanel;
+#pragma unroll
+    for (int k = 0; k < B_DMA; ++k) {
+      const int i = wave * B_DMA + k, panel = i / 4, j = i % 4;
+      dma16_aux<AFD_RING_B_AUX>(rb, st + panel * kStepPanelBytes + j * 1024, lane * 16,
+                                in ? pbase + panel * bpanel + c * kStepPanelBytes + j * 1024 : oobB);
     }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int aoff = nx ? nxt.aoff[rt] : cur.aoff[rt];
+      areg[slot][rt][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff, in ? c * kStepBytes : oobA, 0);
+      areg[slot][rt][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff, in ? c * kStepBytes + 16 : oobA, 0);
+    }
+    dma16(rs, scopy >= 0 ? st + S_OFF + scopy * 1024 : ring + kRingSinkOff, nx ? nxt.svoff : cur.svoff,
+          in ? c * sstep : soob);
+  };
 
-    f32x4 acc[RT][2 * NPW];
+  auto compute = [&](int slot) {
+    const uint8_t* Bs = ring + slot * SLOT;
+    const float* S = reinterpret_cast<const float*>(Bs + S_OFF);
+    float sa[RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) sa[rt] = S[wm * 32 + rt * 16 + tok];
+    const float sw0 = *reinterpret_cast<const float*>(Bs + S_OFF + 1024);
+    const float sw1 = *reinterpret_cast<const float*>(Bs + S_OFF + 2048);
+    i32x8 x[RT];
 #pragma unroll
-      for (int b = 0; b < 2 * NPW; ++b)
+    for (int rt = 0; rt < RT; ++rt) x[rt] = cat32v(areg[slot][rt][0], areg[slot][rt][1]);
+    // weight fragment of a 16-column half panel: K bytes 32 kg .. +32 are
+    // 1 KiB chunks 2(kg & 1), +1 of the panel's lane half kg >> 1
+    const int g = kg >> 1, j0 = (kg & 1) * 2;
+    i32x8 wf[NPW][2];  // every weight fragment of the step first, then the products
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[rt][b][r] = 0.0f;
-
-    i32x4 areg[NS][RT][2];
-
-    // step c into ring slot `slot` and register stage `slot`
-    auto issue = [&](int c, int slot) {
-      const bool in = c < ks;
-      uint8_t* st = ring + slot * SLOT;
+    for (int pp = 0; pp < NPW; ++pp)
 #pragma unroll
-      for (int k = 0; k < B_DMA; ++k) {
-        const int i = wave * B_DMA + k, panel = i / 4, j = i % 4;
-        dma16_aux<AFD_RING_B_AUX>(rb, st + panel * kStepPanelBytes + j * 1024, lane * 16,
-                                  in ? pbase + panel * bpanel + c * kStepPanelBytes + j * 1024 : oobB);
+      for (int sh = 0; sh < 2; ++sh) {
+        const uint8_t* lo = Bs + (wn * NPW + pp) * kStepPanelBytes + j0 * 1024 + (16 * sh + tok + 32 * g) * 16;
+        wf[pp][sh] = cat32v(*reinterpret_cast<const i32x4*>(lo), *reinterpret_cast<const i32x4*>(lo + 1024));
       }
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        areg[slot][rt][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[rt], in ? c * kStepBytes : oobA, 0);
-        areg[slot][rt][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[rt], in ? c * kStepBytes + 16 : oobA, 0);
-      }
-      dma16(rsa, wave == 0 ? st + S_OFF : ring + SINK, svoff, in ? c * sstep : oobS);
-    };
-
-    auto compute = [&](int slot, int c) {
-      const uint8_t* Bs = ring + slot * SLOT;
-      const float* S = reinterpret_cast<const float*>(Bs + S_OFF);
-      float sa[RT];
+    for (int pp = 0; pp < NPW; ++pp) {
+      const float sb = GATEUP ? ((pp & 1) ? sw1 : sw0) : (dn_second ? sw1 : sw0);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) sa[rt] = S[wm * 32 + rt * 16 + tok];
-      const int cs = c < ks ? c : ks - 1;
-      const float sb0 = sbs.get0(cs), sb1 = sbs.get1(cs);
-      i32x8 x[RT];
+      for (int sh = 0; sh < 2; ++sh) {
+        const i32x8 w = wf[pp][sh];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) x[rt] = cat32v(areg[slot][rt][0], areg[slot][rt][1]);
-      // weight fragment of a 16-column half panel: K bytes 32 kg .. +32 are
-      // 1 KiB chunks 2(kg & 1), +1 of the panel's lane half kg >> 1
-      const int g = kg >> 1, j0 = (kg & 1) * 2;
+        for (int rt = 0; rt < RT; ++rt) {
+          f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+          t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x[rt], t, 0, 0, 0, 0, 0, 0);
+          const float sc = sa[rt] * sb;
 #pragma unroll
-      for (int pp = 0; pp < NPW; ++pp) {
-        const float sb = (GATEUP && (pp & 1)) ? sb1 : sb0;
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          const uint8_t* lo = Bs + (wn * NPW + pp) * kStepPanelBytes + j0 * 1024 + (16 * sh + tok + 32 * g) * 16;
-          const i32x8 w = cat32v(*reinterpret_cast<const i32x4*>(lo), *reinterpret_cast<const i32x4*>(lo + 1024));
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
-            t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x[rt], t, 0, 0, 0, 0, 0, 0);
-            const float sc = sa[rt] * sb;
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) acc[rt][pp * 2 + sh][r4] += t[r4] * sc;
-          }
+          for (int r4 = 0; r4 < 4; ++r4) acc[rt][pp * 2 + sh][r4] += t[r4] * sc;
         }
       }
-    };
-
-    // The loads of one step stay together (scheduling fences): the wait
-    // counter retires loads in order, so a step's loads mixed into a younger
-    // step's would make the register waits drain that younger step.
-#pragma unroll
-    for (int i = 0; i + 1 < NS; ++i) {
-      issue(i, i);
-      __builtin_amdgcn_sched_barrier(0);
     }
-    for (int t0 = 0; t0 < nsr; t0 += NS) {
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        wait_vmcnt<(NS - 2) * PER_STAGE>();  // step t0 + i has landed (this wave's copies) ...
-        lds_reads_done();
-        raw_barrier();                       // ... and every wave's; slot of the previous step is free
-        issue(t0 + i + NS - 1, (i + NS - 1) % NS);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(i, t0 + i);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    wait_vmcnt<0>();  // the out-of-range steps issued past the end
-    lds_reads_done();
-    raw_barrier();    // every wave is done with the ring before the next task refills it
+  };
 
-    // ------------------------------------------------------------- epilogue
+  // The task's outputs.  Its barriers are the ring's kind (LDS only): the
+  // next task's copies stay in flight.
+  auto epilogue = [&](const RingDesc& d) {
+    const int row0 = d.row0, rows = d.rows, q = d.q;
     if constexpr (GATEUP) {
       // h of unit u = 4q + (wn NPW + pp) / 2 (pp even: gate, pp + 1: up), per
       // token amax over the task's 128 h columns: this wave's, then over WN
@@ -242,7 +305,8 @@ __device__ __forceinline__ void ring_task(const GemmParams& p, const int4 tile, 
         a = fmaxf(a, __shfl_xor(a, 32, 64));
         if (kg == 0) red[(wm * WN + wn) * 32 + rt * 16 + tok] = a;
       }
-      __syncthreads();
+      lds_reads_done();
+      raw_barrier();
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int mi = rt * 16 + tok;
@@ -268,7 +332,8 @@ __device__ __forceinline__ void ring_task(const GemmParams& p, const int4 tile, 
           if (wn == 0 && kg == 0) p.c_scales[(int64_t)q * p.c_scale_ld + row0 + m] = scale;
         }
       }
-      __syncthreads();  // red[] is rewritten by the next task
+      lds_reads_done();
+      raw_barrier();  // red[] is rewritten by the next task
     } else {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -279,57 +344,121 @@ __device__ __forceinline__ void ring_task(const GemmParams& p, const int4 tile, 
         for (int pp = 0; pp < NPW; ++pp) {
           const int P = q * kRingPanels + wn * NPW + pp;
           if (P >= p.n_panels) continue;
-#pragma unroll
-          for (int sh = 0; sh < 2; ++sh) {
-            const int col = 32 * P + 16 * sh + 4 * kg;
-            uint2 o;
-            o.x = pack_bf16x2(acc[rt][pp * 2 + sh][0], acc[rt][pp * 2 + sh][1]);
-            o.y = pack_bf16x2(acc[rt][pp * 2 + sh][2], acc[rt][pp * 2 + sh][3]);
-            *reinterpret_cast<uint2*>(orow + (int64_t)col * 2) = o;
-          }
+          // lane pairs (kg, kg ^ 1) of a token swap one half panel each, so
+          // every lane stores 8 consecutive columns (16 bytes) and one store
+          // covers the panel's 64 bytes of 16 rows
+          uint2 o0, o1;
+          o0.x = pack_bf16x2(acc[rt][pp * 2][0], acc[rt][pp * 2][1]);
+          o0.y = pack_bf16x2(acc[rt][pp * 2][2], acc[rt][pp * 2][3]);
+          o1.x = pack_bf16x2(acc[rt][pp * 2 + 1][0], acc[rt][pp * 2 + 1][1]);
+          o1.y = pack_bf16x2(acc[rt][pp * 2 + 1][2], acc[rt][pp * 2 + 1][3]);
+          const bool odd = (kg & 1) != 0;
+          const uint2 snd = odd ? o0 : o1;
+          uint2 rcv;
+          rcv.x = __shfl_xor(snd.x, 16, 64);
+          rcv.y = __shfl_xor(snd.y, 16, 64);
+          const uint4 v = odd ? make_uint4(rcv.x, rcv.y, o1.x, o1.y) : make_uint4(o0.x, o0.y, rcv.x, rcv.y);
+          const int col = odd ? 32 * P + 16 + 4 * (kg - 1) : 32 * P + 4 * kg;
+          *reinterpret_cast<uint4*>(orow + (int64_t)col * 2) = v;
         }
       }
     }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int b = 0; b < 2 * NPW; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[rt][b][r] = 0.0f;
+  };
+
+  // The row sources of a task are copied two tasks ahead into alternating
+  // buffers, so the descriptor of the next task can be built when the current
+  // one starts, from data that landed behind the previous task's waits.  The
+  // two tasks ahead of the loop may be waited for: nothing is in flight yet.
+  int t = first, mt = 0, q = 0;
+  ring_decode(t, n_tiles, nq, mt, q);
+  const int4 tile = load_tile(tiles, mt);
+  int t1 = t + stride, mt1 = mt, q1 = q;
+  if (t1 < count) ring_decode(t1, n_tiles, nq, mt1, q1);
+  int4 tile1 = load_tile(tiles, mt1);
+  if (GATEUP) {
+    meta_copy(tile, true, 0);
+    meta_copy(tile1, t1 < count, 1);
+    wait_vmcnt<0>();
   }
+  RingDesc cur = make_desc(tile, q, true, 0);
+  // The loads of one step stay together (scheduling fences): the wait
+  // counter retires loads in order, so a step's loads mixed into a younger
+  // step's would make the register waits drain that younger step.
+  lds_reads_done();
+#pragma unroll
+  for (int i = 0; i + 1 < NS; ++i) {
+    issue(cur, cur, i, i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int buf = 0;  // meta buffer of the current task
+  while (true) {
+    const bool has_next = t1 < count;
+    // the next task, from the row sources copied one task ago
+    const RingDesc nxt = make_desc(tile1, q1, has_next, buf ^ 1);
+    // the task after it: its tile, and its row sources into the buffer the
+    // current task's came from (read when it started, so free)
+    const int t2 = t1 + stride;
+    int mt2 = mt1, q2 = q1;
+    if (t2 < count) ring_decode(t2, n_tiles, nq, mt2, q2);
+    const int4 tile2 = load_tile(tiles, mt2);
+    lds_reads_done();
+    // This copy goes out behind the current task's first steps; it only ever
+    // makes the wait counts below stricter (as do the previous task's
+    // stores), never looser.
+    if (GATEUP) meta_copy(tile2, t2 < count, buf);
+    __builtin_amdgcn_sched_barrier(0);
+    int t0 = 0;
+    do {  // the last round issues the next task's first NS - 1 steps
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        wait_vmcnt<(NS - 2) * PER_STAGE>();  // step t0 + i has landed (this wave's copies) ...
+        lds_reads_done();
+        raw_barrier();                       // ... and every wave's; slot of the previous step is free
+        issue(cur, nxt, t0 + i + NS - 1, (i + NS - 1) % NS);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      t0 += NS;
+    } while (t0 < nsr);
+    epilogue(cur);
+    if (!has_next) break;
+    cur = nxt;
+    t1 = t2;
+    tile1 = tile2;
+    q1 = q2;
+    mt1 = mt2;
+    buf ^= 1;
+  }
+  wait_vmcnt<0>();  // the empty steps issued past the last task
+  lds_reads_done();
+  raw_barrier();    // every wave is done with the ring before another list refills it
 }
 
 // Both tile lists in one persistent launch: the heavy list's tasks (m-tiles
 // of up to 128 rows), then the light list's (up to 64 rows), so a GEMM stage
-// has one tail instead of two.  Tasks run in blocks of kRingMB m-tiles x all
-// column groups; workgroup ranks are renumbered so that each XCD owns a
+// has one tail instead of two.  A workgroup runs tasks rank, rank + G, ... of
+// the two lists in a row; ranks are renumbered so that each XCD owns a
 // contiguous run of tasks (shared rows stay in its L2).
 template <bool GATEUP>
 __global__ __launch_bounds__(kRingWaves * 64, 1) void gemm_ring_kernel(GemmParams p) {
   const int nq = p.n_groups;
   const int nh = uniform(p.num_mtiles2 ? p.num_mtiles2[0] : 0);
   const int nl = uniform(p.num_mtiles[0]);
-  const int th = nh * nq, tl = nl * nq;
+  const int th = nh * nq;
   const int G = gridDim.x;
   const int rank = (AFD_RING_XCD_REMAP && G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds
                                                           : blockIdx.x;
-  // task t of a list of n m-tiles -> (m-tile, column group)
-  auto decode = [&](int t, int n, int& mt, int& q) {
-    const int full = (n / kRingMB) * kRingMB * nq;
-    if (t < full) {
-      const int blk = t / (kRingMB * nq), w = t % (kRingMB * nq);
-      q = w / kRingMB;
-      mt = blk * kRingMB + w % kRingMB;
-    } else {
-      const int rem = n % kRingMB, u = t - full;
-      q = u / rem;
-      mt = (n / kRingMB) * kRingMB + u % rem;
-    }
-  };
-  for (int task = rank; task < th + tl; task += G) {
-    int mt, q;
-    if (task < th) {
-      decode(task, nh, mt, q);
-      ring_task<GATEUP, 128>(p, p.mtiles2[mt], q);
-    } else {
-      decode(task - th, nl, mt, q);
-      ring_task<GATEUP, 64>(p, p.mtiles[mt], q);
-    }
-  }
+  if (nh > 0) ring_list<GATEUP, 128>(p, p.mtiles2, nh, rank, G);
+  // this workgroup's first task past the heavy list, as an index into the light list
+  const int first_l = rank >= th ? rank - th : rank + (th - rank + G - 1) / G * G - th;
+  ring_list<GATEUP, 64>(p, p.mtiles, nl, first_l, G);
 }
 
 template <bool GATEUP>

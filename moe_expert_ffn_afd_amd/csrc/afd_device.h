@@ -43,6 +43,19 @@ __device__ inline uint32_t pack_fp8x4(float a, float b, float c, float d) {
   return (uint32_t)v;
 }
 
+// 32x32 MFMA output rows: lane l holds 4 columns of a row for each of two
+// r4 values (columns 8 r4 + 4 (l >> 5) + 0..3, lo = the even r4, hi_v = the
+// odd one).  Lanes l and l ^ 32 swap halves so each stores 8 consecutive
+// columns (16 bytes) at dst: the lower lane columns 16 r2 + 0..7, the upper
+// lane 16 r2 + 8..15.  Both lanes of a pair must be active.
+__device__ inline void store_pair16(uint8_t* dst, uint2 lo, uint2 hi_v, bool upper) {
+  const uint2 snd = upper ? lo : hi_v;
+  uint2 rcv;
+  rcv.x = __shfl_xor(snd.x, 32, 64);
+  rcv.y = __shfl_xor(snd.y, 32, 64);
+  *reinterpret_cast<uint4*>(dst) = upper ? make_uint4(rcv.x, rcv.y, hi_v.x, hi_v.y) : make_uint4(lo.x, lo.y, rcv.x, rcv.y);
+}
+
 // Raw buffer resource: stride 0, byte-addressed; reads at offsets >= the
 // record count return zero without touching memory.
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {

@@ -190,16 +190,21 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
         const int m = mr * 32 + col;
         if (m >= rows) continue;
         uint8_t* out = p.c + (int64_t)(row0 + m) * p.c_row_bytes + (int64_t)(32 * unit) * 2;
+        // lane l holds columns 8 r4 + 4 g + 0..3; lanes l and l ^ 32 swap one
+        // of each pair of r4 so every lane stores 8 consecutive columns
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int n = 8 * r4 + 4 * g;
-          float h[4];
+        for (int r2 = 0; r2 < 2; ++r2) {
+          uint2 o[2];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = silu_mul(acc[mr][0][4 * r4 + e], acc[mr][1][4 * r4 + e]);
-          uint2 v;
-          v.x = pack_bf16x2(h[0], h[1]);
-          v.y = pack_bf16x2(h[2], h[3]);
-          *reinterpret_cast<uint2*>(out + n * 2) = v;
+          for (int k = 0; k < 2; ++k) {
+            const int r4 = 2 * r2 + k;
+            float h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = silu_mul(acc[mr][0][4 * r4 + e], acc[mr][1][4 * r4 + e]);
+            o[k].x = pack_bf16x2(h[0], h[1]);
+            o[k].y = pack_bf16x2(h[2], h[3]);
+          }
+          store_pair16(out + (16 * r2 + 8 * g) * 2, o[0], o[1], g != 0);
         }
       }
     } else {
@@ -212,12 +217,15 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
           if (NPW * unit + pp >= p.n_panels) continue;
           uint8_t* out = p.c + (int64_t)(row0 + m) * p.c_row_bytes + (int64_t)(32 * (NPW * unit + pp)) * 2;
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int n = 8 * r4 + 4 * g;
-            uint2 v;
-            v.x = pack_bf16x2(acc[mr][pp][4 * r4 + 0], acc[mr][pp][4 * r4 + 1]);
-            v.y = pack_bf16x2(acc[mr][pp][4 * r4 + 2], acc[mr][pp][4 * r4 + 3]);
-            *reinterpret_cast<uint2*>(out + n * 2) = v;
+          for (int r2 = 0; r2 < 2; ++r2) {
+            uint2 o[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+              const int r4 = 2 * r2 + k;
+              o[k].x = pack_bf16x2(acc[mr][pp][4 * r4 + 0], acc[mr][pp][4 * r4 + 1]);
+              o[k].y = pack_bf16x2(acc[mr][pp][4 * r4 + 2], acc[mr][pp][4 * r4 + 3]);
+            }
+            store_pair16(out + (16 * r2 + 8 * g) * 2, o[0], o[1], g != 0);
           }
         }
       }

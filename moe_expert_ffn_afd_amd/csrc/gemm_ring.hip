@@ -321,13 +321,19 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
 #pragma unroll
           for (int u = 0; u < NPW / 2; ++u) {
             const int unit = 4 * q + (wn * NPW) / 2 + u;
+            uint32_t o[2];
 #pragma unroll
             for (int sh = 0; sh < 2; ++sh) {
               float v[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) v[e] = fminf(fmaxf(h[rt][u][sh][e] * inv, -448.0f), 448.0f);
-              *reinterpret_cast<uint32_t*>(orow + 32 * unit + 16 * sh + 4 * kg) = pack_fp8x4(v[0], v[1], v[2], v[3]);
+              o[sh] = pack_fp8x4(v[0], v[1], v[2], v[3]);
             }
+            // lanes kg and kg ^ 1 swap one half each: 8 consecutive codes per lane
+            const bool odd = (kg & 1) != 0;
+            const uint32_t rcv = __shfl_xor(odd ? o[0] : o[1], 16, 64);
+            const uint2 w = odd ? make_uint2(rcv, o[1]) : make_uint2(o[0], rcv);
+            *reinterpret_cast<uint2*>(orow + 32 * unit + (odd ? 16 + 4 * (kg - 1) : 4 * kg)) = w;
           }
           if (wn == 0 && kg == 0) p.c_scales[(int64_t)q * p.c_scale_ld + row0 + m] = scale;
         }

@@ -251,17 +251,22 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_tiled_kernel(GemmParams p) {
         const int P = q * kBNP + wn * NPW + pp;  // packed panel index (gate/up: 2 per unit)
         if (P >= (GATEUP ? 2 * p.n_panels : p.n_panels)) continue;
         const int col0 = GATEUP ? 32 * (P / 2) : 32 * P;
+        // lanes l and l ^ 32 swap halves: 16-byte stores of 8 columns
+        const bool hi = lane >= 32;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int n = 8 * r4 + 4 * (lane >> 5);
-          float v[4];
+        for (int r2 = 0; r2 < 2; ++r2) {
+          uint2 o[2];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[e] = GATEUP ? silu_mul(acc[mr][pp][4 * r4 + e], acc[mr][pp + 1][4 * r4 + e]) : acc[mr][pp][4 * r4 + e];
-          uint2 o;
-          o.x = pack_bf16x2(v[0], v[1]);
-          o.y = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<uint2*>(orow + (int64_t)(col0 + n) * 2) = o;
+          for (int k = 0; k < 2; ++k) {
+            const int r4 = 2 * r2 + k;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              v[e] = GATEUP ? silu_mul(acc[mr][pp][4 * r4 + e], acc[mr][pp + 1][4 * r4 + e]) : acc[mr][pp][4 * r4 + e];
+            o[k].x = pack_bf16x2(v[0], v[1]);
+            o[k].y = pack_bf16x2(v[2], v[3]);
+          }
+          store_pair16(orow + (int64_t)(col0 + 16 * r2 + (hi ? 8 : 0)) * 2, o[0], o[1], hi);
         }
       }
     }

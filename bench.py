@@ -40,6 +40,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def gate_up_kernels(cfg: dict, t_mb: int) -> str:
+    """Which launches make up the timed gate/up + SwiGLU stage (the library's tile policy)."""
+    if cfg["dtype"] == "fp8":
+        return "gate/up + SwiGLU stage: gemm_ring_kernel<true> (heavy and light tiles in one launch)"
+    if cfg["dtype"] == "f32":
+        return "gate/up + SwiGLU stage: gemm_f32_kernel<true> (one launch)"
+    if not cfg.get("shared_inter") and t_mb * cfg["K"] <= 16 * cfg["E"]:
+        return "gate/up + SwiGLU stage: gemm_grouped_kernel<true, 1> (every expert in 32-row tiles, one launch)"
+    return ("gate/up + SwiGLU stage: gemm_tiled_kernel<true> (experts above one light tile) "
+            "then gemm_grouped_kernel<true, MR> (light experts), same stream")
+
+
 def algorithmic_units(cfg: dict, ids) -> dict:
     """Bytes and flops each kernel must move / do at minimum for this routing."""
     import numpy as np
@@ -202,8 +214,7 @@ def main():
         ach = gu_flops / gu_launch_s / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_TFLOPS[dt], 4)}
-    roof["kernel"] = ("gate/up + SwiGLU stage: gemm_tiled_kernel (experts above one light tile) "
-                      "then gemm_grouped_kernel (light experts), same stream")
+    roof["kernel"] = gate_up_kernels(cfg, T // mbs)
     roof["launch_ms"] = round(per_launch[2], 4)
     traffic = None
     try:

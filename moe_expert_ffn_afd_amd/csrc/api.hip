@@ -406,7 +406,11 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   const int bm = 32 * mr;
   const bool fp8 = dt == kFP8;
   const int bm_heavy = dt == kF32 ? bm : fp8 ? ring_rows(true) : tiled_rows(dt);
-  const int heavy_min = dt == kF32 ? 0x7fffffff : bm + 1;
+  // bf16 batches of at most 16 rows per expert on average (decode) run the
+  // light list only: an expert that still gets more than bm rows takes several
+  // light tiles, which saves the two (nearly always empty) heavy launches
+  const bool light_only = dt == kF32 || (dt == kBF16 && !a->S && n_flat <= 16ll * E);
+  const int heavy_min = light_only ? 0x7fffffff : bm + 1;
   std::vector<hipEvent_t> ev;
   auto mark = [&]() -> afd_status {
     if (!a->timing) return AFD_OK;
@@ -470,7 +474,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
 
   // upper bounds of the routed + shared m-tiles of this call, per list
   const int64_t mt_bound = n_flat / bm + std::min<int64_t>(E, n_flat) + (a->S ? (T + bm - 1) / bm : 0) + 1;
-  const int64_t mth_bound = dt == kF32 ? 0 : n_flat / heavy_min + (a->S ? (T + bm_heavy - 1) / bm_heavy : 0) + 1;
+  const int64_t mth_bound = light_only ? 0 : n_flat / heavy_min + (a->S ? (T + bm_heavy - 1) / bm_heavy : 0) + 1;
   const int64_t rows_ld_h = (int64_t)I * esize_of(dt);
   const int64_t h_rows = nmax + (a->S ? a->Tmax : 0);
   const int occupancy_wgs = 4;  // resident workgroups per CU the persistent grids aim for

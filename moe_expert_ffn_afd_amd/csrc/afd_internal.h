@@ -60,6 +60,7 @@ constexpr int kXcds = 8;               // accelerator complex dies of an MI355X 
 constexpr int kDispatchThreads = 1024;
 constexpr int kDispatchLdsInts = 12288;  // chunk x expert counters held in LDS (48 KiB)
 constexpr int kMaxExperts = 512;
+constexpr int kDispatchFuseSlots = 4096;  // up to this many flat slots: one dispatch launch
 constexpr int kMaxTopK = 32;
 
 struct DispatchParams {
@@ -82,6 +83,7 @@ struct DispatchParams {
   int4* mtiles;            // light tile list
   int4* mtiles_heavy;      // heavy tile list
   int32_t* num_mtiles;     // [2]: light, heavy
+  int32_t fused;           // 1: count_scan also places the slots (n_flat <= kDispatchFuseSlots)
 };
 
 struct GemmParams {

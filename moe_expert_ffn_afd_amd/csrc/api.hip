@@ -428,6 +428,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   d.num_experts = E;
   d.chunk_shift = chunk_shift_for(n_flat, E);
   d.n_chunks = (int32_t)((n_flat + (1ll << d.chunk_shift) - 1) >> d.chunk_shift);
+  d.fused = n_flat <= kDispatchFuseSlots ? 1 : 0;
   d.counts = a->counts;
   d.offsets = a->offsets;
   d.chunk_base = a->chunk_base;

@@ -12,7 +12,8 @@
 //   row_of[f]            = r with sorted_assign[r] == f, or -1
 // Being a pure function of the ids, it is reproduced bit for bit.
 //
-// Two kernels.  count_scan (one workgroup): per-(chunk, expert) counts with
+// Two kernels (one for batches of at most kDispatchFuseSlots slots, where
+// count_scan also does the placement).  count_scan (one workgroup): per-(chunk, expert) counts with
 // LDS atomics (counts do not depend on order), per-expert prefix over chunks,
 // exclusive scan over experts, first sorted row of every (chunk, expert), and
 // the GEMM m-tile list.  scatter (one workgroup per chunk): each wave ranks its
@@ -57,6 +58,51 @@ __device__ inline int block_exclusive_scan_1024(int v, int* lds_waves, int* tota
 }
 
 }  // namespace
+
+// Stable placement of the flat slots [f0, f_end) in rounds of 1024: cursor[e]
+// holds the next sorted row of expert e and advances round by round; wcnt is
+// [16][E] LDS, zero on entry and on return.  Every thread of the 1024-thread
+// workgroup calls it.
+__device__ void scatter_rounds(const DispatchParams& p, int f0, int f_end, int* cursor, int* wcnt) {
+  const int E = p.num_experts;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = f0; base < f_end; base += kDispatchThreads) {
+    const int f = base + tid;
+    const int e = f < f_end ? p.ids[f] : -1;
+    const bool valid = e >= 0 && e < E;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      match &= bit ? m : ~m;
+    }
+    const int rank = __popcll(match & lt_mask);
+    if (valid && rank == 0) wcnt[wave * E + e] = __popcll(match);
+    __syncthreads();
+    if (valid) {
+      int prefix = 0;
+      for (int w = 0; w < wave; ++w) prefix += wcnt[w * E + e];
+      const int pos = cursor[e] + prefix + rank;
+      p.sorted_assign[pos] = f;
+      p.row_of[f] = pos;
+    } else if (f < f_end) {
+      p.row_of[f] = -1;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += kDispatchThreads) {
+      int s = 0;
+      for (int w = 0; w < 16; ++w) s += wcnt[w * E + x];
+      cursor[x] += s;
+    }
+    __syncthreads();
+    if (valid && rank == 0) wcnt[wave * E + e] = 0;
+    __syncthreads();
+  }
+}
 
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(DispatchParams p) {
   extern __shared__ int cc[];  // [n_chunks][E] counts, then chunk-local prefixes
@@ -122,7 +168,8 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
   }
   __syncthreads();
 
-  for (int i = tid; i < ncc; i += kDispatchThreads) p.chunk_base[i] = excl[i % E] + cc[i];
+  if (!p.fused)
+    for (int i = tid; i < ncc; i += kDispatchThreads) p.chunk_base[i] = excl[i % E] + cc[i];
 
   // m-tile lists: experts with at least heavy_min_rows rows go to the heavy
   // list (tiles of bm_heavy rows), the others to the light list (bm_light);
@@ -159,6 +206,17 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
       p.num_mtiles[1] = n_heavy + (sh_heavy ? n_shared : 0);
     }
   }
+
+  // small batches: the placement too, all slots in order in this workgroup
+  // (cursors start at the experts' first rows), instead of a second launch
+  if (p.fused) {
+    int* wcnt = cc + ncc;  // [16][E]
+    for (int i = tid; i < 16 * E; i += kDispatchThreads) wcnt[i] = 0;
+    __syncthreads();  // every read of total[] above is done: it becomes the cursors
+    for (int e = tid; e < E; e += kDispatchThreads) total[e] = excl[e];
+    __syncthreads();
+    scatter_rounds(p, 0, p.n_flat, total, wcnt);
+  }
 }
 
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_scatter_kernel(DispatchParams p) {
@@ -167,52 +225,14 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_scatter_kernel(Disp
   int* cursor = lds;          // [E]
   int* wcnt = lds + E;        // [16][E] per-wave counts of the current round
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
   const int chunk = blockIdx.x;
   const int chunk_len = 1 << p.chunk_shift;
   const int f0 = chunk * chunk_len;
   const int f_end = min(f0 + chunk_len, p.n_flat);
-
-  int nbits = 1;
-  while ((1 << nbits) < E) ++nbits;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
   for (int e = tid; e < E; e += kDispatchThreads) cursor[e] = p.chunk_base[chunk * E + e];
   for (int i = tid; i < 16 * E; i += kDispatchThreads) wcnt[i] = 0;
   __syncthreads();
-
-  for (int base = f0; base < f_end; base += kDispatchThreads) {
-    const int f = base + tid;
-    const int e = f < f_end ? p.ids[f] : -1;
-    const bool valid = e >= 0 && e < E;
-    uint64_t match = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t m = __ballot(bit);
-      match &= bit ? m : ~m;
-    }
-    const int rank = __popcll(match & lt_mask);
-    if (valid && rank == 0) wcnt[wave * E + e] = __popcll(match);
-    __syncthreads();
-    if (valid) {
-      int prefix = 0;
-      for (int w = 0; w < wave; ++w) prefix += wcnt[w * E + e];
-      const int pos = cursor[e] + prefix + rank;
-      p.sorted_assign[pos] = f;
-      p.row_of[f] = pos;
-    } else if (f < f_end) {
-      p.row_of[f] = -1;
-    }
-    __syncthreads();
-    for (int x = tid; x < E; x += kDispatchThreads) {
-      int s = 0;
-      for (int w = 0; w < 16; ++w) s += wcnt[w * E + x];
-      cursor[x] += s;
-    }
-    __syncthreads();
-    if (valid && rank == 0) wcnt[wave * E + e] = 0;
-    __syncthreads();
-  }
+  scatter_rounds(p, f0, f_end, cursor, wcnt);
 }
 
 // Block-FP8 only: the caller's 1x128 activation scales [T][H/128], gathered
@@ -246,13 +266,13 @@ hipError_t launch_gather_scales(const ScaleGatherParams& p, hipStream_t s) {
 }
 
 hipError_t launch_dispatch_count_scan(const DispatchParams& p, hipStream_t s) {
-  size_t lds = sizeof(int) * (size_t)p.n_chunks * p.num_experts;
+  size_t lds = sizeof(int) * ((size_t)p.n_chunks + (p.fused ? 16 : 0)) * p.num_experts;
   hipLaunchKernelGGL(dispatch_count_scan_kernel, dim3(1), dim3(kDispatchThreads), lds, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_dispatch_scatter(const DispatchParams& p, hipStream_t s) {
-  if (p.n_chunks == 0) return hipSuccess;
+  if (p.n_chunks == 0 || p.fused) return hipSuccess;
   size_t lds = sizeof(int) * (size_t)17 * p.num_experts;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(p.n_chunks), dim3(kDispatchThreads), lds, s, p);
   return hipGetLastError();

@@ -57,6 +57,26 @@ def test_empty_and_tiny_batches(dtype):
     layer.close()
 
 
+def test_dispatch_either_side_of_the_single_launch_limit():
+    """Up to 4096 flat slots one dispatch launch also places the slots; above it a
+    second launch does.  Both must give the oracle's bit-exact dispatch."""
+    c = dict(dtype="bf16", T=513, H=128, I=128, E=200, K=8, routing="zipf", zipf_s=1.2, shared_inter=0)
+    p = problem(c, seed=11)
+    layer = afd.Layer(p, max_tokens=513)
+    for T in (511, 512, 513):
+        say("case T =", T, "slots =", T * 8)
+        q = {k: v for k, v in p.items()}
+        for k in ("hidden", "hidden_scales", "ids", "weights"):
+            if q[k] is not None:
+                q[k] = p[k][:T].contiguous()
+        q["T"] = T
+        out = layer.forward(q["hidden"], q["hidden_scales"], q["ids"], q["weights"])
+        torch.cuda.synchronize()
+        check_dispatch(layer, q)
+        compare(out, oracle_out(to_host_problem(q)), "bf16", what="T=%d" % T)
+    layer.close()
+
+
 def test_unused_experts_poisoned_with_nan():
     T, E, K = 50, 8, 2
     rng = np.random.default_rng(4)

@@ -14,8 +14,10 @@
 // buffer unit copies each 128-deep super-step of the 8 panels (32 KiB) straight
 // into a ring of NS slots, so NS-1 super-steps (96 KiB at NS = 4) are in flight
 // per CU without holding a register.  The activation rows are small and served
-// from cache; each wave loads its own two 16-row token tiles straight into MFMA
-// operand registers, NS-1 steps ahead as well.  Every scale a step needs rides
+// from cache; each wave loads its own 16-row token tile straight into MFMA
+// operand registers, NS-1 steps ahead as well (one tile per wave rather than
+// two halves the row loads, which share the CU's cache-line request budget
+// with the weight copies; the extra LDS reads of the weights cost less).  Every scale a step needs rides
 // in the same slot: the tile's 1x128 row scales (stored step-major in
 // sorted-row order, by the dispatch for the hidden rows and by the gate/up
 // epilogue for h, so one step's scales of a tile are one contiguous run) and
@@ -42,8 +44,8 @@
 // fragment first, token fragment second, so lane l holds token l % 16 and
 // output columns 4(l / 16) + r of a 16-column half panel; the product is added
 // into the accumulator times (token scale x block scale).  Eight waves, two per
-// SIMD, as WM x WN = (BM / 32) x (8 / (BM / 32)): each wave owns 32 rows and
-// 8 / WN panels.
+// SIMD, as WM x WN = (BM / 16) x (8 / (BM / 16)): each wave owns 16 rows and
+// 8 / WN panels (8 x 1 for 128-row tiles, 4 x 2 for 64-row tiles).
 #include <algorithm>
 
 #include "afd_device.h"
@@ -59,6 +61,12 @@ namespace {
 #endif
 #ifndef AFD_RING_B_AUX
 #define AFD_RING_B_AUX 0  // cache policy of the weight copies
+#endif
+#ifndef AFD_RING_RT_HEAVY
+#define AFD_RING_RT_HEAVY 1  // 16-row token tiles per wave, 128-row m-tiles
+#endif
+#ifndef AFD_RING_RT_LIGHT
+#define AFD_RING_RT_LIGHT 1  // same, 64-row m-tiles
 #endif
 #ifndef AFD_RING_XCD_REMAP
 #define AFD_RING_XCD_REMAP 1
@@ -129,13 +137,15 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   __shared__ float red[kRingWaves * 32];  // gate/up: per-wave token amax
   constexpr int NS = kRingNS;
-  constexpr int WM = BM / 32, WN = kRingWaves / WM, NPW = kRingPanels / WN;
-  constexpr int RT = 2;                                   // 16-row token tiles per wave
+  constexpr int WM = BM / (16 * (BM > 64 ? AFD_RING_RT_HEAVY : AFD_RING_RT_LIGHT)), WN = kRingWaves / WM,
+                NPW = kRingPanels / WN;
+  constexpr int RT = BM > 64 ? AFD_RING_RT_HEAVY : AFD_RING_RT_LIGHT;  // 16-row token tiles per wave
+  constexpr int WR = 16 * RT;                             // rows per wave
   constexpr int B_DMA = kRingPanels * 4 / kRingWaves;     // 1 KiB weight copies per wave and step
   constexpr int PER_STAGE = B_DMA + 2 * RT + 1;           // + two 16-byte row loads per tile + scales
   constexpr int SLOT = kRingSlotBytes;
   constexpr int S_OFF = kRingWeightBytes;
-  static_assert(WM * WN == kRingWaves && NPW % 2 == 0 && NPW <= 4 && BM <= 256, "wave grid");
+  static_assert(WM * WN == kRingWaves && NPW % 2 == 0 && NPW <= 8 && RT <= 2 && BM <= 256, "wave grid");
   static_assert(NS >= 2 && (NS - 2) * PER_STAGE < 64, "wait count");
 
   const int nq = p.n_groups;
@@ -166,7 +176,6 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
   const int soob = scopy <= 0 ? oobS : clamp31(p.b_scale_bytes);
   uint8_t* const meta = ring + kRingMetaOff + wave * 2 * kRingMetaBytes;  // two buffers
   // down: the block scale of this wave's panels
-  const bool dn_second = ((kRingPanels / WN) * wn) / 4 != 0;
 
   // gate/up: copy the sorted-row -> flat-slot entries of this wave's 32 rows of
   // a tile (lanes 0..31) and of the tile's first row (lane 32) into meta
@@ -174,7 +183,7 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
   auto meta_copy = [&](const int4 tile, const bool valid, const int buf) {
     const int row0 = uniform(tile.y);
     int v = 0x7fffffff;
-    if (valid && lane < 32) v = (row0 + wm * 32 + lane) * 4;
+    if (valid && lane < WR) v = (row0 + wm * WR + lane) * 4;
     if (valid && lane == 32) v = row0 * 4;
     dma4(rmeta, meta + buf * kRingMetaBytes, v, 0);
   };
@@ -190,7 +199,7 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       // rows past the tile's count repeat its first row (computed, never stored)
-      const int m = wm * 32 + rt * 16 + tok;
+      const int m = wm * WR + rt * 16 + tok;
       const int r = d.row0 + (m < d.rows ? m : 0);
       int src = r;
       if (GATEUP && r < p.shared_row0) src = (m < d.rows ? mi[rt * 16 + tok] : mi[32]) / p.top_k;
@@ -245,7 +254,7 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
     const float* S = reinterpret_cast<const float*>(Bs + S_OFF);
     float sa[RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) sa[rt] = S[wm * 32 + rt * 16 + tok];
+    for (int rt = 0; rt < RT; ++rt) sa[rt] = S[wm * WR + rt * 16 + tok];
     const float sw0 = *reinterpret_cast<const float*>(Bs + S_OFF + 1024);
     const float sw1 = *reinterpret_cast<const float*>(Bs + S_OFF + 2048);
     i32x8 x[RT];
@@ -254,27 +263,34 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
     // weight fragment of a 16-column half panel: K bytes 32 kg .. +32 are
     // 1 KiB chunks 2(kg & 1), +1 of the panel's lane half kg >> 1
     const int g = kg >> 1, j0 = (kg & 1) * 2;
-    i32x8 wf[NPW][2];  // every weight fragment of the step first, then the products
+    // the weight fragments of PG panels first, then their products (PG = all
+    // of a wave's panels up to 4)
+    constexpr int PG = NPW < 4 ? NPW : 4;
 #pragma unroll
-    for (int pp = 0; pp < NPW; ++pp)
+    for (int p0 = 0; p0 < NPW; p0 += PG) {
+      i32x8 wf[PG][2];
 #pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        const uint8_t* lo = Bs + (wn * NPW + pp) * kStepPanelBytes + j0 * 1024 + (16 * sh + tok + 32 * g) * 16;
-        wf[pp][sh] = cat32v(*reinterpret_cast<const i32x4*>(lo), *reinterpret_cast<const i32x4*>(lo + 1024));
-      }
+      for (int dp = 0; dp < PG; ++dp)
 #pragma unroll
-    for (int pp = 0; pp < NPW; ++pp) {
-      const float sb = GATEUP ? ((pp & 1) ? sw1 : sw0) : (dn_second ? sw1 : sw0);
+        for (int sh = 0; sh < 2; ++sh) {
+          const uint8_t* lo = Bs + (wn * NPW + p0 + dp) * kStepPanelBytes + j0 * 1024 + (16 * sh + tok + 32 * g) * 16;
+          wf[dp][sh] = cat32v(*reinterpret_cast<const i32x4*>(lo), *reinterpret_cast<const i32x4*>(lo + 1024));
+        }
 #pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        const i32x8 w = wf[pp][sh];
+      for (int dp = 0; dp < PG; ++dp) {
+        const int pp = p0 + dp;
+        // gate/up: even panels gate, odd up; down: the 128-column block of the panel
+        const float sb = GATEUP ? ((pp & 1) ? sw1 : sw0) : ((wn * NPW + pp) >= 4 ? sw1 : sw0);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
-          t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x[rt], t, 0, 0, 0, 0, 0, 0);
-          const float sc = sa[rt] * sb;
+        for (int sh = 0; sh < 2; ++sh) {
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) acc[rt][pp * 2 + sh][r4] += t[r4] * sc;
+          for (int rt = 0; rt < RT; ++rt) {
+            f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+            t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[dp][sh], x[rt], t, 0, 0, 0, 0, 0, 0);
+            const float sc = sa[rt] * sb;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) acc[rt][pp * 2 + sh][r4] += t[r4] * sc;
+          }
         }
       }
     }
@@ -310,7 +326,7 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int mi = rt * 16 + tok;
-        const int m = wm * 32 + mi;
+        const int m = wm * WR + mi;
         float amax = 0.0f;
 #pragma unroll
         for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, red[(wm * WN + w2) * 32 + mi]);
@@ -343,7 +359,7 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
     } else {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const int m = wm * 32 + rt * 16 + tok;
+        const int m = wm * WR + rt * 16 + tok;
         if (m >= rows) continue;
         uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes;
 #pragma unroll

@@ -56,6 +56,21 @@ __device__ inline void store_pair16(uint8_t* dst, uint2 lo, uint2 hi_v, bool upp
   *reinterpret_cast<uint4*>(dst) = upper ? make_uint4(rcv.x, rcv.y, hi_v.x, hi_v.y) : make_uint4(lo.x, lo.y, rcv.x, rcv.y);
 }
 
+// Four 16-byte LDS reads at the given byte addresses, waited for inside the
+// same asm block (the outputs are complete when it ends).  For reads the
+// compiler must not order against in-flight copies into LDS.
+__device__ inline void lds_read4x16(i32x4 (&d)[4], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+
 // Raw buffer resource: stride 0, byte-addressed; reads at offsets >= the
 // record count return zero without touching memory.
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {

@@ -49,6 +49,11 @@ using namespace dev;
 #ifndef AFD_B_AUX
 #define AFD_B_AUX 2
 #endif
+// activation rows: 1 = copied once per workgroup into LDS and shared by its
+// waves, 0 = loaded by every wave into registers
+#ifndef AFD_STREAM_LDS_A
+#define AFD_STREAM_LDS_A 1
+#endif
 #ifndef AFD_PIPE_SCHED
 #define AFD_PIPE_SCHED 1
 #endif
@@ -66,6 +71,15 @@ struct Stage {
   uint4 b[NPW][4];
 };
 
+template <int NPW>
+struct StageB {
+  uint4 b[NPW][4];
+};
+
+constexpr int kArowSlots = 4;  // LDS slots of activation rows (shared-row variant; a power of 2)
+template <int MR>
+constexpr int kArowBytes = AFD_STREAM_LDS_A ? kArowSlots * MR * 32 * kStepBytes : 0;
+
 }  // namespace
 
 #ifndef AFD_DOWN_NPW
@@ -77,8 +91,9 @@ struct Stage {
 template <bool GATEUP, int MR>
 __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
   constexpr int NPW = (GATEUP || MR > 1) ? 2 : AFD_DOWN_NPW;
+
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = uniform(threadIdx.x >> 6);
   const int g = lane >> 5;
   const int col = lane & 31;
 
@@ -130,6 +145,98 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mr][pp][r] = 0.0f;
 
+#if AFD_STREAM_LDS_A
+    {
+      // kArowSlots x MR x 32 rows x 128 bytes (declared here, inside the block:
+      // see the ring GEMM for why the copies want a local declaration)
+      extern __shared__ __attribute__((aligned(16))) uint8_t arow[];
+      // The step's activation rows go through LDS once per workgroup: wave w
+      // copies rows 8w .. 8w+7 of every fragment (8 whole 128-byte rows per
+      // copy), and every wave reads its MFMA fragments from there.  Weights
+      // stay in registers.  Every wave runs the loop (copies and barriers),
+      // an inactive one on out-of-range weight offsets.
+      const int oobA = (int)(p.a_bytes > 0x7fffffff ? 0x7fffffff : p.a_bytes);
+      const int oobB = (int)p.b_expert_bytes;
+      const int bbase = active ? boff : oobB;
+      // copy lane L: row 8 wave + L / 8 of a fragment, 16-byte chunk
+      // (L + L / 8) % 8 of it, landing at byte 16 L of the wave's KiB: each
+      // row's chunks are rotated by the row, so a fragment read is
+      // conflict-free
+      int doff[MR];
+#pragma unroll
+      for (int mr = 0; mr < MR; ++mr) {
+        const int r8 = lane >> 3;
+        const int m = mr * 32 + 8 * wave + r8;
+        const int r = row0 + (m < rows ? m : 0);
+        int src = r;
+        if (p.gather) src = r >= p.shared_row0 ? (r - p.shared_row0) : (p.sorted_assign[r] / p.top_k);
+        doff[mr] = (int)(src * p.a_row_bytes) + (((lane & 7) + r8) & 7) * 16;
+      }
+      // fragment read of lane (col, g), chunk 4g + j of row col
+      const int rbase = (col >> 3) * 1024 + (col & 7) * 128;
+      auto load = [&](StageB<NPW>& s, int c) {
+        const bool in = c < ks;
+        uint8_t* dst = arow + (c & (kArowSlots - 1)) * (MR * 32 * kStepBytes) + wave * 1024;
+        const int sa = uniform(in ? c * kStepBytes : oobA);
+        const int sb = uniform(in && active ? bbase + c * kStepPanelBytes : oobB);
+#pragma unroll
+        for (int mr = 0; mr < MR; ++mr) dma16(ra, dst + mr * 4096, doff[mr], sa);
+#pragma unroll
+        for (int pp = 0; pp < NPW; ++pp)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s.b[pp][j] = bload16<AFD_B_AUX>(rb, voffB, sb + pp * bpanel + j * 1024);
+      };
+      auto compute = [&](const StageB<NPW>& s, int c) {
+        const uint8_t* src = arow + (c & (kArowSlots - 1)) * (MR * 32 * kStepBytes) + rbase;
+        // The fragment reads are one asm block that also waits for them: as
+        // plain loads, the compiler would make them wait for the copies of
+        // the next step too (they might write the same LDS), which drains the
+        // pipeline; the slot protocol above already orders them.
+        i32x4 af[MR][4];
+#pragma unroll
+        for (int mr = 0; mr < MR; ++mr) {
+          uint32_t ad[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            ad[j] = (uint32_t)(uintptr_t)(lds_ptr)(src + mr * 4096 + (((4 * g + j) - (col & 7)) & 7) * 16);
+          lds_read4x16(af[mr], ad);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int mr = 0; mr < MR; ++mr)
+#pragma unroll
+            for (int pp = 0; pp < NPW; ++pp)
+              acc[mr][pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  as_bf16x8(s.b[pp][j]), __builtin_bit_cast(bf16x8, af[mr][j]), acc[mr][pp], 0, 0, 0);
+      };
+      // NST register stages of weights, kArowSlots LDS slots of rows: the
+      // copy of step c + NST - 1 refills the slot read at step c + NST - 1 -
+      // kArowSlots, which every wave finished before the previous barrier
+      constexpr int NST = MR == 1 ? AFD_STAGES_MR1 : AFD_STAGES_MR2;
+      constexpr int PER = MR + 4 * NPW;  // copies + weight loads per step
+      static_assert(NST + 1 <= kArowSlots, "row slots");
+      StageB<NPW> st[NST];
+#pragma unroll
+      for (int i = 0; i + 1 < NST; ++i) {
+        load(st[i], i);
+        AFD_PIPE_FENCE();
+      }
+      for (int c0 = 0; c0 < ks; c0 += NST) {
+#pragma unroll
+        for (int i = 0; i < NST; ++i) {
+          load(st[(i + NST - 1) % NST], c0 + i + NST - 1);
+          AFD_PIPE_FENCE();
+          wait_vmcnt<(NST - 1) * PER>();  // step c0 + i has landed (this wave's loads and copies) ...
+          raw_barrier();                  // ... and every wave's copies
+          compute(st[i], c0 + i);
+          AFD_PIPE_FENCE();
+        }
+      }
+      wait_vmcnt<0>();  // the copies of steps past the end
+      raw_barrier();    // every wave is done with the row slots before the next task
+    }
+#else
     if (active) {
       // Loads of step c >= ks use an offset past the end of the buffer, which
       // the buffer unit returns as zeros: the loop body stays branch-free (so
@@ -182,6 +289,7 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
       }
     }
 
+#endif
     // ---------------------------------------------------------------- epilogue
     if (!active) continue;
     if (GATEUP) {
@@ -239,7 +347,7 @@ static hipError_t launch_one(const GemmParams& p, int64_t max_tasks, int num_cus
   static int per_cu = 0;
   if (per_cu == 0) {
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_grouped_kernel<GATEUP, MR>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_grouped_kernel<GATEUP, MR>, 256, kArowBytes<MR>) !=
             hipSuccess ||
         occ <= 0)
       occ = 1;
@@ -247,7 +355,7 @@ static hipError_t launch_one(const GemmParams& p, int64_t max_tasks, int num_cus
   }
   const int64_t grid = std::min<int64_t>(max_tasks, (int64_t)num_cus * per_cu);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_grouped_kernel<GATEUP, MR>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_grouped_kernel<GATEUP, MR>), dim3((unsigned)grid), dim3(256), kArowBytes<MR>, s, p);
   return hipGetLastError();
 }
 

@@ -19,7 +19,10 @@
 // reduction straight from HBM into MFMA operand registers (the packed layout
 // makes each 16-byte lane load one contiguous KiB per wave), with the next
 // super-step's loads in flight while the current one is multiplied.  The
-// activation rows are small, shared by the 4 waves and served from cache.
+// activation rows are small and shared by the 4 waves: each step's rows are
+// copied once per workgroup into LDS (a whole 128-byte row per 8 lanes, so a
+// copy costs one cache-line request per row instead of one per row and wave
+// and fragment), and each wave reads its fragments from there.
 //
 // MFMA orientation: the weight fragment is the first operand and the
 // activation fragment the second, so the 32x32 accumulator holds out^T: lane l
@@ -41,6 +44,9 @@ using namespace dev;
 // register stages per wave, by row fragments per tile
 #ifndef AFD_STAGES_MR1
 #define AFD_STAGES_MR1 2
+#endif
+#ifndef AFD_STAGES_GU1
+#define AFD_STAGES_GU1 3  // gate/up, single-fragment tiles
 #endif
 #ifndef AFD_STAGES_MR2
 #define AFD_STAGES_MR2 2
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
       // NST register stages of weights, kArowSlots LDS slots of rows: the
       // copy of step c + NST - 1 refills the slot read at step c + NST - 1 -
       // kArowSlots, which every wave finished before the previous barrier
-      constexpr int NST = MR == 1 ? AFD_STAGES_MR1 : AFD_STAGES_MR2;
+      constexpr int NST = MR == 1 ? (GATEUP ? AFD_STAGES_GU1 : AFD_STAGES_MR1) : AFD_STAGES_MR2;
       constexpr int PER = MR + 4 * NPW;  // copies + weight loads per step
       static_assert(NST + 1 <= kArowSlots, "row slots");
       StageB<NPW> st[NST];

@@ -71,6 +71,17 @@ __device__ inline void lds_read4x16(i32x4 (&d)[4], const uint32_t (&a)[4]) {
       : "memory");
 }
 
+// m-tile mt of a device-built tile list.  The lists are not written by the
+// GEMM kernels, so the read goes through the constant address space and
+// becomes a scalar load (a vector load would need a wait of its own in the
+// middle of a load pipeline).
+__device__ inline int4 load_tile(const int4* tiles, int mt) {
+  typedef const __attribute__((address_space(4))) int* cptr;
+  const cptr c = (cptr)(const void*)tiles;
+  const int i = 4 * uniform(mt);
+  return make_int4(c[i], c[i + 1], c[i + 2], c[i + 3]);
+}
+
 // Raw buffer resource: stride 0, byte-addressed; reads at offsets >= the
 // record count return zero without touching memory.
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {

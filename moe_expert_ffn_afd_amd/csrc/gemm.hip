@@ -55,11 +55,6 @@ using namespace dev;
 #ifndef AFD_B_AUX
 #define AFD_B_AUX 2
 #endif
-// activation rows: 1 = copied once per workgroup into LDS and shared by its
-// waves, 0 = loaded by every wave into registers
-#ifndef AFD_STREAM_LDS_A
-#define AFD_STREAM_LDS_A 1
-#endif
 #ifndef AFD_PIPE_SCHED
 #define AFD_PIPE_SCHED 1
 #endif
@@ -71,20 +66,14 @@ using namespace dev;
 
 namespace {
 
-template <int MR, int NPW>
-struct Stage {
-  uint4 a[MR][4];
-  uint4 b[NPW][4];
-};
-
 template <int NPW>
 struct StageB {
   uint4 b[NPW][4];
 };
 
-constexpr int kArowSlots = 4;  // LDS slots of activation rows (shared-row variant; a power of 2)
+constexpr int kArowSlots = 4;  // LDS slots of activation rows (a power of 2)
 template <int MR>
-constexpr int kArowBytes = AFD_STREAM_LDS_A ? kArowSlots * MR * 32 * kStepBytes : 0;
+constexpr int kArowBytes = kArowSlots * MR * 32 * kStepBytes;
 
 }  // namespace
 
@@ -119,24 +108,13 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
   for (int task = rank; task < num_tasks; task += G) {
     const int mt = task % num_mt;
     const int q = task / num_mt;
-    const int4 tile = p.mtiles[mt];
+    const int4 tile = load_tile(p.mtiles, mt);
     const int expert = uniform(tile.x);
     const int row0 = uniform(tile.y);
     const int rows = uniform(tile.z);
     const int unit = q * kWaves + wave;
     const bool active = GATEUP ? (unit < p.n_panels) : (NPW * unit < p.n_panels);
 
-    // activation rows (rows past the tile's count repeat its first row): one
-    // 32-bit buffer offset per lane and row fragment; weights: SGPR offsets only
-    int aoff[MR];
-#pragma unroll
-    for (int mr = 0; mr < MR; ++mr) {
-      int m = mr * 32 + col;
-      int r = row0 + (m < rows ? m : 0);
-      int src = r;
-      if (p.gather) src = r >= p.shared_row0 ? (r - p.shared_row0) : (p.sorted_assign[r] / p.top_k);
-      aoff[mr] = (int)(src * p.a_row_bytes) + g * 64;
-    }
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b + (int64_t)expert * p.b_expert_bytes, p.b_expert_bytes);
     const int boff = uniform((int)((int64_t)(NPW * unit) * p.b_panel_bytes));
@@ -151,7 +129,6 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mr][pp][r] = 0.0f;
 
-#if AFD_STREAM_LDS_A
     {
       // kArowSlots x MR x 32 rows x 128 bytes (declared here, inside the block:
       // see the ring GEMM for why the copies want a local declaration)
@@ -242,60 +219,6 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
       wait_vmcnt<0>();  // the copies of steps past the end
       raw_barrier();    // every wave is done with the row slots before the next task
     }
-#else
-    if (active) {
-      // Loads of step c >= ks use an offset past the end of the buffer, which
-      // the buffer unit returns as zeros: the loop body stays branch-free (so
-      // the compiler's waits only cover the stage being multiplied) and the
-      // phantom step adds exact zeros.
-      const int oobA = (int)(p.a_bytes > 0x7fffffff ? 0x7fffffff : p.a_bytes);
-      const int oobB = (int)p.b_expert_bytes;
-      auto load = [&](Stage<MR, NPW>& s, int c) {
-        const bool in = c < ks;
-        const int sb = in ? boff + c * kStepPanelBytes : oobB;
-        const int sa = in ? c * kStepBytes : oobA;
-#pragma unroll
-        for (int pp = 0; pp < NPW; ++pp)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) s.b[pp][j] = bload16<AFD_B_AUX>(rb, voffB, sb + pp * bpanel + j * 1024);
-#pragma unroll
-        for (int mr = 0; mr < MR; ++mr)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) s.a[mr][j] = bload16(ra, aoff[mr], sa + j * 16);
-      };
-      auto compute = [&](const Stage<MR, NPW>& s) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int mr = 0; mr < MR; ++mr)
-#pragma unroll
-            for (int pp = 0; pp < NPW; ++pp)
-              acc[mr][pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(s.b[pp][j]), as_bf16x8(s.a[mr][j]),
-                                                                    acc[mr][pp], 0, 0, 0);
-      };
-
-      // NST register stages: the loads of step c + NST - 1 are issued, kept
-      // together by scheduling fences, ahead of step c's multiplies, so
-      // NST - 1 super-steps stay in flight per wave.
-      constexpr int NST = MR == 1 ? AFD_STAGES_MR1 : AFD_STAGES_MR2;
-      Stage<MR, NPW> st[NST];
-#pragma unroll
-      for (int i = 0; i + 1 < NST; ++i) {
-        load(st[i], i);
-        AFD_PIPE_FENCE();  // a stage's loads stay together, also here (in-order wait counts)
-      }
-      for (int c0 = 0; c0 < ks; c0 += NST) {
-#pragma unroll
-        for (int i = 0; i < NST; ++i) {
-          load(st[(i + NST - 1) % NST], c0 + i + NST - 1);
-          AFD_PIPE_FENCE();
-          compute(st[i]);
-          AFD_PIPE_FENCE();
-        }
-      }
-    }
-
-#endif
     // ---------------------------------------------------------------- epilogue
     if (!active) continue;
     if (GATEUP) {

@@ -105,16 +105,6 @@ __device__ inline void ring_decode(int t, int n, int nq, int& mt, int& q) {
   }
 }
 
-// m-tile mt of a list.  The lists are not written by this kernel, so the
-// read goes through the constant address space and becomes a scalar load (a
-// vector load would need a wait of its own in the middle of the pipeline).
-__device__ inline int4 load_tile(const int4* tiles, int mt) {
-  typedef const __attribute__((address_space(4))) int* cptr;
-  const cptr c = (cptr)(const void*)tiles;
-  const int i = 4 * uniform(mt);
-  return make_int4(c[i], c[i + 1], c[i + 2], c[i + 3]);
-}
-
 // One task as a wave holds it while its steps are issued: the m-tile, the
 // column group and the per-lane offsets (buffer descriptors are rebuilt per
 // step from these, which is cheaper than holding two tasks' in registers).

@@ -146,6 +146,8 @@ def main():
     layers = [afd.Layer(p, max_tokens=T // mbs)]
     while len(layers) < mbs:
         layers.append(layers[0].clone())
+    for layer in layers:  # the microbatches run side by side, each on its share of the CUs
+        layer.set_concurrency(mbs)
     if mbs == 1:
         parts = [p]
         streams = [torch.cuda.current_stream()]

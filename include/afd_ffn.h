@@ -120,6 +120,17 @@ afd_status afd_ffn_create(const afd_ffn_config *cfg, afd_ffn_t **out_handle);
  * (FastAFD System Design item 4: two ping-pong microbatches). */
 afd_status afd_ffn_clone(const afd_ffn_t *src, afd_ffn_t **out_handle);
 
+/* How many forwards the caller runs at once on different streams (the
+ * handle and its clones), 1 <= streams <= the device's CU count; default 1,
+ * and a clone starts with its source's value.  The GEMM kernels keep
+ * persistent grids resident: with streams = N each call's grids take 1/N of
+ * the CUs, so concurrent calls (FastAFD System Design item 4: two ping-pong
+ * microbatches) run side by side instead of one queueing behind the other's
+ * resident workgroups.  Affects scheduling only, never results.  Returns
+ * AFD_ERR_INVALID_ARG (handle unchanged) for a NULL handle or a value out of
+ * range. */
+afd_status afd_ffn_set_concurrency(afd_ffn_t *handle, int32_t streams);
+
 /*
  * One layer forward for T = num_tokens tokens (0 <= T <= max_tokens):
  *   hidden         device [T, H]: fp32 | bf16 | e4m3 codes (per dtype)

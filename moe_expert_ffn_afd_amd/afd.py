@@ -27,7 +27,7 @@ DTYPE_CODES = {"f32": AFD_DTYPE_F32, "bf16": AFD_DTYPE_BF16, "fp8": AFD_DTYPE_FP
 
 EXPORTS = ("afd_ffn_validate_config", "afd_ffn_create", "afd_ffn_clone", "afd_ffn_forward",
            "afd_ffn_destroy", "afd_ffn_status_string", "afd_ffn_last_error", "afd_ffn_debug_dispatch",
-           "afd_ffn_routing_errors", "afd_ffn_set_timing", "afd_ffn_get_timing")
+           "afd_ffn_routing_errors", "afd_ffn_set_timing", "afd_ffn_get_timing", "afd_ffn_set_concurrency")
 
 
 class afd_ffn_config(ctypes.Structure):
@@ -68,6 +68,7 @@ def load(path: str = LIB_PATH):
     lib.afd_ffn_debug_dispatch.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.afd_ffn_routing_errors.argtypes = [vp, ctypes.POINTER(i32), vp]
     lib.afd_ffn_set_timing.argtypes = [vp, i32]
+    lib.afd_ffn_set_concurrency.argtypes = [vp, i32]
     lib.afd_ffn_get_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
     for name in EXPORTS:
         if name not in ("afd_ffn_status_string", "afd_ffn_last_error"):
@@ -160,6 +161,10 @@ def afd_ffn_routing_errors(handle, stream=None) -> int:
     return int(n.value)
 
 
+def afd_ffn_set_concurrency(handle, streams: int) -> None:
+    _check(load().afd_ffn_set_concurrency(handle, int(streams)))
+
+
 def afd_ffn_set_timing(handle, enable: bool) -> None:
     _check(load().afd_ffn_set_timing(handle, 1 if enable else 0))
 
@@ -209,6 +214,10 @@ class Layer:
         other.__dict__.update(self.__dict__)
         other.handle = afd_ffn_clone(self.handle)
         return other
+
+    def set_concurrency(self, streams: int) -> None:
+        """Forwards run at once on other streams (this handle and its clones)."""
+        afd_ffn_set_concurrency(self.handle, streams)
 
     def out_like(self, T: int, device="cuda"):
         dt = torch.float32 if self.dtype == "f32" else torch.bfloat16

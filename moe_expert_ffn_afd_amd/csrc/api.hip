@@ -80,6 +80,7 @@ int esize_of(int dtype) { return dtype == kF32 ? 4 : dtype == kBF16 ? 2 : 1; }
 struct afd_ffn {
   int H = 0, I = 0, E = 0, K = 0, Tmax = 0, S = 0, dtype = 0, device = 0;
   int num_cus = 256;
+  int concurrency = 1;  // forwards the caller runs at once on other streams (afd_ffn_set_concurrency)
   WeightStore* w = nullptr;
   // workspace
   uint8_t* ws = nullptr;
@@ -349,6 +350,7 @@ afd_status afd_ffn_clone(const afd_ffn_t* src, afd_ffn_t** out_handle) {
   a->dtype = src->dtype;
   a->device = src->device;
   a->num_cus = src->num_cus;
+  a->concurrency = src->concurrency;
   a->w = src->w;
   a->w->refs.fetch_add(1);
   afd_status st = alloc_workspace(a);
@@ -479,6 +481,9 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   const int64_t rows_ld_h = (int64_t)I * esize_of(dt);
   const int64_t h_rows = nmax + (a->S ? a->Tmax : 0);
   const int occupancy_wgs = 4;  // resident workgroups per CU the persistent grids aim for
+  // CUs this call's persistent grids spread over: all of them, or an equal
+  // share when the caller runs several forwards at once on other streams
+  const int cus = std::max(1, a->num_cus / a->concurrency);
 
   if (dt == kF32) {
     F32Params g{};
@@ -494,7 +499,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.kdim = H;
     g.ndim = I;
     g.c = (float*)a->h;
-    int grid = (int)std::min<int64_t>(mt_bound * ((I + 63) / 64), (int64_t)a->num_cus * occupancy_wgs);
+    int grid = (int)std::min<int64_t>(mt_bound * ((I + 63) / 64), (int64_t)cus * occupancy_wgs);
     AFD_HIP(launch_gemm_f32(true, g, grid, s));
     if ((st = mark())) return st;
     g.gather = 0;
@@ -504,7 +509,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.kdim = I;
     g.ndim = H;
     g.c = (float*)a->y;
-    grid = (int)std::min<int64_t>(mt_bound * ((H + 63) / 64), (int64_t)a->num_cus * occupancy_wgs);
+    grid = (int)std::min<int64_t>(mt_bound * ((H + 63) / 64), (int64_t)cus * occupancy_wgs);
     AFD_HIP(launch_gemm_f32(false, g, grid, s));
     if ((st = mark())) return st;
   } else {
@@ -584,11 +589,11 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
         GemmParams both = light;
         both.mtiles2 = heavy.mtiles;
         both.num_mtiles2 = heavy.num_mtiles;
-        return launch_gemm_ring(gate_up, both, (mt_bound + mth_bound) * light.n_groups, a->num_cus, s);
+        return launch_gemm_ring(gate_up, both, (mt_bound + mth_bound) * light.n_groups, cus, s);
       }
-      hipError_t e = launch_gemm_tiled(dt, gate_up, heavy, mth_bound * heavy.n_groups, a->num_cus, s);
+      hipError_t e = launch_gemm_tiled(dt, gate_up, heavy, mth_bound * heavy.n_groups, cus, s);
       if (e != hipSuccess) return e;
-      return launch_gemm(dt, gate_up, mr, light, mt_bound * light.n_groups, a->num_cus, s);
+      return launch_gemm(dt, gate_up, mr, light, mt_bound * light.n_groups, cus, s);
     };
     AFD_HIP(stage(true, gu_light, gu_heavy));
     if ((st = mark())) return st;
@@ -633,6 +638,15 @@ afd_status afd_ffn_routing_errors(afd_ffn_t* a, int32_t* count, void* stream) {
   AFD_HIP(hipMemcpyAsync(count, a->err, 4, hipMemcpyDeviceToHost, s));
   AFD_HIP(hipStreamSynchronize(s));
   return *count > 0 ? fail(AFD_ERR_BAD_ROUTING, "%d ids outside [-1, %d)", *count, a->E) : AFD_OK;
+}
+
+afd_status afd_ffn_set_concurrency(afd_ffn_t* a, int32_t streams) {
+  g_last_error.clear();
+  if (!a) return fail(AFD_ERR_INVALID_ARG, "handle is NULL");
+  if (streams < 1 || streams > a->num_cus)
+    return fail(AFD_ERR_INVALID_ARG, "concurrency %d outside [1, %d]", streams, a->num_cus);
+  a->concurrency = streams;
+  return AFD_OK;
 }
 
 afd_status afd_ffn_set_timing(afd_ffn_t* a, int32_t enable) {

@@ -77,6 +77,19 @@ def test_dispatch_either_side_of_the_single_launch_limit():
     layer.close()
 
 
+def test_concurrency_bounds_checked():
+    p = problem(cfg("bf16"), seed=1)
+    layer = afd.Layer(p)
+    for bad in (0, -1, 1 << 20):
+        with pytest.raises(afd.AfdError):
+            layer.set_concurrency(bad)
+    layer.set_concurrency(3)  # a share that does not divide the CU count
+    out = layer.forward(p["hidden"], p["hidden_scales"], p["ids"], p["weights"])
+    torch.cuda.synchronize()
+    compare(out, oracle_out(to_host_problem(p)), "bf16", what="concurrency 3")
+    layer.close()
+
+
 def test_unused_experts_poisoned_with_nan():
     T, E, K = 50, 8, 2
     rng = np.random.default_rng(4)

@@ -91,13 +91,20 @@ def test_verify_shard_two_streams_ping_pong():
     torch.cuda.synchronize()
     mbs = [inputs.slice_tokens(p, 0, half), inputs.slice_tokens(p, half, T)]
     s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
-    outs = [l0.out_like(half), l1.out_like(half)]
-    torch.cuda.synchronize()
-    for layer, mb, st, o in ((l0, mbs[0], s0, outs[0]), (l1, mbs[1], s1, outs[1])):
-        with torch.cuda.stream(st):
-            layer.forward(mb["hidden"], mb["hidden_scales"], mb["ids"], mb["weights"], out=o, stream=st)
-    torch.cuda.synchronize()
-    pp = torch.cat(outs)
+    runs = []
+    for conc in (1, 2):  # whole-device grids, then each call on half the CUs
+        say("concurrency", conc)
+        l0.set_concurrency(conc)
+        l1.set_concurrency(conc)
+        outs = [l0.out_like(half), l1.out_like(half)]
+        torch.cuda.synchronize()
+        for layer, mb, st, o in ((l0, mbs[0], s0, outs[0]), (l1, mbs[1], s1, outs[1])):
+            with torch.cuda.stream(st):
+                layer.forward(mb["hidden"], mb["hidden_scales"], mb["ids"], mb["weights"], out=o, stream=st)
+        torch.cuda.synchronize()
+        runs.append(torch.cat(outs))
+    assert torch.equal(runs[0], runs[1]), "the CU share changed the result"
+    pp = runs[1]
     assert torch.equal(pp, single), "ping-pong microbatches differ from the single call"
     local = (p["ids"] >= 0).float().mean().item()
     say("  local hit fraction %.3f" % local)

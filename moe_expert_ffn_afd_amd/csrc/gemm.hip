@@ -15,8 +15,9 @@
 // holds runs of at most 32*MR rows of one expert.  A workgroup task is one
 // m-tile times one group of 4 "units" along N, one unit per wave: for gate/up
 // a unit is gate panel p plus up panel p (32 h columns, so a task covers 128
-// h columns); for down a unit is two adjacent 32-column panels of H.  Every wave streams its own panels over the whole
-// reduction straight from HBM into MFMA operand registers (the packed layout
+// h columns); for down a unit is NPW adjacent 32-column panels of H (4 for
+// single-fragment tiles, else 2).  Every wave streams its own panels over the
+// whole reduction straight from HBM into MFMA operand registers (the packed layout
 // makes each 16-byte lane load one contiguous KiB per wave), with the next
 // super-step's loads in flight while the current one is multiplied.  The
 // activation rows are small and shared by the 4 waves: each step's rows are

@@ -29,7 +29,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}
 METRIC = "routed tokens/s per MoE layer on 1 MI355X; % of MFMA/HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ("gemm.hip", "gemm_tiled.hip", "gemm_ring.hip", "afd_device.h", "afd_internal.h")
+KERNEL_SOURCES = ("gemm.hip", "gemm_stream.h", "gemm_tiled.hip", "gemm_ring.hip", "afd_device.h", "afd_internal.h")
 
 
 def kernel_source_hash() -> str:
@@ -48,8 +48,9 @@ def gate_up_kernels(cfg: dict, t_mb: int) -> str:
         return "gate/up + SwiGLU stage: gemm_f32_kernel<true> (one launch)"
     if not cfg.get("shared_inter") and t_mb * cfg["K"] <= 16 * cfg["E"]:
         return "gate/up + SwiGLU stage: gemm_grouped_kernel<true, 1> (every expert in 32-row tiles, one launch)"
-    return ("gate/up + SwiGLU stage: gemm_tiled_kernel<true> (experts above one light tile) "
-            "then gemm_grouped_kernel<true, MR> (light experts), same stream")
+    mr = 1 if t_mb * cfg["K"] <= 32 * cfg["E"] else 2
+    return ("gate/up + SwiGLU stage: gemm_mixed_kernel<true, %d> (one launch: heavy tiles and light "
+            "experts on disjoint CUs, side by side)" % mr)
 
 
 def algorithmic_units(cfg: dict, ids) -> dict:

@@ -82,9 +82,23 @@ struct DispatchParams {
   int32_t shared_row0;     // first shared row (N_max)
   int4* mtiles;            // light tile list
   int4* mtiles_heavy;      // heavy tile list
-  int32_t* num_mtiles;     // [2]: light, heavy
+  int32_t* num_mtiles;     // [3]: light tiles, heavy tiles, light workgroups of the mixed GEMM
   int32_t fused;           // 1: count_scan also places the slots (n_flat <= kDispatchFuseSlots)
+  int32_t mix_cus;         // > 0: workgroups of the mixed bf16 GEMM launches (one per CU)
 };
+
+// Cost of one heavy bf16 m-tile (tiled_rows() rows, both GEMMs) in units of
+// one light m-tile, each on one CU: a heavy tile's MFMA time against a light
+// tile's weight stream at the rate one light workgroup sustains beside the
+// heavy ones (about 37 GB/s).  Measured on the aggregated Zipf batch: a heavy
+// tile takes about 2.2 ms of one CU, a light one about 1.0 ms, and of the
+// ratios tried (1.8, 2.2, 2.8) 1.8-2.2 balance the two roles; the ratio does
+// not depend on H or I (both costs scale with H*I).  The dispatch splits the
+// mixed launch's workgroups in proportion to the two lists' costs.
+#ifndef AFD_HEAVY_TILE_COST
+#define AFD_HEAVY_TILE_COST 2.2f
+#endif
+constexpr float kHeavyTileCost = AFD_HEAVY_TILE_COST;
 
 struct GemmParams {
   const int4* mtiles;
@@ -166,7 +180,10 @@ hipError_t launch_gather_scales(const ScaleGatherParams& p, hipStream_t s);
 int down_panels_per_task(int mr);
 hipError_t launch_gemm(int dtype, bool gate_up, int mr, const GemmParams& p, int64_t max_tasks,
                        int num_cus, hipStream_t s);
-hipError_t launch_gemm_tiled(int dtype, bool gate_up, const GemmParams& p, int64_t max_tasks, int num_cus,
+// bf16 layers with heavy experts (gemm_tiled.hip): one launch of num_cus
+// workgroups runs the heavy list (LDS-tiled) and the light list (streaming)
+// side by side, split as the dispatch decided (num_mtiles[2])
+hipError_t launch_gemm_mixed(bool gate_up, int mr, const GemmParams& heavy, const GemmParams& light, int num_cus,
                              hipStream_t s);
 int tiled_rows(int dtype);  // m-tile rows of the LDS-tiled GEMM
 int tiled_panels();         // weight panels of one LDS-tiled task

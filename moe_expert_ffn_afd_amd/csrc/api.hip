@@ -170,7 +170,7 @@ afd_status alloc_workspace(afd_ffn* a) {
   int64_t off = 0;
   auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + bytes, 256); return o; };
   const int64_t o_counts = take(4ll * a->E), o_offsets = take(4ll * (a->E + 1)), o_err = take(4),
-                o_nmt = take(8), o_cb = take(4ll * a->max_chunks * a->E), o_sa = take(4 * nmax),
+                o_nmt = take(16), o_cb = take(4ll * a->max_chunks * a->E), o_sa = take(4 * nmax),
                 o_ro = take(4 * nmax), o_mt = take(16ll * a->max_mtiles), o_mth = take(16ll * a->max_mtiles),
                 o_h = take(rows * a->I * es),
                 o_hs = take(a->dtype == kFP8 ? rows * (a->I / 128) * 4 : 0),
@@ -413,6 +413,9 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   // light tiles, which saves the two (nearly always empty) heavy launches
   const bool light_only = dt == kF32 || (dt == kBF16 && !a->S && n_flat <= 16ll * E);
   const int heavy_min = light_only ? 0x7fffffff : bm + 1;
+  // CUs this call's persistent grids spread over: all of them, or an equal
+  // share when the caller runs several forwards at once on other streams
+  const int cus = std::max(1, a->num_cus / a->concurrency);
   std::vector<hipEvent_t> ev;
   auto mark = [&]() -> afd_status {
     if (!a->timing) return AFD_OK;
@@ -431,6 +434,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   d.chunk_shift = chunk_shift_for(n_flat, E);
   d.n_chunks = (int32_t)((n_flat + (1ll << d.chunk_shift) - 1) >> d.chunk_shift);
   d.fused = n_flat <= kDispatchFuseSlots ? 1 : 0;
+  d.mix_cus = (dt == kBF16 && !light_only) ? cus : 0;
   d.counts = a->counts;
   d.offsets = a->offsets;
   d.chunk_base = a->chunk_base;
@@ -481,9 +485,6 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   const int64_t rows_ld_h = (int64_t)I * esize_of(dt);
   const int64_t h_rows = nmax + (a->S ? a->Tmax : 0);
   const int occupancy_wgs = 4;  // resident workgroups per CU the persistent grids aim for
-  // CUs this call's persistent grids spread over: all of them, or an equal
-  // share when the caller runs several forwards at once on other streams
-  const int cus = std::max(1, a->num_cus / a->concurrency);
 
   if (dt == kF32) {
     F32Params g{};
@@ -579,11 +580,13 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     dn_heavy.num_mtiles = a->num_mtiles + 1;
     dn_heavy.n_groups = (H / 32 + tiled_panels() - 1) / tiled_panels();  // bf16 only
 
-    // Both lists on the caller's stream, heavy first.  (Running the light list
-    // on a second stream did not overlap the two: a heavy workgroup's LDS and
-    // registers leave no room for a light one on the same CU, and the mixed
-    // order only lengthened the tails.)  Block-FP8 runs both lists in one
-    // launch of the ring GEMM.
+    // One launch per GEMM.  bf16: the light list alone (streaming kernel, several
+    // workgroups per CU) or, once heavy experts may occur, the mixed kernel:
+    // one workgroup per CU, the dispatch's share of them streaming the light
+    // list while the rest run the heavy tiles (HBM-bound and MFMA-bound work
+    // side by side; a heavy workgroup leaves no room for a light one on its
+    // CU, so the split is by CU).  Block-FP8 runs both lists in one launch of
+    // the ring GEMM.
     auto stage = [&](bool gate_up, const GemmParams& light, const GemmParams& heavy) -> hipError_t {
       if (fp8) {
         GemmParams both = light;
@@ -591,9 +594,8 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
         both.num_mtiles2 = heavy.num_mtiles;
         return launch_gemm_ring(gate_up, both, (mt_bound + mth_bound) * light.n_groups, cus, s);
       }
-      hipError_t e = launch_gemm_tiled(dt, gate_up, heavy, mth_bound * heavy.n_groups, cus, s);
-      if (e != hipSuccess) return e;
-      return launch_gemm(dt, gate_up, mr, light, mt_bound * light.n_groups, cus, s);
+      if (light_only) return launch_gemm(dt, gate_up, mr, light, mt_bound * light.n_groups, cus, s);
+      return launch_gemm_mixed(gate_up, mr, heavy, light, cus, s);
     };
     AFD_HIP(stage(true, gu_light, gu_heavy));
     if ((st = mark())) return st;

@@ -57,6 +57,22 @@ __device__ inline int block_exclusive_scan_1024(int v, int* lds_waves, int* tota
   return r;
 }
 
+// Workgroups of the mixed bf16 GEMM launch (cus of them) that take the light
+// list: in proportion to the light list's share of the cost, a multiple of 8
+// where cus is (the same number on every XCD), at least one for a nonempty
+// list of either kind.
+__device__ inline int mixed_light_workgroups(int cus, int nl, int nh) {
+  if (cus <= 0 || nl == 0) return 0;
+  if (nh == 0) return cus;
+  const float share = (float)nl / ((float)nl + kHeavyTileCost * (float)nh);
+  int l = (int)(share * (float)cus + 0.5f);
+  if (cus % kXcds == 0 && cus >= 2 * kXcds) {
+    l = (l + kXcds / 2) / kXcds * kXcds;
+    return min(max(l, kXcds), cus - kXcds);
+  }
+  return min(max(l, 1), cus - 1);
+}
+
 }  // namespace
 
 // Stable placement of the flat slots [f0, f_end) in rounds of 1024: cursor[e]
@@ -202,8 +218,10 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
       list[base + j] = make_int4(E, p.shared_row0 + r0, min(bms, p.shared_rows - r0), 0);
     }
     if (tid == 0) {
-      p.num_mtiles[0] = n_light + (sh_heavy ? 0 : n_shared);
-      p.num_mtiles[1] = n_heavy + (sh_heavy ? n_shared : 0);
+      const int nl = n_light + (sh_heavy ? 0 : n_shared), nh = n_heavy + (sh_heavy ? n_shared : 0);
+      p.num_mtiles[0] = nl;
+      p.num_mtiles[1] = nh;
+      p.num_mtiles[2] = mixed_light_workgroups(p.mix_cus, nl, nh);
     }
   }
 

@@ -30,9 +30,15 @@
 // 32x32x16, 128 fp32 accumulators per lane; ring of 4 half-super-step slots
 // (128 KiB), three in flight while one is multiplied.  (Block-FP8 layers run
 // gemm_ring.hip.)
+//
+// The kernel launched is gemm_mixed_kernel: one 8-wave workgroup per CU, of
+// which the dispatch gives a share to the light list (the streaming body of
+// gemm_stream.h, as two 4-wave halves) and the rest to the heavy tiles, so
+// the HBM-bound light experts and the MFMA-bound heavy ones run at the same
+// time on disjoint CUs.
 #include <algorithm>
 
-#include "afd_device.h"
+#include "gemm_stream.h"
 
 namespace afd {
 
@@ -82,8 +88,9 @@ __device__ inline int swz(int r) {
 
 }  // namespace
 
+// The heavy tasks as workgroup b of G.
 template <bool GATEUP>
-__global__ __launch_bounds__(kNW * 64, 1) void gemm_tiled_kernel(GemmParams p) {
+__device__ __forceinline__ void tiled_body(const GemmParams& p, const int b, const int G) {
   constexpr int NW = kNW, WM = kWM, WN = kWN, BM = kBM, NS = kNS, SUB = kSUB;
   constexpr int RB = kStepBytes / SUB;        // activation bytes per row and slot
   constexpr int PB = kStepPanelBytes / SUB;   // weight bytes per panel and slot
@@ -117,9 +124,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_tiled_kernel(GemmParams p) {
   // outer within a block, and workgroup ranks renumbered so each XCD owns a
   // contiguous run of tasks.  The ~32 tiles an XCD runs at once then share a
   // few activation chunks and weight panels through its L2.
-  const int G = gridDim.x;
-  const int rank = (AFD_TILED_XCD_REMAP && G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds
-                                                           : blockIdx.x;
+  const int rank = (AFD_TILED_XCD_REMAP && G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
   const int nq = p.n_groups;
   const int full = (num_mt / kMB) * kMB * nq;  // tasks in complete blocks
   const int rem = num_mt % kMB;
@@ -273,33 +278,48 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_tiled_kernel(GemmParams p) {
   }
 }
 
-template <bool GATEUP>
-static hipError_t launch_tiled_one(const GemmParams& p, int64_t max_tasks, int num_cus, hipStream_t s) {
-  static int per_cu = 0;
-  if (per_cu == 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled_kernel<GATEUP>),
+// One launch per GEMM of a bf16 layer with heavy experts: one workgroup of 8
+// waves per CU, the first L of them (L from the dispatch, a multiple of 8
+// where the grid is, so every XCD gets L/8) stream the light list as two
+// 4-wave halves, the others run the heavy tiles.  The light tasks are bound
+// by HBM and the heavy ones by MFMA and LDS, so running both at once overlaps
+// the two limits instead of paying them one after the other.
+template <bool GATEUP, int MR>
+__global__ __launch_bounds__(kNW * 64, 1) void gemm_mixed_kernel(GemmParams heavy, GemmParams light) {
+  static_assert(kNW == 2 * kWaves, "the light role runs two 4-wave halves");
+  static_assert(2 * kArowBytes<MR> <= kLds, "the light role's row slots fit the tiled ring");
+  const int n = gridDim.x;
+  const int L = min(max(uniform(light.num_mtiles[2]), 0), n);
+  if ((int)blockIdx.x < L)
+    stream_body<GATEUP, MR, 2>(light, blockIdx.x, L);
+  else
+    tiled_body<GATEUP>(heavy, blockIdx.x - L, n - L);
+}
+
+template <bool GATEUP, int MR>
+static hipError_t launch_mixed_one(const GemmParams& heavy, const GemmParams& light, int num_cus, hipStream_t s) {
+  static bool ready = false;
+  if (!ready) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mixed_kernel<GATEUP, MR>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
-    int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_tiled_kernel<GATEUP>, kNW * 64, kLds) !=
-            hipSuccess ||
-        occ <= 0)
-      occ = 1;
-    per_cu = occ;
+    ready = true;
   }
-  const int64_t grid = std::min<int64_t>(max_tasks, (int64_t)num_cus * per_cu);
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_tiled_kernel<GATEUP>), dim3((unsigned)grid), dim3(kNW * 64), kLds, s, p);
+  if (num_cus <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_mixed_kernel<GATEUP, MR>), dim3((unsigned)num_cus), dim3(kNW * 64), kLds, s, heavy, light);
   return hipGetLastError();
 }
 
 int tiled_rows(int dtype) { return dtype == kBF16 ? kBM : 0; }
 int tiled_panels() { return kBNP; }
 
-hipError_t launch_gemm_tiled(int dtype, bool gate_up, const GemmParams& p, int64_t max_tasks, int num_cus,
+hipError_t launch_gemm_mixed(bool gate_up, int mr, const GemmParams& heavy, const GemmParams& light, int num_cus,
                              hipStream_t s) {
-  if (dtype != kBF16) return hipErrorInvalidValue;
-  return gate_up ? launch_tiled_one<true>(p, max_tasks, num_cus, s) : launch_tiled_one<false>(p, max_tasks, num_cus, s);
+  if (mr == 1)
+    return gate_up ? launch_mixed_one<true, 1>(heavy, light, num_cus, s) : launch_mixed_one<false, 1>(heavy, light, num_cus, s);
+  if (mr == 2)
+    return gate_up ? launch_mixed_one<true, 2>(heavy, light, num_cus, s) : launch_mixed_one<false, 2>(heavy, light, num_cus, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace afd

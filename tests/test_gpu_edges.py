@@ -90,6 +90,39 @@ def test_concurrency_bounds_checked():
     layer.close()
 
 
+def round_robin_ids(T, E, K):
+    """Slot k of token t -> expert (K t + k) % E: every expert gets T K / E rows (+-1)."""
+    return ((np.arange(T)[:, None] * K + np.arange(K)[None, :]) % E).astype(np.int32)
+
+
+@pytest.mark.parametrize("case", ["heavy_only", "light_only", "both", "both_on_a_share_of_3"])
+def test_mixed_launch_role_split(case):
+    """bf16 batches past the decode bound (more than 16 rows per expert on
+    average) run one launch per GEMM whose workgroups the dispatch splits
+    between the heavy (LDS-tiled) and the light (streaming) tile lists: all
+    heavy, all light, both, and both on a CU share that is not a multiple of 8."""
+    rng = np.random.default_rng(11)
+    if case == "heavy_only":      # 128 rows on each of 8 experts: heavy tiles only
+        c, routing = cfg("bf16", T=512, E=8, K=2), round_robin_ids(512, 8, 2)
+    elif case == "light_only":    # 18-19 rows on each of 64 experts: light tiles only
+        c, routing = cfg("bf16", T=600, E=64, K=2), round_robin_ids(600, 64, 2)
+    else:                         # Zipf: a few heavy experts, many light ones
+        c, routing = dict(dtype="bf16", T=513, H=256, I=256, E=32, K=4, routing="zipf", zipf_s=1.2,
+                          shared_inter=0), None
+    if routing is not None:
+        routing = (routing, rng.uniform(0.0, 1.0, size=routing.shape).astype(np.float32))
+    say("case", case)
+    p = problem(c, seed=12, routing=routing)
+    layer = afd.Layer(p)
+    if case == "both_on_a_share_of_3":
+        layer.set_concurrency(3)
+    out = layer.forward(p["hidden"], p["hidden_scales"], p["ids"], p["weights"])
+    torch.cuda.synchronize()
+    check_dispatch(layer, p)
+    compare(out, oracle_out(to_host_problem(p)), "bf16", what=case)
+    layer.close()
+
+
 def test_unused_experts_poisoned_with_nan():
     T, E, K = 50, 8, 2
     rng = np.random.default_rng(4)

@@ -7,7 +7,9 @@ grouped GEMM gate/up + SwiGLU, grouped GEMM down, combine) over one batch of
 seeded synthetic tokens already resident in HBM; the verify_shard workload
 runs its two microbatches on two streams per step.  Prints one JSON line with
 routed tokens/s, the roofline of the dominant kernel (timed with HIP events
-on its own stream inside the timed region) and the oracle's CPU baseline.
+on its own stream inside the timed region, the only stage timed there) and
+the oracle's CPU baseline; the per-stage breakdown comes from up to 20 further
+steps with every stage timed.
 
 Other modes: --copy-calibration runs a plain device copy of known size (the
 reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters);
@@ -29,6 +31,8 @@ PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}
 METRIC = "routed tokens/s per MoE layer on 1 MI355X; % of MFMA/HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+GATE_UP_STAGE = 2  # stage index of the grouped GEMM gate/up + SwiGLU in the library's timing
+STAGE_STEPS = 20   # steps with every stage timed, after the timed steps, for the per-stage breakdown
 KERNEL_SOURCES = ("gemm.hip", "gemm_stream.h", "gemm_tiled.hip", "gemm_ring.hip", "afd_device.h", "afd_internal.h")
 
 
@@ -177,11 +181,23 @@ def main():
             done.record(streams[i])
             main_stream.wait_event(done)
 
+    def collect():
+        # average duration per forward of each timed stage (ms), then reset
+        tot, nfwd = [0.0] * afd.AFD_NUM_STAGES, 0
+        for layer in layers:
+            ms, n = afd.afd_ffn_get_timing(layer.handle)
+            tot = [a + b for a, b in zip(tot, ms)]
+            nfwd += n
+        return [m / max(nfwd, 1) for m in tot]
+
     for _ in range(args.warmup):
         step_fn()
     torch.cuda.synchronize()
+    # In the timed steps only the gate/up stage (the roofline's kernel) is
+    # bracketed by HIP events on its stream: every event costs the stream a
+    # few microseconds, which the step time should not carry.
     for layer in layers:
-        afd.afd_ffn_set_timing(layer.handle, True)
+        afd.afd_ffn_set_timing_stages(layer.handle, [GATE_UP_STAGE])
         afd.afd_ffn_get_timing(layer.handle)  # reset
 
     torch.cuda.synchronize()
@@ -190,20 +206,23 @@ def main():
         step_fn()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    gu_launch_ms = collect()[GATE_UP_STAGE]
 
-    stage_ms = [0.0] * afd.AFD_NUM_STAGES
-    nfwd = 0
+    # The per-stage breakdown comes from further steps with every stage timed.
     for layer in layers:
-        ms, n = afd.afd_ffn_get_timing(layer.handle)
-        stage_ms = [a + b for a, b in zip(stage_ms, ms)]
-        nfwd += n
-    per_launch = [m / max(nfwd, 1) for m in stage_ms]  # average launch duration per stage (ms)
+        afd.afd_ffn_set_timing(layer.handle, True)
+    for _ in range(min(args.steps, STAGE_STEPS)):
+        step_fn()
+    torch.cuda.synchronize()
+    per_launch = collect()
+    for layer in layers:
+        afd.afd_ffn_set_timing(layer.handle, False)
 
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = T / (ms_per_step * 1e-3)
     dt = cfg["dtype"]
     # dominant kernel: grouped GEMM gate/up + SwiGLU (two thirds of the weight bytes and flops)
-    gu_launch_s = per_launch[2] * 1e-3
+    gu_launch_s = gu_launch_ms * 1e-3
     launches_per_step = mbs
     gu_bytes = units["gu_bytes"] / launches_per_step
     gu_flops = units["gu_flops"] / launches_per_step
@@ -218,7 +237,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_TFLOPS[dt], 4)}
     roof["kernel"] = gate_up_kernels(cfg, T // mbs)
-    roof["launch_ms"] = round(per_launch[2], 4)
+    roof["launch_ms"] = round(gu_launch_ms, 4)
     traffic = None
     try:
         with open(TRAFFIC_FILE) as f:
@@ -252,7 +271,8 @@ def main():
                   "roofline_frac": round(max(units["layer_flops"] / (PEAK_TFLOPS[dt] * 1e12),
                                              units["layer_bytes"] / (PEAK_HBM_GBS * 1e9)) /
                                          (ms_per_step * 1e-3), 4),
-                  "stage_ms": {n: round(v, 4) for n, v in zip(afd.STAGE_NAMES, per_launch)}},
+                  "stage_ms": {n: round(v, 4) for n, v in zip(afd.STAGE_NAMES, per_launch)},
+                  "stage_ms_steps": min(args.steps, STAGE_STEPS)},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

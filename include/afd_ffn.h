@@ -183,15 +183,22 @@ afd_status afd_ffn_routing_errors(afd_ffn_t *handle, int32_t *count, void *strea
 
 /*
  * Per-kernel timing of forwards, for measurement.  When enabled, forward
- * records HIP events on its stream around each of its kernels; the query
- * synchronises on the last event and returns, per stage, the summed time in
- * milliseconds and the number of forwards since the last reset, then resets.
- * Stages: 0 dispatch count+scan, 1 dispatch scatter, 2 grouped GEMM
- * gate/up + SwiGLU, 3 grouped GEMM down, 4 combine.  ms must hold
- * AFD_NUM_STAGES floats.
+ * records HIP events on its stream around each timed stage; the query
+ * synchronises on each forward's last event and returns, per stage, the
+ * summed time in milliseconds (0 for stages not timed) and the number of
+ * forwards since the last reset, then resets.  Stages: 0 dispatch
+ * count+scan, 1 dispatch scatter, 2 grouped GEMM gate/up + SwiGLU, 3 grouped
+ * GEMM down, 4 combine.  ms must hold AFD_NUM_STAGES floats.
+ *
+ * set_timing: every stage (enable != 0) or none.  set_timing_stages: the
+ * stages whose bit is set in stage_mask (bit s = stage s; 0 = none); each
+ * event costs the stream a few microseconds, so a measurement loop times
+ * only the stages it needs.  AFD_ERR_INVALID_ARG for a NULL handle or a bit
+ * at AFD_NUM_STAGES or above.  The setting applies to later forwards.
  */
 #define AFD_NUM_STAGES 5
 afd_status afd_ffn_set_timing(afd_ffn_t *handle, int32_t enable);
+afd_status afd_ffn_set_timing_stages(afd_ffn_t *handle, uint32_t stage_mask);
 afd_status afd_ffn_get_timing(afd_ffn_t *handle, float *ms, int32_t *num_forwards);
 
 #ifdef __cplusplus

@@ -27,7 +27,8 @@ DTYPE_CODES = {"f32": AFD_DTYPE_F32, "bf16": AFD_DTYPE_BF16, "fp8": AFD_DTYPE_FP
 
 EXPORTS = ("afd_ffn_validate_config", "afd_ffn_create", "afd_ffn_clone", "afd_ffn_forward",
            "afd_ffn_destroy", "afd_ffn_status_string", "afd_ffn_last_error", "afd_ffn_debug_dispatch",
-           "afd_ffn_routing_errors", "afd_ffn_set_timing", "afd_ffn_get_timing", "afd_ffn_set_concurrency")
+           "afd_ffn_routing_errors", "afd_ffn_set_timing", "afd_ffn_set_timing_stages", "afd_ffn_get_timing",
+           "afd_ffn_set_concurrency")
 
 
 class afd_ffn_config(ctypes.Structure):
@@ -68,6 +69,7 @@ def load(path: str = LIB_PATH):
     lib.afd_ffn_debug_dispatch.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.afd_ffn_routing_errors.argtypes = [vp, ctypes.POINTER(i32), vp]
     lib.afd_ffn_set_timing.argtypes = [vp, i32]
+    lib.afd_ffn_set_timing_stages.argtypes = [vp, ctypes.c_uint32]
     lib.afd_ffn_set_concurrency.argtypes = [vp, i32]
     lib.afd_ffn_get_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
     for name in EXPORTS:
@@ -167,6 +169,14 @@ def afd_ffn_set_concurrency(handle, streams: int) -> None:
 
 def afd_ffn_set_timing(handle, enable: bool) -> None:
     _check(load().afd_ffn_set_timing(handle, 1 if enable else 0))
+
+
+def afd_ffn_set_timing_stages(handle, stages) -> None:
+    """Time only the given stage indices (0..AFD_NUM_STAGES-1) of later forwards."""
+    mask = 0
+    for st in stages:
+        mask |= 1 << int(st)
+    _check(load().afd_ffn_set_timing_stages(handle, mask))
 
 
 def afd_ffn_get_timing(handle):

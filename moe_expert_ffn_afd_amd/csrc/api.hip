@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <array>
 #include <atomic>
 #include <string>
 #include <vector>
@@ -95,10 +96,10 @@ struct afd_ffn {
   uint8_t* y = nullptr;
   int max_chunks = 0, max_mtiles = 0;
   int last_T = 0;
-  // per-stage timing
-  bool timing = false;
+  // per-stage timing: bit s of the mask times stage s (boundaries s and s + 1)
+  uint32_t timing_mask = 0;
   std::vector<hipEvent_t> ev_free;
-  std::vector<std::vector<hipEvent_t>> ev_pending;  // one list of 6 events per forward
+  std::vector<std::array<hipEvent_t, AFD_NUM_STAGES + 1>> ev_pending;  // per forward, per boundary (or null)
 };
 
 namespace {
@@ -261,7 +262,8 @@ afd_status pack_weights(const afd_ffn_config* c, afd_ffn* a) {
 void free_handle(afd_ffn* a) {
   if (!a) return;
   for (auto& v : a->ev_pending)
-    for (hipEvent_t e : v) (void)hipEventDestroy(e);
+    for (hipEvent_t e : v)
+      if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : a->ev_free) (void)hipEventDestroy(e);
   if (a->ws) (void)hipFree(a->ws);
   if (a->w && a->w->refs.fetch_sub(1) == 1) delete a->w;
@@ -416,13 +418,16 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   // CUs this call's persistent grids spread over: all of them, or an equal
   // share when the caller runs several forwards at once on other streams
   const int cus = std::max(1, a->num_cus / a->concurrency);
-  std::vector<hipEvent_t> ev;
-  auto mark = [&]() -> afd_status {
-    if (!a->timing) return AFD_OK;
+  // boundary b lies before stage b (b = AFD_NUM_STAGES: after the last)
+  std::array<hipEvent_t, AFD_NUM_STAGES + 1> ev{};
+  const uint32_t tmask = a->timing_mask;
+  auto mark = [&](int b) -> afd_status {
+    const bool need = ((tmask >> b) & 1u) || (b > 0 && ((tmask >> (b - 1)) & 1u));
+    if (!need) return AFD_OK;
     hipEvent_t e = take_event(a);
     if (!e) return fail(AFD_ERR_HIP, "hipEventCreate failed");
     AFD_HIP(hipEventRecord(e, s));
-    ev.push_back(e);
+    ev[b] = e;
     return AFD_OK;
   };
   afd_status st;
@@ -451,14 +456,12 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   d.num_mtiles = a->num_mtiles;
   a->last_T = T;
 
-  if ((st = mark())) return st;
+  if ((st = mark(0))) return st;
   AFD_HIP(launch_dispatch_count_scan(d, s));
-  if ((st = mark())) return st;
+  if ((st = mark(1))) return st;
   if (T == 0) {
-    // nothing else to do; keep the timing record shape (6 events)
-    while (ev.size() < 6 && a->timing)
-      if ((st = mark())) return st;
-    if (a->timing) a->ev_pending.push_back(ev);
+    // nothing else to do (the later stages count as not timed)
+    if (tmask) a->ev_pending.push_back(ev);
     return AFD_OK;
   }
   AFD_HIP(launch_dispatch_scatter(d, s));
@@ -477,7 +480,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     sg.ld = (int32_t)a->h_rows;
     AFD_HIP(launch_gather_scales(sg, s));
   }
-  if ((st = mark())) return st;
+  if ((st = mark(2))) return st;
 
   // upper bounds of the routed + shared m-tiles of this call, per list
   const int64_t mt_bound = n_flat / bm + std::min<int64_t>(E, n_flat) + (a->S ? (T + bm - 1) / bm : 0) + 1;
@@ -502,7 +505,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.c = (float*)a->h;
     int grid = (int)std::min<int64_t>(mt_bound * ((I + 63) / 64), (int64_t)cus * occupancy_wgs);
     AFD_HIP(launch_gemm_f32(true, g, grid, s));
-    if ((st = mark())) return st;
+    if ((st = mark(3))) return st;
     g.gather = 0;
     g.a = (const float*)a->h;
     g.w0 = (const float*)a->w->dn;
@@ -512,7 +515,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     g.c = (float*)a->y;
     grid = (int)std::min<int64_t>(mt_bound * ((H + 63) / 64), (int64_t)cus * occupancy_wgs);
     AFD_HIP(launch_gemm_f32(false, g, grid, s));
-    if ((st = mark())) return st;
+    if ((st = mark(4))) return st;
   } else {
     const int es = esize_of(dt);
     GemmParams g{};
@@ -598,9 +601,9 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
       return launch_gemm_mixed(gate_up, mr, heavy, light, cus, s);
     };
     AFD_HIP(stage(true, gu_light, gu_heavy));
-    if ((st = mark())) return st;
+    if ((st = mark(3))) return st;
     AFD_HIP(stage(false, dn_light, dn_heavy));
-    if ((st = mark())) return st;
+    if ((st = mark(4))) return st;
   }
 
   CombineParams cp{};
@@ -613,8 +616,8 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   cp.shared_row0 = a->S ? (int32_t)nmax : -1;
   cp.out = (uint8_t*)out;
   AFD_HIP(launch_combine(dt == kF32 ? kF32 : kBF16, cp, T, s));
-  if ((st = mark())) return st;
-  if (a->timing) a->ev_pending.push_back(ev);
+  if ((st = mark(5))) return st;
+  if (tmask) a->ev_pending.push_back(ev);
   return AFD_OK;
 }
 
@@ -654,7 +657,16 @@ afd_status afd_ffn_set_concurrency(afd_ffn_t* a, int32_t streams) {
 afd_status afd_ffn_set_timing(afd_ffn_t* a, int32_t enable) {
   g_last_error.clear();
   if (!a) return fail(AFD_ERR_INVALID_ARG, "handle is NULL");
-  a->timing = enable != 0;
+  a->timing_mask = enable ? (1u << AFD_NUM_STAGES) - 1 : 0u;
+  return AFD_OK;
+}
+
+afd_status afd_ffn_set_timing_stages(afd_ffn_t* a, uint32_t stage_mask) {
+  g_last_error.clear();
+  if (!a) return fail(AFD_ERR_INVALID_ARG, "handle is NULL");
+  if (stage_mask >> AFD_NUM_STAGES)
+    return fail(AFD_ERR_INVALID_ARG, "stage mask 0x%x has bits past stage %d", stage_mask, AFD_NUM_STAGES - 1);
+  a->timing_mask = stage_mask;
   return AFD_OK;
 }
 
@@ -665,13 +677,18 @@ afd_status afd_ffn_get_timing(afd_ffn_t* a, float* ms, int32_t* num_forwards) {
   for (int i = 0; i < AFD_NUM_STAGES; ++i) ms[i] = 0.0f;
   int n = 0;
   for (auto& v : a->ev_pending) {
-    AFD_HIP(hipEventSynchronize(v.back()));
-    for (int i = 0; i + 1 < (int)v.size() && i < AFD_NUM_STAGES; ++i) {
+    hipEvent_t last = nullptr;
+    for (hipEvent_t e : v)
+      if (e) last = e;
+    if (last) AFD_HIP(hipEventSynchronize(last));
+    for (int i = 0; i < AFD_NUM_STAGES; ++i) {
+      if (!v[i] || !v[i + 1]) continue;
       float t = 0.0f;
       AFD_HIP(hipEventElapsedTime(&t, v[i], v[i + 1]));
       ms[i] += t;
     }
-    for (hipEvent_t e : v) a->ev_free.push_back(e);
+    for (hipEvent_t e : v)
+      if (e) a->ev_free.push_back(e);
     ++n;
   }
   a->ev_pending.clear();

@@ -103,6 +103,7 @@ def test_null_arguments_rejected_on_host(lib):
     assert lib.afd_ffn_clone(None, ctypes.byref(h)) == afd.AFD_ERR_INVALID_ARG
     assert lib.afd_ffn_debug_dispatch(None, None, None, None, None, None) == afd.AFD_ERR_INVALID_ARG
     assert lib.afd_ffn_set_timing(None, 1) == afd.AFD_ERR_INVALID_ARG
+    assert lib.afd_ffn_set_timing_stages(None, 4) == afd.AFD_ERR_INVALID_ARG
     assert lib.afd_ffn_set_concurrency(None, 2) == afd.AFD_ERR_INVALID_ARG
     assert lib.afd_ffn_destroy(None) == afd.AFD_OK
 

@@ -225,4 +225,16 @@ def test_timing_records_every_stage():
         layer.forward(p["hidden"], None, p["ids"], p["weights"])
     ms, n = afd.afd_ffn_get_timing(layer.handle)
     assert n == 3 and all(t > 0 for t in ms), ms
+    # one stage only: the others read 0; a bit past the last stage is rejected
+    afd.afd_ffn_set_timing_stages(layer.handle, [2])
+    for _ in range(2):
+        layer.forward(p["hidden"], None, p["ids"], p["weights"])
+    ms, n = afd.afd_ffn_get_timing(layer.handle)
+    assert n == 2 and ms[2] > 0 and all(ms[i] == 0 for i in (0, 1, 3, 4)), ms
+    with pytest.raises(afd.AfdError):
+        afd.afd_ffn_set_timing_stages(layer.handle, [afd.AFD_NUM_STAGES])
+    afd.afd_ffn_set_timing(layer.handle, False)
+    layer.forward(p["hidden"], None, p["ids"], p["weights"])
+    ms, n = afd.afd_ffn_get_timing(layer.handle)
+    assert n == 0 and all(t == 0 for t in ms), ms
     layer.close()

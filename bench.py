@@ -116,6 +116,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--serial", action="store_true",
+                    help="microbatch workloads: run the microbatches one after the other on one stream, "
+                         "each on every CU (the baseline the two-stream ping-pong is compared with)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -151,23 +154,26 @@ def main():
     layers = [afd.Layer(p, max_tokens=T // mbs)]
     while len(layers) < mbs:
         layers.append(layers[0].clone())
+    serial = args.serial and mbs > 1
     for layer in layers:  # the microbatches run side by side, each on its share of the CUs
-        layer.set_concurrency(mbs)
+        layer.set_concurrency(1 if serial else mbs)
     if mbs == 1:
         parts = [p]
         streams = [torch.cuda.current_stream()]
     else:
         step = T // mbs
         parts = [inputs.slice_tokens(p, i * step, (i + 1) * step) for i in range(mbs)]
-        streams = [torch.cuda.Stream() for _ in range(mbs)]
+        streams = [torch.cuda.current_stream()] * mbs if serial else [torch.cuda.Stream() for _ in range(mbs)]
     outs = [layers[i].out_like(parts[i]["T"]) for i in range(mbs)]
 
     main_stream = torch.cuda.current_stream()
 
     def step_fn():
-        if mbs == 1:
-            layers[0].forward(p["hidden"], p["hidden_scales"], p["ids"], p["weights"], out=outs[0],
-                              stream=main_stream)
+        if mbs == 1 or serial:  # one stream
+            for i in range(mbs):
+                q = parts[i]
+                layers[i].forward(q["hidden"], q["hidden_scales"], q["ids"], q["weights"], out=outs[i],
+                                  stream=main_stream)
             return
         ev = torch.cuda.Event()
         ev.record(main_stream)
@@ -238,6 +244,8 @@ def main():
                 "frac": round(ach / PEAK_TFLOPS[dt], 4)}
     roof["kernel"] = gate_up_kernels(cfg, T // mbs)
     roof["launch_ms"] = round(gu_launch_ms, 4)
+    # launches of this kernel running at once, each on its share of the CUs
+    roof["concurrent_launches"] = 1 if serial else mbs
     traffic = None
     try:
         with open(TRAFFIC_FILE) as f:
@@ -263,7 +271,8 @@ def main():
         "data": "synthetic (seeded; random-init expert weights N(0,0.02), hidden N(0,1))",
         "config": {"workload": inputs.WORKLOAD_TITLES[args.workload], "T": T, "H": cfg["H"], "I": cfg["I"],
                    "E": cfg["E"], "top_k": cfg["K"], "shared_inter": cfg.get("shared_inter", 0),
-                   "routing": cfg["routing"], "microbatches": mbs, "routed_rows": units["N"],
+                   "routing": cfg["routing"], "microbatches": mbs, "microbatch_streams": 1 if serial else mbs,
+                   "routed_rows": units["N"],
                    "nonempty_experts": units["nonempty"] if mbs == 1 else [u["nonempty"] for u in per_mb],
                    "seed": args.seed},
         "layer": {"tflops": round(units["layer_flops"] / (ms_per_step * 1e-3) / 1e12, 2),

@@ -371,7 +371,7 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
           rcv.y = __shfl_xor(snd.y, 16, 64);
           const uint4 v = odd ? make_uint4(rcv.x, rcv.y, o1.x, o1.y) : make_uint4(o0.x, o0.y, rcv.x, rcv.y);
           const int col = odd ? 32 * P + 16 + 4 * (kg - 1) : 32 * P + 4 * kg;
-          *reinterpret_cast<uint4*>(orow + (int64_t)col * 2) = v;
+          store16<true>(orow + (int64_t)col * 2, v);
         }
       }
     }

@@ -280,7 +280,7 @@ __device__ __forceinline__ void stream_body(const GemmParams& p, const int rank,
               o[k].x = pack_bf16x2(acc[mr][pp][4 * r4 + 0], acc[mr][pp][4 * r4 + 1]);
               o[k].y = pack_bf16x2(acc[mr][pp][4 * r4 + 2], acc[mr][pp][4 * r4 + 3]);
             }
-            store_pair16(out + (16 * r2 + 8 * g) * 2, o[0], o[1], g != 0);
+            store_pair16<true>(out + (16 * r2 + 8 * g) * 2, o[0], o[1], g != 0);
           }
         }
       }

@@ -271,6 +271,8 @@ __device__ __forceinline__ void tiled_body(const GemmParams& p, const int b, con
             o[k].x = pack_bf16x2(v[0], v[1]);
             o[k].y = pack_bf16x2(v[2], v[3]);
           }
+          // (default policy: non-temporal stores of y made this kernel's down
+          // launch 14 % slower, unlike the streaming and ring GEMMs')
           store_pair16(orow + (int64_t)(col0 + 16 * r2 + (hi ? 8 : 0)) * 2, o[0], o[1], hi);
         }
       }

@@ -29,7 +29,8 @@
 //  128-deep scale block and one panel lies inside one 128-column block.
 //
 //  Workspace (per handle, sized for max_tokens T_max; N_max = T_max * K):
-//    counts[E], offsets[E+1], err[1], num_mtiles[2]
+//    counts[E], offsets[E+1], err[1], num_mtiles[3] (light tiles, heavy tiles,
+//    light workgroups of a mixed bf16 launch; 16 bytes reserved)
 //    chunk_base[n_chunks][E]          first sorted row of each (chunk, expert)
 //    sorted_assign[N_max], row_of[N_max]
 //    mtiles[max_mtiles] (int4) x 2    light and heavy lists {expert, first row, rows, 0}

@@ -13,10 +13,12 @@
 // Being a pure function of the ids, it is reproduced bit for bit.
 //
 // Two kernels (one for batches of at most kDispatchFuseSlots slots, where
-// count_scan also does the placement).  count_scan (one workgroup): per-(chunk, expert) counts with
-// LDS atomics (counts do not depend on order), per-expert prefix over chunks,
-// exclusive scan over experts, first sorted row of every (chunk, expert), and
-// the GEMM m-tile list.  scatter (one workgroup per chunk): each wave ranks its
+// count_scan also does the placement).  count_scan (one workgroup):
+// per-(chunk, expert) counts with LDS atomics (counts do not depend on order),
+// per-expert prefix over chunks, exclusive scan over experts, first sorted row
+// of every (chunk, expert), the GEMM m-tile lists and, for a mixed bf16
+// launch, how many of its workgroups take the light list.  scatter (one
+// workgroup per chunk): each wave ranks its
 // 64 slots among equal ids with ballots over the id bits (match mask, popcount
 // of the lower lanes), waves are ordered through per-wave counts in LDS, and
 // rounds of 1024 slots advance per-expert cursors, so every slot lands at its

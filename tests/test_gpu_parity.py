@@ -77,11 +77,21 @@ def test_full_size_workload(name):
     layer.close()
 
 
-def test_verify_shard_two_streams_ping_pong():
-    """Two microbatches of 2048 on two streams (clone shares weights) equal the
+PING_PONG = {
+    # the speculative-verify shard at full size (block-FP8 ring GEMMs)
+    "verify_shard": inputs.workload("verify_shard"),
+    # bf16 with Zipf routing: each microbatch has heavy and light experts, so
+    # both run the mixed launch (on all CUs, then on half of them)
+    "bf16_zipf_mixed": small("bf16", 2048, 1024, 512, 32, 8, routing="zipf"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PING_PONG))
+def test_two_streams_ping_pong(name):
+    """Two microbatches on two streams (clone shares weights) equal the
     one-call result bit for bit, and match the oracle on sampled tokens."""
-    cfg = inputs.workload("verify_shard")
-    say("workload verify_shard", inputs.WORKLOAD_TITLES["verify_shard"])
+    cfg = PING_PONG[name]
+    say("ping-pong", name, cfg)
     p = problem(cfg, 0)
     T = cfg["T"]
     half = T // 2
@@ -110,7 +120,7 @@ def test_verify_shard_two_streams_ping_pong():
     say("  local hit fraction %.3f" % local)
     tokens = np.sort(np.random.default_rng(5).choice(T, 12, replace=False))
     ref = oracle_out(to_host_problem(p), tokens)
-    compare(single, ref, "fp8", tokens=tokens, what="verify_shard")
+    compare(single, ref, cfg["dtype"], tokens=tokens, what=name)
     check_dispatch(l1, mbs[1])
     l1.close()
     l0.close()

@@ -27,8 +27,10 @@
 // banks).
 //
 // Tile 256 x 256, 8 waves (two per SIMD) as 4 x 2 of 64 rows x 4 panels, MFMA
-// 32x32x16, 128 fp32 accumulators per lane; ring of 4 half-super-step slots
-// (128 KiB), three in flight while one is multiplied.  (Block-FP8 layers run
+// 32x32x16, 128 fp32 accumulators per lane; two slots of a whole super-step
+// (64 KiB each), one copied while the other is multiplied: one barrier per
+// super-step (four slots of half a super-step, three in flight, were 1-2 %
+// slower: twice the barriers, and the copies hit in L2 anyway).  (Block-FP8 layers run
 // gemm_ring.hip.)
 //
 // The kernel launched is gemm_mixed_kernel: one 8-wave workgroup per CU, of
@@ -53,7 +55,7 @@ namespace {
 #define AFD_TILED_WM 4
 #endif
 #ifndef AFD_TILED_NS
-#define AFD_TILED_NS 4
+#define AFD_TILED_NS 2
 #endif
 #ifndef AFD_TILED_B_NT
 #define AFD_TILED_B_NT 0  // 1: weight copies non-temporal (panels are re-read by sibling m-tiles)
@@ -67,7 +69,11 @@ namespace {
 
 // NW waves form a WM x WN grid over BM rows x 8 panels; SUB ring slots per
 // super-step (a slot holds 128/SUB bytes of K per row).
-constexpr int kNW = AFD_TILED_NW, kWM = AFD_TILED_WM, kWN = kNW / kWM, kBM = 256, kNS = AFD_TILED_NS, kSUB = 2;
+#ifndef AFD_TILED_SUB
+#define AFD_TILED_SUB 1
+#endif
+constexpr int kNW = AFD_TILED_NW, kWM = AFD_TILED_WM, kWN = kNW / kWM, kBM = 256, kNS = AFD_TILED_NS,
+              kSUB = AFD_TILED_SUB;
 #ifndef AFD_TILED_BNP
 #define AFD_TILED_BNP 8
 #endif

@@ -298,10 +298,14 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_mixed_kernel(GemmParams heav
   static_assert(2 * kArowBytes<MR> <= kLds, "the light role's row slots fit the tiled ring");
   const int n = gridDim.x;
   const int L = min(max(uniform(light.num_mtiles[2]), 0), n);
-  if ((int)blockIdx.x < L)
+  if ((int)blockIdx.x < L) {
     stream_body<GATEUP, MR, 2>(light, blockIdx.x, L);
-  else
-    tiled_body<GATEUP>(heavy, blockIdx.x - L, n - L);
+    return;
+  }
+  tiled_body<GATEUP>(heavy, blockIdx.x - L, n - L);
+  // No light workgroups (no light tiles, or a grid of one workgroup, too
+  // small to split): the heavy workgroups run the light list afterwards.
+  if (L == 0) stream_body<GATEUP, MR, 2>(light, blockIdx.x, n);
 }
 
 template <bool GATEUP, int MR>

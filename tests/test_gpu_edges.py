@@ -95,12 +95,14 @@ def round_robin_ids(T, E, K):
     return ((np.arange(T)[:, None] * K + np.arange(K)[None, :]) % E).astype(np.int32)
 
 
-@pytest.mark.parametrize("case", ["heavy_only", "light_only", "both", "both_on_a_share_of_3"])
+@pytest.mark.parametrize("case", ["heavy_only", "light_only", "both", "both_on_a_share_of_3",
+                                  "both_on_two_workgroups", "both_on_one_workgroup"])
 def test_mixed_launch_role_split(case):
     """bf16 batches past the decode bound (more than 16 rows per expert on
     average) run one launch per GEMM whose workgroups the dispatch splits
     between the heavy (LDS-tiled) and the light (streaming) tile lists: all
-    heavy, all light, both, and both on a CU share that is not a multiple of 8."""
+    heavy, all light, both, both on a CU share that is not a multiple of 8,
+    and both on grids of two workgroups and of one (which runs both lists)."""
     rng = np.random.default_rng(11)
     if case == "heavy_only":      # 128 rows on each of 8 experts: heavy tiles only
         c, routing = cfg("bf16", T=512, E=8, K=2), round_robin_ids(512, 8, 2)
@@ -114,8 +116,13 @@ def test_mixed_launch_role_split(case):
     say("case", case)
     p = problem(c, seed=12, routing=routing)
     layer = afd.Layer(p)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     if case == "both_on_a_share_of_3":
         layer.set_concurrency(3)
+    elif case == "both_on_two_workgroups":
+        layer.set_concurrency(cus // 2)
+    elif case == "both_on_one_workgroup":
+        layer.set_concurrency(cus)
     out = layer.forward(p["hidden"], p["hidden_scales"], p["ids"], p["weights"])
     torch.cuda.synchronize()
     check_dispatch(layer, p)

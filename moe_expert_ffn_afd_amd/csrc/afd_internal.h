@@ -191,7 +191,9 @@ int tiled_panels();         // weight panels of one LDS-tiled task
 // Block-FP8 GEMM with a weight ring in LDS (gemm_ring.hip): one launch over
 // the heavy list (mtiles2, m-tiles of up to ring_rows(true) rows) and then the
 // light list (mtiles, up to ring_rows(false) rows)
-hipError_t launch_gemm_ring(bool gate_up, const GemmParams& p, int64_t max_tasks, int num_cus, hipStream_t s);
+// stream_weights: weight copies non-temporal (no other forward runs beside this one)
+hipError_t launch_gemm_ring(bool gate_up, bool stream_weights, const GemmParams& p, int64_t max_tasks, int num_cus,
+                            hipStream_t s);
 int ring_rows(bool heavy);
 hipError_t launch_gemm_f32(bool gate_up, const F32Params& p, int grid, hipStream_t s);
 hipError_t launch_combine(int dtype, const CombineParams& p, int tokens, hipStream_t s);

@@ -595,7 +595,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
         GemmParams both = light;
         both.mtiles2 = heavy.mtiles;
         both.num_mtiles2 = heavy.num_mtiles;
-        return launch_gemm_ring(gate_up, both, (mt_bound + mth_bound) * light.n_groups, cus, s);
+        return launch_gemm_ring(gate_up, a->concurrency == 1, both, (mt_bound + mth_bound) * light.n_groups, cus, s);
       }
       if (light_only) return launch_gemm(dt, gate_up, mr, light, mt_bound * light.n_groups, cus, s);
       return launch_gemm_mixed(gate_up, mr, heavy, light, cus, s);

@@ -59,9 +59,11 @@ namespace {
 #ifndef AFD_RING_NS
 #define AFD_RING_NS 4
 #endif
-#ifndef AFD_RING_B_AUX
-#define AFD_RING_B_AUX 0  // cache policy of the weight copies
-#endif
+// Cache policy of the weight copies (WNT = the kernel's template argument):
+// non-temporal when the layer runs alone (fp8_shared 1.6 % faster), the
+// default when other forwards run beside it (the ping-pong microbatches read
+// the same experts at about the same time, and with non-temporal copies the
+// verify shard was 2 % slower).
 #ifndef AFD_RING_RT_HEAVY
 #define AFD_RING_RT_HEAVY 1  // 16-row token tiles per wave, 128-row m-tiles
 #endif
@@ -120,7 +122,7 @@ struct RingDesc {
 // Every task rank + k * stride (k = 0, 1, ...) below n_tiles x n_groups of one
 // m-tile list, in one continuous pipeline.  Every wave of the workgroup calls
 // it with the same arguments.
-template <bool GATEUP, int BM>
+template <bool GATEUP, int BM, bool WNT>
 __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles, const int n_tiles,
                                           const int first, const int stride) {
   // declared here, not passed in: the copies need pointers known to be in LDS
@@ -226,7 +228,7 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
 #pragma unroll
     for (int k = 0; k < B_DMA; ++k) {
       const int i = wave * B_DMA + k, panel = i / 4, j = i % 4;
-      dma16_aux<AFD_RING_B_AUX>(rb, st + panel * kStepPanelBytes + j * 1024, lane * 16,
+      dma16_aux<WNT ? 2 : 0>(rb, st + panel * kStepPanelBytes + j * 1024, lane * 16,
                                 in ? pbase + panel * bpanel + c * kStepPanelBytes + j * 1024 : oobB);
     }
 #pragma unroll
@@ -458,7 +460,7 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
 // has one tail instead of two.  A workgroup runs tasks rank, rank + G, ... of
 // the two lists in a row; ranks are renumbered so that each XCD owns a
 // contiguous run of tasks (shared rows stay in its L2).
-template <bool GATEUP>
+template <bool GATEUP, bool WNT>
 __global__ __launch_bounds__(kRingWaves * 64, 1) void gemm_ring_kernel(GemmParams p) {
   const int nq = p.n_groups;
   const int nh = uniform(p.num_mtiles2 ? p.num_mtiles2[0] : 0);
@@ -467,22 +469,22 @@ __global__ __launch_bounds__(kRingWaves * 64, 1) void gemm_ring_kernel(GemmParam
   const int G = gridDim.x;
   const int rank = (AFD_RING_XCD_REMAP && G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds
                                                           : blockIdx.x;
-  if (nh > 0) ring_list<GATEUP, 128>(p, p.mtiles2, nh, rank, G);
+  if (nh > 0) ring_list<GATEUP, 128, WNT>(p, p.mtiles2, nh, rank, G);
   // this workgroup's first task past the heavy list, as an index into the light list
   const int first_l = rank >= th ? rank - th : rank + (th - rank + G - 1) / G * G - th;
-  ring_list<GATEUP, 64>(p, p.mtiles, nl, first_l, G);
+  ring_list<GATEUP, 64, WNT>(p, p.mtiles, nl, first_l, G);
 }
 
-template <bool GATEUP>
+template <bool GATEUP, bool WNT>
 static hipError_t launch_ring_one(const GemmParams& p, int64_t max_tasks, int num_cus, hipStream_t s) {
   constexpr int lds = kRingLdsBytes;
   static int per_cu = 0;
   if (per_cu == 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_ring_kernel<GATEUP>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_ring_kernel<GATEUP, WNT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_ring_kernel<GATEUP>, kRingWaves * 64, lds) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_ring_kernel<GATEUP, WNT>, kRingWaves * 64, lds) !=
             hipSuccess ||
         occ <= 0)
       occ = 1;
@@ -490,14 +492,19 @@ static hipError_t launch_ring_one(const GemmParams& p, int64_t max_tasks, int nu
   }
   const int64_t grid = std::min<int64_t>(max_tasks, (int64_t)num_cus * per_cu);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_ring_kernel<GATEUP>), dim3((unsigned)grid), dim3(kRingWaves * 64), lds, s, p);
+  hipLaunchKernelGGL((gemm_ring_kernel<GATEUP, WNT>), dim3((unsigned)grid), dim3(kRingWaves * 64), lds, s, p);
   return hipGetLastError();
 }
 
 int ring_rows(bool heavy) { return heavy ? 128 : 64; }
 
-hipError_t launch_gemm_ring(bool gate_up, const GemmParams& p, int64_t max_tasks, int num_cus, hipStream_t s) {
-  return gate_up ? launch_ring_one<true>(p, max_tasks, num_cus, s) : launch_ring_one<false>(p, max_tasks, num_cus, s);
+hipError_t launch_gemm_ring(bool gate_up, bool stream_weights, const GemmParams& p, int64_t max_tasks, int num_cus,
+                            hipStream_t s) {
+  if (stream_weights)
+    return gate_up ? launch_ring_one<true, true>(p, max_tasks, num_cus, s)
+                   : launch_ring_one<false, true>(p, max_tasks, num_cus, s);
+  return gate_up ? launch_ring_one<true, false>(p, max_tasks, num_cus, s)
+                 : launch_ring_one<false, false>(p, max_tasks, num_cus, s);
 }
 
 }  // namespace afd

@@ -401,18 +401,19 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   const int64_t nmax = (int64_t)a->Tmax * K;
   // Light experts (rows <= bm_light, one m-tile) and heavier ones (and the
   // shared expert) go to two tile lists.  bf16: light experts stream their
-  // weights through registers (gemm.hip), heavy ones take the LDS-tiled GEMM
-  // (gemm_tiled.hip), which fetches each weight panel once per tile of
-  // tiled_rows() rows.  Block-FP8: both lists run the weight-ring GEMM
-  // (gemm_ring.hip), light tiles (<= 64 rows) and heavy tiles of
-  // ring_rows(true) rows.  fp32 uses light tiles of 32 rows only.
+  // weights through registers (gemm_stream.h), heavy ones take the LDS-tiled
+  // GEMM (gemm_tiled.hip), which fetches each weight panel once per tile of
+  // tiled_rows() rows; one mixed launch runs both, on disjoint CUs.
+  // Block-FP8: both lists run the weight-ring GEMM (gemm_ring.hip), light
+  // tiles (<= 64 rows) and heavy tiles of ring_rows(true) rows.  fp32 uses
+  // light tiles of 32 rows only.
   const int mr = dt == kF32 ? 1 : (n_flat <= 32ll * E ? 1 : 2);
   const int bm = 32 * mr;
   const bool fp8 = dt == kFP8;
   const int bm_heavy = dt == kF32 ? bm : fp8 ? ring_rows(true) : tiled_rows(dt);
   // bf16 batches of at most 16 rows per expert on average (decode) run the
-  // light list only: an expert that still gets more than bm rows takes several
-  // light tiles, which saves the two (nearly always empty) heavy launches
+  // light list only, on the streaming kernel alone (several workgroups per
+  // CU): an expert that still gets more than bm rows takes several light tiles
   const bool light_only = dt == kF32 || (dt == kBF16 && !a->S && n_flat <= 16ll * E);
   const int heavy_min = light_only ? 0x7fffffff : bm + 1;
   // CUs this call's persistent grids spread over: all of them, or an equal

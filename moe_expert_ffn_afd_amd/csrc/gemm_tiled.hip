@@ -199,24 +199,32 @@ __device__ __forceinline__ void tiled_body(const GemmParams& p, const int b, con
     auto compute = [&](const uint8_t* st) {
       const uint8_t* Bs = st + B_OFF;
       const uint8_t* As = st + A_OFF;
-      // slot t holds MFMAs j = JJ(t%SUB) + jj of its super-step
-#pragma unroll
-      for (int jj = 0; jj < JJ; ++jj) {
-        bf16x8 af[NA], bfr[NPW];
+      // slot t holds MFMAs j = JJ(t%SUB) + jj of its super-step; the
+      // fragments of sub-step jj + 1 are read before the products of jj, so
+      // their LDS latency hides behind those MFMAs
+      bf16x8 af[2][NA], bfr[2][NPW];
+      auto frags = [&](const int jj, const int b) {
 #pragma unroll
         for (int mr = 0; mr < NA; ++mr) {
           const int r = wm * WR + mr * 32 + (lane & 31);
           const int pi = SUB == 1 ? (lane >> 5) * 4 + jj : jj + 2 * (lane >> 5);
-          af[mr] = *reinterpret_cast<const bf16x8*>(As + r * RB + (pi ^ swz<RB>(r)) * 16);
+          af[b][mr] = *reinterpret_cast<const bf16x8*>(As + r * RB + (pi ^ swz<RB>(r)) * 16);
         }
 #pragma unroll
         for (int pp = 0; pp < NPW; ++pp)
-          bfr[pp] = *reinterpret_cast<const bf16x8*>(Bs + (wn * NPW + pp) * PB + jj * 1024 + lane * 16);
+          bfr[b][pp] = *reinterpret_cast<const bf16x8*>(Bs + (wn * NPW + pp) * PB + jj * 1024 + lane * 16);
+      };
+      frags(0, 0);
+#pragma unroll
+      for (int jj = 0; jj < JJ; ++jj) {
+        if (jj + 1 < JJ) frags(jj + 1, (jj + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mr = 0; mr < NA; ++mr)
 #pragma unroll
           for (int pp = 0; pp < NPW; ++pp)
-            acc[mr][pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[pp], af[mr], acc[mr][pp], 0, 0, 0);
+            acc[mr][pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jj & 1][pp], af[jj & 1][mr], acc[mr][pp], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
 

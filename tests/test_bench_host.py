@@ -42,3 +42,17 @@ def test_algorithmic_units_hand_counted():
     assert u["Ns"] == 5 + T and u["nonempty"] == 4
     w = 128 * 128 * (1 + 4.0 / (128 * 128))
     assert abs(u["gu_bytes"] - (4 * 2 * w + T * 128 * (1 + 4.0 / 128) + 8 * 128 * (1 + 4.0 / 128))) < 1e-6
+
+
+def test_roofline_kernel_labels_follow_the_tile_policy():
+    """The label bench.py puts on the roofline's kernel names the launch the
+    library makes for that batch: streaming kernel alone for decode-sized bf16
+    batches, the mixed heavy + light launch otherwise, the ring for block-FP8."""
+    b = _bench()
+    from moe_expert_ffn_afd_amd import inputs
+    assert "gemm_grouped_kernel<true, 1>" in b.gate_up_kernels(inputs.workload("decode"), 256)
+    assert "gemm_mixed_kernel<true, 2>" in b.gate_up_kernels(inputs.workload("aggregated"), 4096)
+    # 17-32 rows per expert on average: the mixed launch with 32-row light tiles
+    assert "gemm_mixed_kernel<true, 1>" in b.gate_up_kernels(inputs.workload("decode"), 512)
+    assert "gemm_ring_kernel<true>" in b.gate_up_kernels(inputs.workload("fp8_shared"), 2048)
+    assert "gemm_f32_kernel<true>" in b.gate_up_kernels(inputs.workload("tiny"), 64)

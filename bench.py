@@ -275,7 +275,8 @@ def main():
                    "routed_rows": units["N"],
                    "nonempty_experts": units["nonempty"] if mbs == 1 else [u["nonempty"] for u in per_mb],
                    "seed": args.seed},
-        "layer": {"tflops": round(units["layer_flops"] / (ms_per_step * 1e-3) / 1e12, 2),
+        "layer": {"assignments_per_s": round(units["N"] / (ms_per_step * 1e-3), 1),  # routed (token, expert) rows
+                  "tflops": round(units["layer_flops"] / (ms_per_step * 1e-3) / 1e12, 2),
                   "hbm_gbs": round(units["layer_bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
                   "roofline_frac": round(max(units["layer_flops"] / (PEAK_TFLOPS[dt] * 1e12),
                                              units["layer_bytes"] / (PEAK_HBM_GBS * 1e9)) /

@@ -126,7 +126,9 @@ afd_status afd_ffn_clone(const afd_ffn_t *src, afd_ffn_t **out_handle);
  * persistent grids resident: with streams = N each call's grids take 1/N of
  * the CUs, so concurrent calls (FastAFD System Design item 4: two ping-pong
  * microbatches) run side by side instead of one queueing behind the other's
- * resident workgroups.  Affects scheduling only, never results.  Returns
+ * resident workgroups; with streams > 1 the block-FP8 weight copies also
+ * stay cacheable, so microbatches reading the same experts at about the same
+ * time can share them.  Affects scheduling only, never results.  Returns
  * AFD_ERR_INVALID_ARG (handle unchanged) for a NULL handle or a value out of
  * range. */
 afd_status afd_ffn_set_concurrency(afd_ffn_t *handle, int32_t streams);

@@ -13,7 +13,11 @@ steps with every stage timed.
 
 Other modes: --copy-calibration runs a plain device copy of known size (the
 reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters);
---no-cpu-baseline skips the oracle timing.
+--no-cpu-baseline skips the oracle timing; --sweep times the layer at the
+workload's shape over a range of batch sizes T (the FFN-side time T_e as a
+function of the aggregated batch, the term the AFD performance model of
+"Revisiting Disaggregated Large Language Model Serving" balances against the
+attention side) and prints one JSON line per T.
 """
 from __future__ import annotations
 
@@ -51,7 +55,9 @@ def gate_up_kernels(cfg: dict, t_mb: int) -> str:
     if cfg["dtype"] == "f32":
         return "gate/up + SwiGLU stage: gemm_f32_kernel<true> (one launch)"
     if not cfg.get("shared_inter") and t_mb * cfg["K"] <= 16 * cfg["E"]:
-        return "gate/up + SwiGLU stage: gemm_grouped_kernel<true, 1> (every expert in 32-row tiles, one launch)"
+        return ("gate/up + SwiGLU stage: gemm_grouped_kernel<true, 1> (every expert in 32-row tiles) while "
+                "the largest expert has at most 64 rows, else gemm_mixed_kernel<true, 1>; the dispatch "
+                "chooses and the other launch returns at once")
     mr = 1 if t_mb * cfg["K"] <= 32 * cfg["E"] else 2
     return ("gate/up + SwiGLU stage: gemm_mixed_kernel<true, %d> (one launch: heavy tiles and light "
             "experts on disjoint CUs, side by side)" % mr)
@@ -106,6 +112,54 @@ def cpu_baseline(p: dict, cfg: dict, budget_s: float = 12.0) -> dict:
             "sample": "first %d of the %d tokens of the same seeded batch, fp64, %.1f s" % (total_n, T, total_t)}
 
 
+SWEEP_TOKENS = (64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384)
+
+
+def sweep(args) -> None:
+    """Layer time against the batch size at one workload's shape: one handle
+    sized for the largest T, one seeded batch of that size, and each T taking
+    its first T tokens (the routing's distribution does not change with T)."""
+    import torch
+
+    from moe_expert_ffn_afd_amd import afd, inputs
+
+    base = inputs.workload(args.workload)
+    if base.get("microbatches", 1) != 1:
+        sys.exit("--sweep takes a one-microbatch workload")
+    H, I, K = base["H"], base["I"], base["K"]
+    out_row = 4 if base["dtype"] == "f32" else 2
+    rows_per_token = K + (1 if base.get("shared_inter") else 0)
+    # down outputs [rows, H] stay within 32-bit buffer offsets
+    sizes = [t for t in SWEEP_TOKENS if t * rows_per_token * H * out_row < (1 << 31)]
+    cfg = dict(base, T=max(sizes))
+    p = inputs.make_problem(cfg, seed=args.seed, device="cuda")
+    layer = afd.Layer(p, max_tokens=cfg["T"])
+    ids_np = p["ids"].cpu().numpy()
+    stream = torch.cuda.current_stream()
+    for T in sizes:
+        q = inputs.slice_tokens(p, 0, T)
+        out = layer.out_like(T)
+        units = algorithmic_units(dict(cfg, T=T), ids_np[:T])
+        for _ in range(args.warmup):
+            layer.forward(q["hidden"], q["hidden_scales"], q["ids"], q["weights"], out=out, stream=stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            layer.forward(q["hidden"], q["hidden_scales"], q["ids"], q["weights"], out=out, stream=stream)
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / args.steps
+        dt = cfg["dtype"]
+        print(json.dumps({
+            "sweep": inputs.WORKLOAD_TITLES[args.workload], "T": T, "routed_rows": units["N"],
+            "nonempty_experts": units["nonempty"], "ms_per_step": round(sec * 1e3, 4),
+            "tokens_per_s": round(T / sec, 1), "hbm_gbs": round(units["layer_bytes"] / sec / 1e9, 1),
+            "tflops": round(units["layer_flops"] / sec / 1e12, 2),
+            "roofline_frac": round(max(units["layer_flops"] / (PEAK_TFLOPS[dt] * 1e12),
+                                       units["layer_bytes"] / (PEAK_HBM_GBS * 1e9)) / sec, 4),
+            "steps": args.steps, "warmup": args.warmup}), flush=True)
+    layer.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +170,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the layer at the workload's shape for T = 64 ... 16384 (one JSON line per T)")
     ap.add_argument("--serial", action="store_true",
                     help="microbatch workloads: run the microbatches one after the other on one stream, "
                          "each on every CU (the baseline the two-stream ping-pong is compared with)")
@@ -128,6 +184,9 @@ def main():
 
     import torch
 
+    if args.sweep:
+        sweep(args)
+        return
     if args.copy_calibration:
         n = 1 << 30
         src = torch.ones(n, dtype=torch.uint8, device="cuda")

@@ -29,8 +29,8 @@
 //  128-deep scale block and one panel lies inside one 128-column block.
 //
 //  Workspace (per handle, sized for max_tokens T_max; N_max = T_max * K):
-//    counts[E], offsets[E+1], err[1], num_mtiles[3] (light tiles, heavy tiles,
-//    light workgroups of a mixed bf16 launch; 16 bytes reserved)
+//    counts[E], offsets[E+1], err[1], num_mtiles[4] (light tiles, heavy tiles,
+//    light workgroups of a mixed bf16 launch, the launch the dispatch chose)
 //    chunk_base[n_chunks][E]          first sorted row of each (chunk, expert)
 //    sorted_assign[N_max], row_of[N_max]
 //    mtiles[max_mtiles] (int4) x 2    light and heavy lists {expert, first row, rows, 0}
@@ -83,10 +83,20 @@ struct DispatchParams {
   int32_t shared_row0;     // first shared row (N_max)
   int4* mtiles;            // light tile list
   int4* mtiles_heavy;      // heavy tile list
-  int32_t* num_mtiles;     // [3]: light tiles, heavy tiles, light workgroups of the mixed GEMM
+  int32_t* num_mtiles;     // [4]: light tiles, heavy tiles, light workgroups of the mixed
+                           //      GEMM, launch the dispatch chose (kLaunchLight / kLaunchMixed)
   int32_t fused;           // 1: count_scan also places the slots (n_flat <= kDispatchFuseSlots)
   int32_t mix_cus;         // > 0: workgroups of the mixed bf16 GEMM launches (one per CU)
+  int32_t auto_heavy_rows; // > 0: heavy experts only when some expert has at least this many
+                           //      rows (else every expert is light); 0: heavy_min_rows alone
 };
+
+// The launch the dispatch chose for a bf16 call whose routing the host cannot
+// see (num_mtiles[3]): the streaming GEMM over the light list alone, or the
+// mixed GEMM over both lists.  The host launches both kernels with gates; the
+// one not chosen returns at once.
+constexpr int32_t kLaunchLight = 1;
+constexpr int32_t kLaunchMixed = 2;
 
 // Cost of one heavy bf16 m-tile (tiled_rows() rows, both GEMMs) in units of
 // one light m-tile, each on one CU: a heavy tile's MFMA time against a light
@@ -103,7 +113,7 @@ constexpr float kHeavyTileCost = AFD_HEAVY_TILE_COST;
 
 struct GemmParams {
   const int4* mtiles;
-  const int32_t* num_mtiles;
+  const int32_t* num_mtiles;     // [0] tiles of mtiles; [3] the launch the dispatch chose
   const int4* mtiles2;           // block-FP8 ring GEMM: the heavy list, run before `mtiles`
   const int32_t* num_mtiles2;
   const int32_t* sorted_assign;  // row -> flat slot (gate/up gather)
@@ -127,6 +137,8 @@ struct GemmParams {
   int32_t k_steps;               // K / super-step
   int32_t n_groups;              // workgroup tasks per m-tile along N
   int32_t n_panels;              // panels of one output matrix (I/32 or H/32)
+  int32_t only_launch;           // 0: always run; kLaunchLight / kLaunchMixed: return at once
+                                 // unless the dispatch chose that launch (num_mtiles[3])
   uint8_t* c;                    // output rows
   int64_t c_row_bytes;
   float* c_scales;               // fp8 gate/up: h scales, step-major [I/128][c_scale_ld]

@@ -411,10 +411,16 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   const int bm = 32 * mr;
   const bool fp8 = dt == kFP8;
   const int bm_heavy = dt == kF32 ? bm : fp8 ? ring_rows(true) : tiled_rows(dt);
-  // bf16 batches of at most 16 rows per expert on average (decode) run the
-  // light list only, on the streaming kernel alone (several workgroups per
-  // CU): an expert that still gets more than bm rows takes several light tiles
-  const bool light_only = dt == kF32 || (dt == kBF16 && !a->S && n_flat <= 16ll * E);
+  // fp32 runs the light list only.  bf16 batches of at most 16 rows per
+  // expert on average (decode) usually do too, on the streaming kernel alone
+  // (several workgroups per CU), an expert with more than bm rows taking
+  // several light tiles; but skewed routing can put hundreds of rows on one
+  // expert of such a batch, and each of its light tiles would stream its
+  // weights again.  The host does not see the routing, so there the dispatch
+  // chooses: every expert light while the largest has at most 2*bm rows, else
+  // the mixed launch.  Both kernels are launched; the other returns at once.
+  const bool light_only = dt == kF32;
+  const bool auto_launch = dt == kBF16 && !a->S && n_flat <= 16ll * E;
   const int heavy_min = light_only ? 0x7fffffff : bm + 1;
   // CUs this call's persistent grids spread over: all of them, or an equal
   // share when the caller runs several forwards at once on other streams
@@ -440,7 +446,8 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   d.chunk_shift = chunk_shift_for(n_flat, E);
   d.n_chunks = (int32_t)((n_flat + (1ll << d.chunk_shift) - 1) >> d.chunk_shift);
   d.fused = n_flat <= kDispatchFuseSlots ? 1 : 0;
-  d.mix_cus = (dt == kBF16 && !light_only) ? cus : 0;
+  d.mix_cus = dt == kBF16 ? cus : 0;
+  d.auto_heavy_rows = auto_launch ? 2 * bm + 1 : 0;
   d.counts = a->counts;
   d.offsets = a->offsets;
   d.chunk_base = a->chunk_base;
@@ -584,8 +591,9 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
     dn_heavy.num_mtiles = a->num_mtiles + 1;
     dn_heavy.n_groups = (H / 32 + tiled_panels() - 1) / tiled_panels();  // bf16 only
 
-    // One launch per GEMM.  bf16: the light list alone (streaming kernel, several
-    // workgroups per CU) or, once heavy experts may occur, the mixed kernel:
+    // One launch per GEMM (two gated ones where the dispatch chooses).  bf16:
+    // the light list alone (streaming kernel, several workgroups per CU) or,
+    // once heavy experts occur, the mixed kernel:
     // one workgroup per CU, the dispatch's share of them streaming the light
     // list while the rest run the heavy tiles (HBM-bound and MFMA-bound work
     // side by side; a heavy workgroup leaves no room for a light one on its
@@ -598,7 +606,14 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
         both.num_mtiles2 = heavy.num_mtiles;
         return launch_gemm_ring(gate_up, a->concurrency == 1, both, (mt_bound + mth_bound) * light.n_groups, cus, s);
       }
-      if (light_only) return launch_gemm(dt, gate_up, mr, light, mt_bound * light.n_groups, cus, s);
+      if (auto_launch) {
+        GemmParams lo = light, mx = light;
+        lo.only_launch = kLaunchLight;
+        mx.only_launch = kLaunchMixed;
+        const hipError_t e = launch_gemm(dt, gate_up, mr, lo, mt_bound * light.n_groups, cus, s);
+        if (e != hipSuccess) return e;
+        return launch_gemm_mixed(gate_up, mr, heavy, mx, cus, s);
+      }
       return launch_gemm_mixed(gate_up, mr, heavy, light, cus, s);
     };
     AFD_HIP(stage(true, gu_light, gu_heavy));

@@ -129,12 +129,16 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
   __shared__ int excl[kMaxExperts];
   __shared__ int scan_tmp[32];
   __shared__ int bad;
+  __shared__ int max_rows;
   const int E = p.num_experts;
   const int tid = threadIdx.x;
   const int ncc = p.n_chunks * E;
 
   for (int i = tid; i < ncc; i += kDispatchThreads) cc[i] = 0;
-  if (tid == 0) bad = 0;
+  if (tid == 0) {
+    bad = 0;
+    max_rows = 0;
+  }
   __syncthreads();
 
   // 8 id loads in flight per thread, then their LDS increments
@@ -167,6 +171,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
       run += v;
     }
     total[e] = run;
+    atomicMax(&max_rows, run);
   }
   __syncthreads();
 
@@ -192,10 +197,15 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
 
   // m-tile lists: experts with at least heavy_min_rows rows go to the heavy
   // list (tiles of bm_heavy rows), the others to the light list (bm_light);
-  // routed experts in expert order, then the shared expert.
+  // routed experts in expert order, then the shared expert.  With
+  // auto_heavy_rows, a batch whose largest expert stays below it keeps every
+  // expert light (one launch of the streaming GEMM); a larger one takes the
+  // mixed launch.
   {
+    const bool mixed = p.auto_heavy_rows <= 0 || max_rows >= p.auto_heavy_rows;
+    const int heavy_min = mixed ? p.heavy_min_rows : 0x7fffffff;
     const int n = tid < E ? total[tid] : 0;
-    const bool heavy = n >= p.heavy_min_rows;
+    const bool heavy = n >= heavy_min;
     const int vl = heavy ? 0 : (n + p.bm_light - 1) / p.bm_light;
     const int vh = heavy ? (n + p.bm_heavy - 1) / p.bm_heavy : 0;
     int n_light = 0, n_heavy = 0;
@@ -211,7 +221,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
         p.mtiles_heavy[offh + j] = make_int4(tid, excl[tid] + r0, min(p.bm_heavy, n - r0), 0);
       }
     }
-    const bool sh_heavy = p.shared_rows >= p.heavy_min_rows;
+    const bool sh_heavy = p.shared_rows >= heavy_min;
     const int bms = sh_heavy ? p.bm_heavy : p.bm_light;
     const int n_shared = (p.shared_rows + bms - 1) / bms;
     int4* list = sh_heavy ? p.mtiles_heavy : p.mtiles;
@@ -225,6 +235,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
       p.num_mtiles[0] = nl;
       p.num_mtiles[1] = nh;
       p.num_mtiles[2] = mixed_light_workgroups(p.mix_cus, nl, nh);
+      p.num_mtiles[3] = mixed ? kLaunchMixed : kLaunchLight;
     }
   }
 

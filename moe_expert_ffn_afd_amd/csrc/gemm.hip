@@ -10,6 +10,7 @@ namespace afd {
 
 template <bool GATEUP, int MR>
 __global__ __launch_bounds__(256) void gemm_grouped_kernel(GemmParams p) {
+  if (p.only_launch && uniform(p.num_mtiles[3]) != p.only_launch) return;
   stream_body<GATEUP, MR, 1>(p, blockIdx.x, gridDim.x);
 }
 

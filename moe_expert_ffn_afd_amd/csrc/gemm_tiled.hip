@@ -304,6 +304,7 @@ template <bool GATEUP, int MR>
 __global__ __launch_bounds__(kNW * 64, 1) void gemm_mixed_kernel(GemmParams heavy, GemmParams light) {
   static_assert(kNW == 2 * kWaves, "the light role runs two 4-wave halves");
   static_assert(2 * kArowBytes<MR> <= kLds, "the light role's row slots fit the tiled ring");
+  if (light.only_launch && uniform(light.num_mtiles[3]) != light.only_launch) return;
   const int n = gridDim.x;
   const int L = min(max(uniform(light.num_mtiles[2]), 0), n);
   if ((int)blockIdx.x < L) {

@@ -50,7 +50,8 @@ def test_roofline_kernel_labels_follow_the_tile_policy():
     batches, the mixed heavy + light launch otherwise, the ring for block-FP8."""
     b = _bench()
     from moe_expert_ffn_afd_amd import inputs
-    assert "gemm_grouped_kernel<true, 1>" in b.gate_up_kernels(inputs.workload("decode"), 256)
+    decode = b.gate_up_kernels(inputs.workload("decode"), 256)
+    assert "gemm_grouped_kernel<true, 1>" in decode and "gemm_mixed_kernel<true, 1>" in decode
     assert "gemm_mixed_kernel<true, 2>" in b.gate_up_kernels(inputs.workload("aggregated"), 4096)
     # 17-32 rows per expert on average: the mixed launch with 32-row light tiles
     assert "gemm_mixed_kernel<true, 1>" in b.gate_up_kernels(inputs.workload("decode"), 512)

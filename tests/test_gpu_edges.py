@@ -130,6 +130,45 @@ def test_mixed_launch_role_split(case):
     layer.close()
 
 
+def skewed_ids(T, E, K, rows0):
+    """Expert 0 in slot 0 of the first rows0 tokens, every other slot spread
+    round-robin over experts 1..E-1: expert 0 gets exactly rows0 rows."""
+    f = np.arange(T)[:, None] * K + np.arange(K)[None, :]
+    ids = 1 + f % (E - 1)
+    ids[:rows0, 0] = 0
+    return ids.astype(np.int32)
+
+
+@pytest.mark.parametrize("case", ["uniform", "largest_64_rows", "largest_65_rows", "largest_128_rows",
+                                  "largest_128_rows_one_workgroup"])
+def test_small_batch_launch_chosen_on_device(case):
+    """bf16 batches of at most 16 rows per expert on average: the dispatch
+    keeps every expert light (streaming GEMM alone) while the largest expert
+    has at most 2 light tiles of rows (64), and takes the mixed launch beyond;
+    both gated kernels are launched and one returns at once.  Each side of
+    the boundary, and a grid of one workgroup."""
+    T, E, K = 128, 32, 4  # 512 slots = 16 per expert on average
+    rng = np.random.default_rng(13)
+    if case == "uniform":
+        c, routing = cfg("bf16", T=T, E=E, K=K), round_robin_ids(T, E, K)
+    else:
+        rows0 = int(case.split("_")[1])
+        c, routing = cfg("bf16", T=T, E=E, K=K), skewed_ids(T, E, K, rows0)
+    routing = (routing, rng.uniform(0.0, 1.0, size=routing.shape).astype(np.float32))
+    say("case", case)
+    p = problem(c, seed=14, routing=routing)
+    layer = afd.Layer(p)
+    if case.endswith("one_workgroup"):
+        layer.set_concurrency(torch.cuda.get_device_properties(0).multi_processor_count)
+    out = layer.forward(p["hidden"], p["hidden_scales"], p["ids"], p["weights"])
+    torch.cuda.synchronize()
+    want = check_dispatch(layer, p)
+    if case != "uniform":
+        assert want["counts"][0] == int(case.split("_")[1])
+    compare(out, oracle_out(to_host_problem(p)), "bf16", what=case)
+    layer.close()
+
+
 def test_unused_experts_poisoned_with_nan():
     T, E, K = 50, 8, 2
     rng = np.random.default_rng(4)

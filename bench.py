@@ -13,7 +13,8 @@ steps with every stage timed.
 
 Other modes: --copy-calibration runs a plain device copy of known size (the
 reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters);
---no-cpu-baseline skips the oracle timing; --sweep times the layer at the
+--no-cpu-baseline skips the oracle timing; --graph also times the step
+captured in a HIP graph and replayed; --sweep times the layer at the
 workload's shape over a range of batch sizes T (the FFN-side time T_e as a
 function of the aggregated batch, the term the AFD performance model of
 "Revisiting Disaggregated Large Language Model Serving" balances against the
@@ -170,6 +171,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph and replayed (graph_ms_per_step)")
     ap.add_argument("--sweep", action="store_true",
                     help="time the layer at the workload's shape for T = 64 ... 16384 (one JSON line per T)")
     ap.add_argument("--serial", action="store_true",
@@ -225,9 +228,9 @@ def main():
         streams = [torch.cuda.current_stream()] * mbs if serial else [torch.cuda.Stream() for _ in range(mbs)]
     outs = [layers[i].out_like(parts[i]["T"]) for i in range(mbs)]
 
-    main_stream = torch.cuda.current_stream()
-
     def step_fn():
+        # the caller's current stream: the default one, or a graph's capture stream
+        main_stream = torch.cuda.current_stream()
         if mbs == 1 or serial:  # one stream
             for i in range(mbs):
                 q = parts[i]
@@ -282,6 +285,29 @@ def main():
     per_launch = collect()
     for layer in layers:
         afd.afd_ffn_set_timing(layer.handle, False)
+
+    graph_ms = None
+    if args.graph:
+        # the same step captured once in a HIP graph (the microbatch streams
+        # fork from and join the capture stream) and replayed
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step_fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step_fn()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        del graph
 
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = T / (ms_per_step * 1e-3)
@@ -344,6 +370,8 @@ def main():
                   "stage_ms_steps": min(args.steps, STAGE_STEPS)},
         "roofline": roof,
     }
+    if graph_ms is not None:
+        result["graph_ms_per_step"] = round(graph_ms, 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p, cfg)
     print(json.dumps(result), flush=True)

@@ -77,6 +77,32 @@ def test_full_size_workload(name):
     layer.close()
 
 
+LARGEST = {
+    # the largest batches of the batch-size sweep: 131072 routed rows; with the
+    # shared expert the down outputs (147456 rows of 7168 bf16) sit just under
+    # the 2 GiB of 32-bit buffer offsets
+    "bf16_uniform_T16384": inputs.workload("decode", T=16384),
+    "bf16_zipf_T16384": inputs.workload("aggregated", T=16384),
+    "fp8_shared_T16384": inputs.workload("fp8_shared", T=16384),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LARGEST))
+def test_largest_batches(name):
+    cfg = LARGEST[name]
+    say("largest batch", name, cfg)
+    p = problem(cfg, 0)
+    layer, out = run_layer(p)
+    check_dispatch(layer, p)
+    T = cfg["T"]
+    # the first and last tokens (first and last rows of every list) and a random sample
+    rand = np.random.default_rng(321).choice(np.arange(2, T - 2), 6, replace=False)
+    tokens = np.unique(np.concatenate([[0, 1, T - 2, T - 1], rand]))
+    ref = oracle_out(to_host_problem(p), tokens)
+    compare(out, ref, cfg["dtype"], tokens=tokens, what=name)
+    layer.close()
+
+
 PING_PONG = {
     # the speculative-verify shard at full size (block-FP8 ring GEMMs)
     "verify_shard": inputs.workload("verify_shard"),

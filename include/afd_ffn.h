@@ -150,6 +150,11 @@ afd_status afd_ffn_set_concurrency(afd_ffn_t *handle, int32_t streams);
  * host).  Asynchronous on `stream`; inputs and out must stay valid until the
  * stream work completes.  The dispatch (counts, offsets, permutation) of this call
  * stays in the handle's workspace until the next forward on the handle.
+ * With timing off, a forward allocates nothing, waits for nothing and records
+ * no memset, so it may be captured into a HIP graph on `stream` and replayed;
+ * a replay recomputes everything from the captured pointers, and the handle's
+ * workspace is shared with any other forward on the handle (replays and eager
+ * calls on one handle must not overlap).
  */
 afd_status afd_ffn_forward(afd_ffn_t *handle, int32_t num_tokens, const void *hidden,
                            const float *hidden_scales, const int32_t *topk_ids,

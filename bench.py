@@ -55,10 +55,11 @@ def gate_up_kernels(cfg: dict, t_mb: int) -> str:
         return "gate/up + SwiGLU stage: gemm_ring_kernel<true> (heavy and light tiles in one launch)"
     if cfg["dtype"] == "f32":
         return "gate/up + SwiGLU stage: gemm_f32_kernel<true> (one launch)"
-    if not cfg.get("shared_inter") and t_mb * cfg["K"] <= 16 * cfg["E"]:
-        return ("gate/up + SwiGLU stage: gemm_grouped_kernel<true, 1> (every expert in 32-row tiles) while "
-                "the largest expert has at most 64 rows, else gemm_mixed_kernel<true, 1>; the dispatch "
-                "chooses and the other launch returns at once")
+    if not cfg.get("shared_inter") and t_mb * cfg["K"] <= 32 * cfg["E"]:
+        mr = 1 if t_mb * cfg["K"] <= 16 * cfg["E"] else 2
+        return ("gate/up + SwiGLU stage: gemm_grouped_kernel<true, %d> (every expert in %d-row tiles) while "
+                "the largest expert has at most %d rows, else gemm_mixed_kernel<true, 1>; the dispatch "
+                "chooses and the other launch returns at once" % (mr, 32 * mr, 64 * mr))
     mr = 1 if t_mb * cfg["K"] <= 32 * cfg["E"] else 2
     return ("gate/up + SwiGLU stage: gemm_mixed_kernel<true, %d> (one launch: heavy tiles and light "
             "experts on disjoint CUs, side by side)" % mr)

@@ -88,7 +88,9 @@ struct DispatchParams {
   int32_t fused;           // 1: count_scan also places the slots (n_flat <= kDispatchFuseSlots)
   int32_t mix_cus;         // > 0: workgroups of the mixed bf16 GEMM launches (one per CU)
   int32_t auto_heavy_rows; // > 0: heavy experts only when some expert has at least this many
-                           //      rows (else every expert is light); 0: heavy_min_rows alone
+                           //      rows; else every expert is light, in tiles of bm_light_only
+                           //      rows; 0: heavy_min_rows alone
+  int32_t bm_light_only;   // light tile rows when auto_heavy_rows keeps every expert light
 };
 
 // The launch the dispatch chose for a bf16 call whose routing the host cannot

@@ -416,12 +416,17 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   // (several workgroups per CU), an expert with more than bm rows taking
   // several light tiles; but skewed routing can put hundreds of rows on one
   // expert of such a batch, and each of its light tiles would stream its
-  // weights again.  The host does not see the routing, so there the dispatch
-  // chooses: every expert light while the largest has at most 2*bm rows, else
-  // the mixed launch.  Both kernels are launched; the other returns at once.
+  // weights again.  The host does not see the routing, so for batches of at
+  // most 32 rows per expert on average the dispatch chooses: every expert
+  // light while the largest has at most two light tiles of rows, else the
+  // mixed launch.  Both kernels are launched; the other returns at once.
   const bool light_only = dt == kF32;
-  const bool auto_launch = dt == kBF16 && !a->S && n_flat <= 16ll * E;
+  const bool auto_launch = dt == kBF16 && !a->S && n_flat <= 32ll * E;
   const int heavy_min = light_only ? 0x7fffffff : bm + 1;
+  // light tiles when the dispatch keeps every expert light: 32 rows up to 16
+  // rows per expert on average, else 64 (one tile for most experts of a
+  // uniform batch); the mixed launch keeps 32-row light tiles
+  const int mr_lo = n_flat <= 16ll * E ? 1 : 2;
   // CUs this call's persistent grids spread over: all of them, or an equal
   // share when the caller runs several forwards at once on other streams
   const int cus = std::max(1, a->num_cus / a->concurrency);
@@ -447,7 +452,8 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   d.n_chunks = (int32_t)((n_flat + (1ll << d.chunk_shift) - 1) >> d.chunk_shift);
   d.fused = n_flat <= kDispatchFuseSlots ? 1 : 0;
   d.mix_cus = dt == kBF16 ? cus : 0;
-  d.auto_heavy_rows = auto_launch ? 2 * bm + 1 : 0;
+  d.auto_heavy_rows = auto_launch ? 2 * 32 * mr_lo + 1 : 0;
+  d.bm_light_only = 32 * mr_lo;
   d.counts = a->counts;
   d.offsets = a->offsets;
   d.chunk_base = a->chunk_base;
@@ -610,7 +616,8 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
         GemmParams lo = light, mx = light;
         lo.only_launch = kLaunchLight;
         mx.only_launch = kLaunchMixed;
-        const hipError_t e = launch_gemm(dt, gate_up, mr, lo, mt_bound * light.n_groups, cus, s);
+        if (!gate_up) lo.n_groups = (H / 32 + down_panels_per_task(mr_lo) - 1) / down_panels_per_task(mr_lo);
+        const hipError_t e = launch_gemm(dt, gate_up, mr_lo, lo, mt_bound * lo.n_groups, cus, s);
         if (e != hipSuccess) return e;
         return launch_gemm_mixed(gate_up, mr, heavy, mx, cus, s);
       }

@@ -199,22 +199,23 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
   // list (tiles of bm_heavy rows), the others to the light list (bm_light);
   // routed experts in expert order, then the shared expert.  With
   // auto_heavy_rows, a batch whose largest expert stays below it keeps every
-  // expert light (one launch of the streaming GEMM); a larger one takes the
-  // mixed launch.
+  // expert light, in tiles of bm_light_only rows (one launch of the streaming
+  // GEMM); a larger one takes the mixed launch.
   {
     const bool mixed = p.auto_heavy_rows <= 0 || max_rows >= p.auto_heavy_rows;
     const int heavy_min = mixed ? p.heavy_min_rows : 0x7fffffff;
+    const int bm_light = mixed ? p.bm_light : p.bm_light_only;
     const int n = tid < E ? total[tid] : 0;
     const bool heavy = n >= heavy_min;
-    const int vl = heavy ? 0 : (n + p.bm_light - 1) / p.bm_light;
+    const int vl = heavy ? 0 : (n + bm_light - 1) / bm_light;
     const int vh = heavy ? (n + p.bm_heavy - 1) / p.bm_heavy : 0;
     int n_light = 0, n_heavy = 0;
     const int offl = block_exclusive_scan_1024(vl, scan_tmp, &n_light);
     const int offh = block_exclusive_scan_1024(vh, scan_tmp, &n_heavy);
     if (tid < E) {
       for (int j = 0; j < vl; ++j) {
-        const int r0 = j * p.bm_light;
-        p.mtiles[offl + j] = make_int4(tid, excl[tid] + r0, min(p.bm_light, n - r0), 0);
+        const int r0 = j * bm_light;
+        p.mtiles[offl + j] = make_int4(tid, excl[tid] + r0, min(bm_light, n - r0), 0);
       }
       for (int j = 0; j < vh; ++j) {
         const int r0 = j * p.bm_heavy;
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
       }
     }
     const bool sh_heavy = p.shared_rows >= heavy_min;
-    const int bms = sh_heavy ? p.bm_heavy : p.bm_light;
+    const int bms = sh_heavy ? p.bm_heavy : bm_light;
     const int n_shared = (p.shared_rows + bms - 1) / bms;
     int4* list = sh_heavy ? p.mtiles_heavy : p.mtiles;
     const int base = sh_heavy ? n_heavy : n_light;

@@ -53,7 +53,10 @@ def test_roofline_kernel_labels_follow_the_tile_policy():
     decode = b.gate_up_kernels(inputs.workload("decode"), 256)
     assert "gemm_grouped_kernel<true, 1>" in decode and "gemm_mixed_kernel<true, 1>" in decode
     assert "gemm_mixed_kernel<true, 2>" in b.gate_up_kernels(inputs.workload("aggregated"), 4096)
-    # 17-32 rows per expert on average: the mixed launch with 32-row light tiles
-    assert "gemm_mixed_kernel<true, 1>" in b.gate_up_kernels(inputs.workload("decode"), 512)
+    # 17-32 rows per expert on average: 64-row light tiles, or the mixed launch with 32-row ones
+    wider = b.gate_up_kernels(inputs.workload("decode"), 512)
+    assert "gemm_grouped_kernel<true, 2>" in wider and "gemm_mixed_kernel<true, 1>" in wider
+    # with a shared expert the mixed launch always runs
+    assert "gemm_mixed_kernel<true, 1>" in b.gate_up_kernels(dict(inputs.workload("decode"), shared_inter=1536), 512)
     assert "gemm_ring_kernel<true>" in b.gate_up_kernels(inputs.workload("fp8_shared"), 2048)
     assert "gemm_f32_kernel<true>" in b.gate_up_kernels(inputs.workload("tiny"), 64)

@@ -139,15 +139,19 @@ def skewed_ids(T, E, K, rows0):
     return ids.astype(np.int32)
 
 
-@pytest.mark.parametrize("case", ["uniform", "largest_64_rows", "largest_65_rows", "largest_128_rows",
-                                  "largest_128_rows_one_workgroup"])
-def test_small_batch_launch_chosen_on_device(case):
-    """bf16 batches of at most 16 rows per expert on average: the dispatch
-    keeps every expert light (streaming GEMM alone) while the largest expert
-    has at most 2 light tiles of rows (64), and takes the mixed launch beyond;
-    both gated kernels are launched and one returns at once.  Each side of
-    the boundary, and a grid of one workgroup."""
-    T, E, K = 128, 32, 4  # 512 slots = 16 per expert on average
+@pytest.mark.parametrize("T, case", [
+    (128, "uniform"), (128, "largest_64_rows"), (128, "largest_65_rows"), (128, "largest_128_rows"),
+    (128, "largest_128_rows_one_workgroup"),
+    (256, "uniform"), (256, "largest_128_rows"), (256, "largest_129_rows"), (256, "largest_200_rows_one_workgroup")])
+def test_small_batch_launch_chosen_on_device(T, case):
+    """bf16 batches of at most 32 rows per expert on average: the dispatch
+    keeps every expert light (streaming GEMM alone, 32-row tiles up to 16
+    rows per expert on average, else 64-row tiles) while the largest expert
+    has at most two light tiles of rows, and takes the mixed launch (32-row
+    light tiles) beyond; both gated kernels are launched and one returns at
+    once.  Each side of the boundary in both regimes (T=128: 16 rows per
+    expert on average, T=256: 32), and grids of one workgroup."""
+    E, K = 32, 4
     rng = np.random.default_rng(13)
     if case == "uniform":
         c, routing = cfg("bf16", T=T, E=E, K=K), round_robin_ids(T, E, K)

@@ -48,7 +48,7 @@ typedef struct afd_ffn afd_ffn_t; /* opaque handle */
 typedef enum {
     AFD_OK = 0,
     AFD_ERR_INVALID_ARG = 1,   /* NULL pointer, bad size, T > max_tokens ...   */
-    AFD_ERR_UNSUPPORTED = 2,   /* shape or dtype this build does not handle      */
+    AFD_ERR_UNSUPPORTED = 2,   /* shape or dtype the library does not handle     */
     AFD_ERR_OUT_OF_MEMORY = 3, /* device allocation failed in create / clone     */
     AFD_ERR_HIP = 4,           /* a HIP runtime call failed (message has it)     */
     AFD_ERR_BAD_ROUTING = 5    /* ids outside [-1, E) were seen (error query)    */

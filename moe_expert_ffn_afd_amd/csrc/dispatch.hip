@@ -80,9 +80,10 @@ __device__ inline int mixed_light_workgroups(int cus, int nl, int nh) {
 
 // Stable placement of the flat slots [f0, f_end) in rounds of 1024: cursor[e]
 // holds the next sorted row of expert e and advances round by round; wcnt is
-// [16][E] LDS, zero on entry and on return.  Every thread of the 1024-thread
+// [16][E] LDS, zero on entry and on return; ids[f] the id of slot f (the
+// caller's array, or a copy in LDS).  Every thread of the 1024-thread
 // workgroup calls it.
-__device__ void scatter_rounds(const DispatchParams& p, int f0, int f_end, int* cursor, int* wcnt) {
+__device__ void scatter_rounds(const DispatchParams& p, const int* ids, int f0, int f_end, int* cursor, int* wcnt) {
   const int E = p.num_experts;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -91,7 +92,7 @@ __device__ void scatter_rounds(const DispatchParams& p, int f0, int f_end, int* 
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int base = f0; base < f_end; base += kDispatchThreads) {
     const int f = base + tid;
-    const int e = f < f_end ? p.ids[f] : -1;
+    const int e = f < f_end ? ids[f] : -1;
     const bool valid = e >= 0 && e < E;
     uint64_t match = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
@@ -133,6 +134,8 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
   const int E = p.num_experts;
   const int tid = threadIdx.x;
   const int ncc = p.n_chunks * E;
+  // small batches keep their ids in LDS for the placement: [n_flat] after wcnt
+  int* ids_lds = cc + ncc + 16 * E;
 
   for (int i = tid; i < ncc; i += kDispatchThreads) cc[i] = 0;
   if (tid == 0) {
@@ -154,6 +157,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
     for (int u = 0; u < kU; ++u) {
       const int f = f0 + u * kDispatchThreads + tid;
       const int e = ev[u];
+      if (p.fused && f < p.n_flat) ids_lds[f] = e;
       if (e >= 0 && e < E)
         atomicAdd(&cc[(f >> p.chunk_shift) * E + e], 1);
       else if (e != -1)
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
     __syncthreads();  // every read of total[] above is done: it becomes the cursors
     for (int e = tid; e < E; e += kDispatchThreads) total[e] = excl[e];
     __syncthreads();
-    scatter_rounds(p, 0, p.n_flat, total, wcnt);
+    scatter_rounds(p, ids_lds, 0, p.n_flat, total, wcnt);
   }
 }
 
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_scatter_kernel(Disp
   for (int e = tid; e < E; e += kDispatchThreads) cursor[e] = p.chunk_base[chunk * E + e];
   for (int i = tid; i < 16 * E; i += kDispatchThreads) wcnt[i] = 0;
   __syncthreads();
-  scatter_rounds(p, f0, f_end, cursor, wcnt);
+  scatter_rounds(p, p.ids, f0, f_end, cursor, wcnt);
 }
 
 // Block-FP8 only: the caller's 1x128 activation scales [T][H/128], gathered
@@ -299,7 +303,9 @@ hipError_t launch_gather_scales(const ScaleGatherParams& p, hipStream_t s) {
 }
 
 hipError_t launch_dispatch_count_scan(const DispatchParams& p, hipStream_t s) {
-  size_t lds = sizeof(int) * ((size_t)p.n_chunks + (p.fused ? 16 : 0)) * p.num_experts;
+  // counters; with the placement fused: per-wave counts and the ids too
+  // (at most 4 * 512 + 16 * 512 + 4096 ints = 56 KiB)
+  size_t lds = sizeof(int) * ((size_t)p.n_chunks * p.num_experts + (p.fused ? 16 * (size_t)p.num_experts + p.n_flat : 0));
   hipLaunchKernelGGL(dispatch_count_scan_kernel, dim3(1), dim3(kDispatchThreads), lds, s, p);
   return hipGetLastError();
 }

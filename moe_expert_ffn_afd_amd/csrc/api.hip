@@ -411,15 +411,15 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   const int bm = 32 * mr;
   const bool fp8 = dt == kFP8;
   const int bm_heavy = dt == kF32 ? bm : fp8 ? ring_rows(true) : tiled_rows(dt);
-  // fp32 runs the light list only.  bf16 batches of at most 16 rows per
-  // expert on average (decode) usually do too, on the streaming kernel alone
-  // (several workgroups per CU), an expert with more than bm rows taking
-  // several light tiles; but skewed routing can put hundreds of rows on one
-  // expert of such a batch, and each of its light tiles would stream its
-  // weights again.  The host does not see the routing, so for batches of at
-  // most 32 rows per expert on average the dispatch chooses: every expert
-  // light while the largest has at most two light tiles of rows, else the
-  // mixed launch.  Both kernels are launched; the other returns at once.
+  // fp32 runs the light list only.  bf16 batches (no shared expert) of at
+  // most 32 rows per expert on average usually need no heavy list either:
+  // the streaming kernel runs alone (several workgroups per CU) over light
+  // tiles of 32 * mr_lo rows.  But skewed routing can put hundreds of rows on
+  // one expert of such a batch, and each of its light tiles would stream its
+  // weights again.  The host does not see the routing, so the dispatch
+  // chooses: every expert light while the largest has at most two light
+  // tiles of rows, else the mixed launch.  Both kernels are launched; the
+  // other returns at once.
   const bool light_only = dt == kF32;
   const bool auto_launch = dt == kBF16 && !a->S && n_flat <= 32ll * E;
   const int heavy_min = light_only ? 0x7fffffff : bm + 1;

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from gpu_util import compare, oracle_out, problem, say, to_host_problem
-from moe_expert_ffn_afd_amd import afd
+from moe_expert_ffn_afd_amd import afd, inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -63,3 +63,51 @@ def test_graph_replays_match_eager(name):
         assert torch.equal(out, eager), "replay %d differs from the eager forward" % r
     del graph
     layer.close()
+
+
+def test_graph_of_two_stream_ping_pong():
+    """Two microbatches on two streams (a handle and its clone), forked from
+    and joined to the capture stream inside one graph: every replay equals
+    the eager two-stream result bit for bit."""
+    c = cfg("fp8", 256, 512, 256, 8, 4, routing="uniform")
+    p = problem(c, 31)
+    half = c["T"] // 2
+    parts = [inputs.slice_tokens(p, i * half, (i + 1) * half) for i in range(2)]
+    layers = [afd.Layer(p, max_tokens=half)]
+    layers.append(layers[0].clone())
+    for layer in layers:
+        layer.set_concurrency(2)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+
+    def step(outs):
+        main = torch.cuda.current_stream()
+        for i in range(2):
+            streams[i].wait_stream(main)
+            with torch.cuda.stream(streams[i]):
+                fwd(layers[i], parts[i], outs[i])
+        for i in range(2):
+            main.wait_stream(streams[i])
+
+    eager = [layers[i].out_like(half) for i in range(2)]
+    step(eager)
+    torch.cuda.synchronize()
+    ref = oracle_out(to_host_problem(p))
+    compare(torch.cat(eager), ref, "fp8", what="two-stream eager")
+
+    outs = [layers[i].out_like(half) for i in range(2)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(outs)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say("two-stream replay", r)
+        for i in range(2):
+            assert torch.equal(outs[i], eager[i]), "replay %d, microbatch %d differs" % (r, i)
+    del graph
+    for layer in layers[::-1]:
+        layer.close()

@@ -78,23 +78,33 @@ int esize_of(int dtype) { return dtype == kF32 ? 4 : dtype == kBF16 ? 2 : 1; }
 
 }  // namespace
 
-struct afd_ffn {
-  int H = 0, I = 0, E = 0, K = 0, Tmax = 0, S = 0, dtype = 0, device = 0;
-  int num_cus = 256;
-  int concurrency = 1;  // forwards the caller runs at once on other streams (afd_ffn_set_concurrency)
-  WeightStore* w = nullptr;
-  // workspace
-  uint8_t* ws = nullptr;
+namespace {
+
+// Per-forward device buffers (section "Workspace" of afd_internal.h), carved
+// out of one allocation for a token capacity `tcap`.
+struct Workspace {
   int32_t *counts = nullptr, *offsets = nullptr, *err = nullptr, *num_mtiles = nullptr;
   int32_t *chunk_base = nullptr, *sorted_assign = nullptr, *row_of = nullptr;
   int4* mtiles = nullptr;
   int4* mtiles_heavy = nullptr;
   uint8_t* h = nullptr;
-  float* h_scales = nullptr;   // FP8: [I/128][h_rows] step-major
-  float* x_scales = nullptr;   // FP8: [H/128][h_rows] hidden scales in sorted-row order
-  int64_t h_rows = 0;
+  float* h_scales = nullptr;  // FP8: [I/128][h_rows] step-major
+  float* x_scales = nullptr;  // FP8: [H/128][h_rows] hidden scales in sorted-row order
   uint8_t* y = nullptr;
-  int max_chunks = 0, max_mtiles = 0;
+  int64_t nmax = 0;    // routed-row capacity tcap * K; the shared expert's rows start here
+  int64_t h_rows = 0;  // rows of h and y: nmax (+ tcap with a shared expert)
+  int tcap = 0;
+};
+
+}  // namespace
+
+struct afd_ffn {
+  int H = 0, I = 0, E = 0, K = 0, Tmax = 0, S = 0, dtype = 0, device = 0;
+  int num_cus = 256;
+  int concurrency = 1;  // forwards the caller runs at once on other streams (afd_ffn_set_concurrency)
+  WeightStore* w = nullptr;
+  uint8_t* ws_mem = nullptr;  // the handle's workspace allocation (sized for Tmax)
+  Workspace ws;
   int last_T = 0;
   // per-stage timing: bit s of the mask times stage s (boundaries s and s + 1)
   uint32_t timing_mask = 0;
@@ -161,41 +171,53 @@ afd_status check_config(const afd_ffn_config* c) {
   return AFD_OK;
 }
 
-afd_status alloc_workspace(afd_ffn* a) {
-  const int64_t nmax = (int64_t)a->Tmax * a->K;
-  const int64_t rows = nmax + (a->S ? a->Tmax : 0);
-  a->max_chunks = (int)((nmax + 1023) / 1024);
-  a->max_mtiles = (int)(nmax / 32 + a->E + (a->S ? (a->Tmax + 31) / 32 : 0) + 1);
+// Lay the workspace of a token capacity `tcap` out from `base` (which may be
+// null: sizes only) and return its size in bytes.
+int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w) {
+  const int64_t nmax = (int64_t)tcap * a->K;
+  const int64_t rows = nmax + (a->S ? tcap : 0);
+  const int64_t max_chunks = (nmax + 1023) / 1024;
+  const int64_t max_mtiles = nmax / 32 + a->E + (a->S ? (tcap + 31) / 32 : 0) + 1;
   const int es = esize_of(a->dtype);
   const int ys = a->dtype == kF32 ? 4 : 2;
   int64_t off = 0;
   auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + bytes, 256); return o; };
   const int64_t o_counts = take(4ll * a->E), o_offsets = take(4ll * (a->E + 1)), o_err = take(4),
-                o_nmt = take(16), o_cb = take(4ll * a->max_chunks * a->E), o_sa = take(4 * nmax),
-                o_ro = take(4 * nmax), o_mt = take(16ll * a->max_mtiles), o_mth = take(16ll * a->max_mtiles),
+                o_nmt = take(16), o_cb = take(4ll * max_chunks * a->E), o_sa = take(4 * nmax),
+                o_ro = take(4 * nmax), o_mt = take(16ll * max_mtiles), o_mth = take(16ll * max_mtiles),
                 o_h = take(rows * a->I * es),
                 o_hs = take(a->dtype == kFP8 ? rows * (a->I / 128) * 4 : 0),
                 o_xs = take(a->dtype == kFP8 ? rows * (a->H / 128) * 4 : 0), o_y = take(rows * a->H * ys);
-  if (hipMalloc((void**)&a->ws, off) != hipSuccess) {
-    (void)hipGetLastError();
-    a->ws = nullptr;
-    return fail(AFD_ERR_OUT_OF_MEMORY, "workspace of %lld bytes", (long long)off);
+  if (base && w) {
+    w->counts = (int32_t*)(base + o_counts);
+    w->offsets = (int32_t*)(base + o_offsets);
+    w->err = (int32_t*)(base + o_err);
+    w->num_mtiles = (int32_t*)(base + o_nmt);
+    w->chunk_base = (int32_t*)(base + o_cb);
+    w->sorted_assign = (int32_t*)(base + o_sa);
+    w->row_of = (int32_t*)(base + o_ro);
+    w->mtiles = (int4*)(base + o_mt);
+    w->mtiles_heavy = (int4*)(base + o_mth);
+    w->h = base + o_h;
+    w->h_scales = a->dtype == kFP8 ? (float*)(base + o_hs) : nullptr;
+    w->x_scales = a->dtype == kFP8 ? (float*)(base + o_xs) : nullptr;
+    w->y = base + o_y;
+    w->nmax = nmax;
+    w->h_rows = rows;
+    w->tcap = tcap;
   }
-  a->counts = (int32_t*)(a->ws + o_counts);
-  a->offsets = (int32_t*)(a->ws + o_offsets);
-  a->err = (int32_t*)(a->ws + o_err);
-  a->num_mtiles = (int32_t*)(a->ws + o_nmt);
-  a->chunk_base = (int32_t*)(a->ws + o_cb);
-  a->sorted_assign = (int32_t*)(a->ws + o_sa);
-  a->row_of = (int32_t*)(a->ws + o_ro);
-  a->mtiles = (int4*)(a->ws + o_mt);
-  a->mtiles_heavy = (int4*)(a->ws + o_mth);
-  a->h = a->ws + o_h;
-  a->h_scales = a->dtype == kFP8 ? (float*)(a->ws + o_hs) : nullptr;
-  a->x_scales = a->dtype == kFP8 ? (float*)(a->ws + o_xs) : nullptr;
-  a->h_rows = rows;
-  a->y = a->ws + o_y;
-  AFD_HIP(hipMemset(a->ws, 0, off));
+  return off;
+}
+
+afd_status alloc_workspace(afd_ffn* a) {
+  const int64_t bytes = layout_workspace(a, a->Tmax, nullptr, nullptr);
+  if (hipMalloc((void**)&a->ws_mem, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    a->ws_mem = nullptr;
+    return fail(AFD_ERR_OUT_OF_MEMORY, "workspace of %lld bytes", (long long)bytes);
+  }
+  layout_workspace(a, a->Tmax, a->ws_mem, &a->ws);
+  AFD_HIP(hipMemset(a->ws_mem, 0, bytes));
   return AFD_OK;
 }
 
@@ -265,7 +287,7 @@ void free_handle(afd_ffn* a) {
     for (hipEvent_t e : v)
       if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : a->ev_free) (void)hipEventDestroy(e);
-  if (a->ws) (void)hipFree(a->ws);
+  if (a->ws_mem) (void)hipFree(a->ws_mem);
   if (a->w && a->w->refs.fetch_sub(1) == 1) delete a->w;
   delete a;
 }
@@ -279,6 +301,281 @@ hipEvent_t take_event(afd_ffn* a) {
   hipEvent_t e = nullptr;
   if (hipEventCreate(&e) != hipSuccess) return nullptr;
   return e;
+}
+
+// Host checks of a forward's arguments (T at most `tcap`).
+afd_status check_forward_args(const afd_ffn* a, int32_t T, int64_t tcap, const void* hidden,
+                              const float* hidden_scales, const int32_t* topk_ids, const float* topk_weights,
+                              const void* out) {
+  if (!a) return fail(AFD_ERR_INVALID_ARG, "handle is NULL");
+  if (T < 0 || T > tcap) return fail(AFD_ERR_INVALID_ARG, "num_tokens %d outside [0, %lld]", T, (long long)tcap);
+  if (T > 0 && (!hidden || !topk_ids || !topk_weights || !out))
+    return fail(AFD_ERR_INVALID_ARG, "hidden, topk_ids, topk_weights and out must be non-NULL");
+  if (a->dtype == kFP8 && T > 0 && !hidden_scales)
+    return fail(AFD_ERR_INVALID_ARG, "block-FP8 input needs hidden_scales");
+  if (a->dtype != kFP8 && hidden_scales)
+    return fail(AFD_ERR_INVALID_ARG, "hidden_scales is only used with AFD_DTYPE_FP8_BLOCK");
+  auto mis = [](const void* q, uintptr_t al) { return q && (reinterpret_cast<uintptr_t>(q) & (al - 1)); };
+  if (mis(hidden, 16) || mis(out, 16)) return fail(AFD_ERR_INVALID_ARG, "hidden and out must be 16-byte aligned");
+  if (mis(hidden_scales, 4) || mis(topk_ids, 4) || mis(topk_weights, 4))
+    return fail(AFD_ERR_INVALID_ARG, "hidden_scales, topk_ids and topk_weights must be 4-byte aligned");
+  return AFD_OK;
+}
+
+// Enqueue one forward on `stream` with the buffers of `w` (capacity w.tcap >= T).
+// `timed`: record the handle's timing events (the handle's own workspace only).
+afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, int32_t T, const void* hidden,
+                        const float* hidden_scales, const int32_t* topk_ids, const float* topk_weights, void* out,
+                        void* stream) {
+  DeviceGuard dg(a->device);
+  if (!dg.ok) return fail(AFD_ERR_HIP, "cannot select device %d", a->device);
+  hipStream_t s = (hipStream_t)stream;
+
+  const int E = a->E, K = a->K, H = a->H, I = a->I, dt = a->dtype;
+  const int64_t n_flat = (int64_t)T * K;
+  const int64_t nmax = w.nmax;
+  // Light experts (rows <= bm_light, one m-tile) and heavier ones (and the
+  // shared expert) go to two tile lists.  bf16: light experts stream their
+  // weights through registers (gemm_stream.h), heavy ones take the LDS-tiled
+  // GEMM (gemm_tiled.hip), which fetches each weight panel once per tile of
+  // tiled_rows() rows; one mixed launch runs both, on disjoint CUs.
+  // Block-FP8: both lists run the weight-ring GEMM (gemm_ring.hip), light
+  // tiles (<= 64 rows) and heavy tiles of ring_rows(true) rows.  fp32 uses
+  // light tiles of 32 rows only.
+  const int mr = dt == kF32 ? 1 : (n_flat <= 32ll * E ? 1 : 2);
+  const int bm = 32 * mr;
+  const bool fp8 = dt == kFP8;
+  const int bm_heavy = dt == kF32 ? bm : fp8 ? ring_rows(true) : tiled_rows(dt);
+  // fp32 runs the light list only.  bf16 batches (no shared expert) of at
+  // most 32 rows per expert on average usually need no heavy list either:
+  // the streaming kernel runs alone (several workgroups per CU) over light
+  // tiles of 32 * mr_lo rows.  But skewed routing can put hundreds of rows on
+  // one expert of such a batch, and each of its light tiles would stream its
+  // weights again.  The host does not see the routing, so the dispatch
+  // chooses: every expert light while the largest has at most two light
+  // tiles of rows, else the mixed launch.  Both kernels are launched; the
+  // other returns at once.
+  const bool light_only = dt == kF32;
+  const bool auto_launch = dt == kBF16 && !a->S && n_flat <= 32ll * E;
+  const int heavy_min = light_only ? 0x7fffffff : bm + 1;
+  // light tiles when the dispatch keeps every expert light: 32 rows up to 16
+  // rows per expert on average, else 64 (one tile for most experts of a
+  // uniform batch); the mixed launch keeps 32-row light tiles
+  const int mr_lo = n_flat <= 16ll * E ? 1 : 2;
+  // CUs this call's persistent grids spread over: all of them, or an equal
+  // share when the caller runs several forwards at once on other streams
+  const int cus = std::max(1, a->num_cus / a->concurrency);
+  // boundary b lies before stage b (b = AFD_NUM_STAGES: after the last)
+  std::array<hipEvent_t, AFD_NUM_STAGES + 1> ev{};
+  const uint32_t tmask = timed ? a->timing_mask : 0u;
+  auto mark = [&](int b) -> afd_status {
+    const bool need = ((tmask >> b) & 1u) || (b > 0 && ((tmask >> (b - 1)) & 1u));
+    if (!need) return AFD_OK;
+    hipEvent_t e = take_event(a);
+    if (!e) return fail(AFD_ERR_HIP, "hipEventCreate failed");
+    AFD_HIP(hipEventRecord(e, s));
+    ev[b] = e;
+    return AFD_OK;
+  };
+  afd_status st;
+
+  DispatchParams d{};
+  d.ids = topk_ids;
+  d.n_flat = (int32_t)n_flat;
+  d.num_experts = E;
+  d.chunk_shift = chunk_shift_for(n_flat, E);
+  d.n_chunks = (int32_t)((n_flat + (1ll << d.chunk_shift) - 1) >> d.chunk_shift);
+  d.fused = n_flat <= kDispatchFuseSlots ? 1 : 0;
+  d.mix_cus = dt == kBF16 ? cus : 0;
+  d.auto_heavy_rows = auto_launch ? 2 * 32 * mr_lo + 1 : 0;
+  d.bm_light_only = 32 * mr_lo;
+  d.counts = w.counts;
+  d.offsets = w.offsets;
+  d.chunk_base = w.chunk_base;
+  d.err = w.err;
+  d.sorted_assign = w.sorted_assign;
+  d.row_of = w.row_of;
+  d.bm_light = bm;
+  d.bm_heavy = bm_heavy;
+  d.heavy_min_rows = heavy_min;
+  d.shared_rows = a->S ? T : 0;
+  d.shared_row0 = (int32_t)nmax;
+  d.mtiles = w.mtiles;
+  d.mtiles_heavy = w.mtiles_heavy;
+  d.num_mtiles = w.num_mtiles;
+
+  if ((st = mark(0))) return st;
+  AFD_HIP(launch_dispatch_count_scan(d, s));
+  if ((st = mark(1))) return st;
+  if (T == 0) {
+    // nothing else to do (the later stages count as not timed)
+    if (tmask) a->ev_pending.push_back(ev);
+    return AFD_OK;
+  }
+  AFD_HIP(launch_dispatch_scatter(d, s));
+  if (dt == kFP8) {
+    ScaleGatherParams sg{};
+    sg.src = hidden_scales;
+    sg.ks = H / 128;
+    sg.tokens = T;
+    sg.top_k = K;
+    sg.sorted_assign = w.sorted_assign;
+    sg.offsets = w.offsets;
+    sg.num_experts = E;
+    sg.routed_max = (int32_t)n_flat;
+    sg.shared_row0 = a->S ? (int32_t)nmax : -1;
+    sg.dst = w.x_scales;
+    sg.ld = (int32_t)w.h_rows;
+    AFD_HIP(launch_gather_scales(sg, s));
+  }
+  if ((st = mark(2))) return st;
+
+  // upper bounds of the routed + shared m-tiles of this call, per list
+  const int64_t mt_bound = n_flat / bm + std::min<int64_t>(E, n_flat) + (a->S ? (T + bm - 1) / bm : 0) + 1;
+  const int64_t mth_bound = light_only ? 0 : n_flat / heavy_min + (a->S ? (T + bm_heavy - 1) / bm_heavy : 0) + 1;
+  const int64_t rows_ld_h = (int64_t)I * esize_of(dt);
+  const int64_t h_rows = w.h_rows;
+  const int occupancy_wgs = 4;  // resident workgroups per CU the persistent grids aim for
+
+  if (dt == kF32) {
+    F32Params g{};
+    g.mtiles = w.mtiles;
+    g.num_mtiles = w.num_mtiles;
+    g.sorted_assign = w.sorted_assign;
+    g.top_k = K;
+    g.shared_row0 = (int32_t)nmax;
+    g.gather = 1;
+    g.a = (const float*)hidden;
+    g.w0 = (const float*)a->w->gu;
+    g.w1 = (const float*)a->w->up;
+    g.kdim = H;
+    g.ndim = I;
+    g.c = (float*)w.h;
+    int grid = (int)std::min<int64_t>(mt_bound * ((I + 63) / 64), (int64_t)cus * occupancy_wgs);
+    AFD_HIP(launch_gemm_f32(true, g, grid, s));
+    if ((st = mark(3))) return st;
+    g.gather = 0;
+    g.a = (const float*)w.h;
+    g.w0 = (const float*)a->w->dn;
+    g.w1 = nullptr;
+    g.kdim = I;
+    g.ndim = H;
+    g.c = (float*)w.y;
+    grid = (int)std::min<int64_t>(mt_bound * ((H + 63) / 64), (int64_t)cus * occupancy_wgs);
+    AFD_HIP(launch_gemm_f32(false, g, grid, s));
+    if ((st = mark(4))) return st;
+  } else {
+    const int es = esize_of(dt);
+    GemmParams g{};
+    g.mtiles = w.mtiles;
+    g.num_mtiles = w.num_mtiles;
+    g.sorted_assign = w.sorted_assign;
+    g.top_k = K;
+    g.shared_row0 = (int32_t)nmax;
+    // gate/up: A = hidden rows gathered by token
+    g.gather = 1;
+    g.a = (const uint8_t*)hidden;
+    g.a_bytes = (int64_t)T * H * es;
+    g.a_row_bytes = (int64_t)H * es;
+    g.a_scales = w.x_scales;  // gathered by gather_scales_kernel
+    g.a_scale_bytes = fp8 ? (int64_t)(H / 128) * w.h_rows * 4 : 0;
+    g.a_scale_ld = (int32_t)w.h_rows;
+    g.b = a->w->gu;
+    g.b_expert_bytes = a->w->gu_expert_bytes;
+    g.b_panel_bytes = a->w->gu_panel_bytes;
+    g.b_scales0 = a->w->sg;
+    g.b_scale_bytes = a->w->scale_bytes;
+    g.b_scales1 = a->w->su;
+    g.b_scale_rows = H / 128;
+    g.b_scale_cols = I / 128;
+    g.k_steps = (int32_t)((int64_t)H * es / kStepBytes);
+    g.n_panels = I / 32;
+    g.n_groups = I / 128;
+    g.c = w.h;
+    g.c_row_bytes = rows_ld_h;
+    g.c_scales = w.h_scales;
+    g.c_scale_ld = (int32_t)w.h_rows;
+    GemmParams gu_light = g;
+    GemmParams gu_heavy = g;
+    gu_heavy.mtiles = w.mtiles_heavy;
+    gu_heavy.num_mtiles = w.num_mtiles + 1;
+    gu_heavy.n_groups = (2 * I / 32 + tiled_panels() - 1) / tiled_panels();  // bf16 only
+    // down: A = h rows in sorted order
+    g.gather = 0;
+    g.a = w.h;
+    g.a_bytes = h_rows * rows_ld_h;
+    g.a_row_bytes = rows_ld_h;
+    g.a_scales = w.h_scales;
+    g.a_scale_bytes = fp8 ? h_rows * (I / 128) * 4 : 0;
+    g.a_scale_ld = (int32_t)w.h_rows;
+    g.b = a->w->dn;
+    g.b_expert_bytes = a->w->dn_expert_bytes;
+    g.b_panel_bytes = a->w->dn_panel_bytes;
+    g.b_scales0 = a->w->sd;
+    g.b_scales1 = a->w->sd;
+    g.b_scale_rows = I / 128;
+    g.b_scale_cols = H / 128;
+    g.k_steps = (int32_t)((int64_t)I * es / kStepBytes);
+    g.n_panels = H / 32;
+    // light tasks of the down GEMM: down_panels_per_task(mr) H panels (bf16
+    // streaming GEMM) or 8 (block-FP8 ring GEMM, both lists)
+    const int dn_panels = fp8 ? 8 : down_panels_per_task(mr);
+    g.n_groups = (H / 32 + dn_panels - 1) / dn_panels;
+    g.c = w.y;
+    g.c_row_bytes = (int64_t)H * 2;
+    g.c_scales = nullptr;
+    g.c_scale_ld = 0;
+    GemmParams dn_light = g;
+    GemmParams dn_heavy = g;
+    dn_heavy.mtiles = w.mtiles_heavy;
+    dn_heavy.num_mtiles = w.num_mtiles + 1;
+    dn_heavy.n_groups = (H / 32 + tiled_panels() - 1) / tiled_panels();  // bf16 only
+
+    // One launch per GEMM (two gated ones where the dispatch chooses).  bf16:
+    // the light list alone (streaming kernel, several workgroups per CU) or,
+    // once heavy experts occur, the mixed kernel:
+    // one workgroup per CU, the dispatch's share of them streaming the light
+    // list while the rest run the heavy tiles (HBM-bound and MFMA-bound work
+    // side by side; a heavy workgroup leaves no room for a light one on its
+    // CU, so the split is by CU).  Block-FP8 runs both lists in one launch of
+    // the ring GEMM.
+    auto stage = [&](bool gate_up, const GemmParams& light, const GemmParams& heavy) -> hipError_t {
+      if (fp8) {
+        GemmParams both = light;
+        both.mtiles2 = heavy.mtiles;
+        both.num_mtiles2 = heavy.num_mtiles;
+        return launch_gemm_ring(gate_up, a->concurrency == 1, both, (mt_bound + mth_bound) * light.n_groups, cus, s);
+      }
+      if (auto_launch) {
+        GemmParams lo = light, mx = light;
+        lo.only_launch = kLaunchLight;
+        mx.only_launch = kLaunchMixed;
+        if (!gate_up) lo.n_groups = (H / 32 + down_panels_per_task(mr_lo) - 1) / down_panels_per_task(mr_lo);
+        const hipError_t e = launch_gemm(dt, gate_up, mr_lo, lo, mt_bound * lo.n_groups, cus, s);
+        if (e != hipSuccess) return e;
+        return launch_gemm_mixed(gate_up, mr, heavy, mx, cus, s);
+      }
+      return launch_gemm_mixed(gate_up, mr, heavy, light, cus, s);
+    };
+    AFD_HIP(stage(true, gu_light, gu_heavy));
+    if ((st = mark(3))) return st;
+    AFD_HIP(stage(false, dn_light, dn_heavy));
+    if ((st = mark(4))) return st;
+  }
+
+  CombineParams cp{};
+  cp.y = w.y;
+  cp.y_bytes = w.h_rows * (int64_t)H * (dt == kF32 ? 4 : 2);
+  cp.row_of = w.row_of;
+  cp.weights = topk_weights;
+  cp.top_k = K;
+  cp.hidden = H;
+  cp.shared_row0 = a->S ? (int32_t)nmax : -1;
+  cp.out = (uint8_t*)out;
+  AFD_HIP(launch_combine(dt == kF32 ? kF32 : kBF16, cp, T, s));
+  if ((st = mark(5))) return st;
+  if (tmask) a->ev_pending.push_back(ev);
+  return AFD_OK;
 }
 
 }  // namespace
@@ -377,271 +674,11 @@ afd_status afd_ffn_destroy(afd_ffn_t* h) {
 afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const float* hidden_scales,
                            const int32_t* topk_ids, const float* topk_weights, void* out, void* stream) {
   g_last_error.clear();
-  if (!a) return fail(AFD_ERR_INVALID_ARG, "handle is NULL");
-  if (T < 0 || T > a->Tmax) return fail(AFD_ERR_INVALID_ARG, "num_tokens %d outside [0, %d]", T, a->Tmax);
-  if (T > 0 && (!hidden || !topk_ids || !topk_weights || !out))
-    return fail(AFD_ERR_INVALID_ARG, "hidden, topk_ids, topk_weights and out must be non-NULL");
-  if (a->dtype == kFP8 && T > 0 && !hidden_scales)
-    return fail(AFD_ERR_INVALID_ARG, "block-FP8 input needs hidden_scales");
-  if (a->dtype != kFP8 && hidden_scales)
-    return fail(AFD_ERR_INVALID_ARG, "hidden_scales is only used with AFD_DTYPE_FP8_BLOCK");
-  {
-    auto mis = [](const void* q, uintptr_t al) { return q && (reinterpret_cast<uintptr_t>(q) & (al - 1)); };
-    if (mis(hidden, 16) || mis(out, 16))
-      return fail(AFD_ERR_INVALID_ARG, "hidden and out must be 16-byte aligned");
-    if (mis(hidden_scales, 4) || mis(topk_ids, 4) || mis(topk_weights, 4))
-      return fail(AFD_ERR_INVALID_ARG, "hidden_scales, topk_ids and topk_weights must be 4-byte aligned");
-  }
-  DeviceGuard dg(a->device);
-  if (!dg.ok) return fail(AFD_ERR_HIP, "cannot select device %d", a->device);
-  hipStream_t s = (hipStream_t)stream;
-
-  const int E = a->E, K = a->K, H = a->H, I = a->I, dt = a->dtype;
-  const int64_t n_flat = (int64_t)T * K;
-  const int64_t nmax = (int64_t)a->Tmax * K;
-  // Light experts (rows <= bm_light, one m-tile) and heavier ones (and the
-  // shared expert) go to two tile lists.  bf16: light experts stream their
-  // weights through registers (gemm_stream.h), heavy ones take the LDS-tiled
-  // GEMM (gemm_tiled.hip), which fetches each weight panel once per tile of
-  // tiled_rows() rows; one mixed launch runs both, on disjoint CUs.
-  // Block-FP8: both lists run the weight-ring GEMM (gemm_ring.hip), light
-  // tiles (<= 64 rows) and heavy tiles of ring_rows(true) rows.  fp32 uses
-  // light tiles of 32 rows only.
-  const int mr = dt == kF32 ? 1 : (n_flat <= 32ll * E ? 1 : 2);
-  const int bm = 32 * mr;
-  const bool fp8 = dt == kFP8;
-  const int bm_heavy = dt == kF32 ? bm : fp8 ? ring_rows(true) : tiled_rows(dt);
-  // fp32 runs the light list only.  bf16 batches (no shared expert) of at
-  // most 32 rows per expert on average usually need no heavy list either:
-  // the streaming kernel runs alone (several workgroups per CU) over light
-  // tiles of 32 * mr_lo rows.  But skewed routing can put hundreds of rows on
-  // one expert of such a batch, and each of its light tiles would stream its
-  // weights again.  The host does not see the routing, so the dispatch
-  // chooses: every expert light while the largest has at most two light
-  // tiles of rows, else the mixed launch.  Both kernels are launched; the
-  // other returns at once.
-  const bool light_only = dt == kF32;
-  const bool auto_launch = dt == kBF16 && !a->S && n_flat <= 32ll * E;
-  const int heavy_min = light_only ? 0x7fffffff : bm + 1;
-  // light tiles when the dispatch keeps every expert light: 32 rows up to 16
-  // rows per expert on average, else 64 (one tile for most experts of a
-  // uniform batch); the mixed launch keeps 32-row light tiles
-  const int mr_lo = n_flat <= 16ll * E ? 1 : 2;
-  // CUs this call's persistent grids spread over: all of them, or an equal
-  // share when the caller runs several forwards at once on other streams
-  const int cus = std::max(1, a->num_cus / a->concurrency);
-  // boundary b lies before stage b (b = AFD_NUM_STAGES: after the last)
-  std::array<hipEvent_t, AFD_NUM_STAGES + 1> ev{};
-  const uint32_t tmask = a->timing_mask;
-  auto mark = [&](int b) -> afd_status {
-    const bool need = ((tmask >> b) & 1u) || (b > 0 && ((tmask >> (b - 1)) & 1u));
-    if (!need) return AFD_OK;
-    hipEvent_t e = take_event(a);
-    if (!e) return fail(AFD_ERR_HIP, "hipEventCreate failed");
-    AFD_HIP(hipEventRecord(e, s));
-    ev[b] = e;
-    return AFD_OK;
-  };
-  afd_status st;
-
-  DispatchParams d{};
-  d.ids = topk_ids;
-  d.n_flat = (int32_t)n_flat;
-  d.num_experts = E;
-  d.chunk_shift = chunk_shift_for(n_flat, E);
-  d.n_chunks = (int32_t)((n_flat + (1ll << d.chunk_shift) - 1) >> d.chunk_shift);
-  d.fused = n_flat <= kDispatchFuseSlots ? 1 : 0;
-  d.mix_cus = dt == kBF16 ? cus : 0;
-  d.auto_heavy_rows = auto_launch ? 2 * 32 * mr_lo + 1 : 0;
-  d.bm_light_only = 32 * mr_lo;
-  d.counts = a->counts;
-  d.offsets = a->offsets;
-  d.chunk_base = a->chunk_base;
-  d.err = a->err;
-  d.sorted_assign = a->sorted_assign;
-  d.row_of = a->row_of;
-  d.bm_light = bm;
-  d.bm_heavy = bm_heavy;
-  d.heavy_min_rows = heavy_min;
-  d.shared_rows = a->S ? T : 0;
-  d.shared_row0 = (int32_t)nmax;
-  d.mtiles = a->mtiles;
-  d.mtiles_heavy = a->mtiles_heavy;
-  d.num_mtiles = a->num_mtiles;
-  a->last_T = T;
-
-  if ((st = mark(0))) return st;
-  AFD_HIP(launch_dispatch_count_scan(d, s));
-  if ((st = mark(1))) return st;
-  if (T == 0) {
-    // nothing else to do (the later stages count as not timed)
-    if (tmask) a->ev_pending.push_back(ev);
-    return AFD_OK;
-  }
-  AFD_HIP(launch_dispatch_scatter(d, s));
-  if (dt == kFP8) {
-    ScaleGatherParams sg{};
-    sg.src = hidden_scales;
-    sg.ks = H / 128;
-    sg.tokens = T;
-    sg.top_k = K;
-    sg.sorted_assign = a->sorted_assign;
-    sg.offsets = a->offsets;
-    sg.num_experts = E;
-    sg.routed_max = (int32_t)n_flat;
-    sg.shared_row0 = a->S ? (int32_t)nmax : -1;
-    sg.dst = a->x_scales;
-    sg.ld = (int32_t)a->h_rows;
-    AFD_HIP(launch_gather_scales(sg, s));
-  }
-  if ((st = mark(2))) return st;
-
-  // upper bounds of the routed + shared m-tiles of this call, per list
-  const int64_t mt_bound = n_flat / bm + std::min<int64_t>(E, n_flat) + (a->S ? (T + bm - 1) / bm : 0) + 1;
-  const int64_t mth_bound = light_only ? 0 : n_flat / heavy_min + (a->S ? (T + bm_heavy - 1) / bm_heavy : 0) + 1;
-  const int64_t rows_ld_h = (int64_t)I * esize_of(dt);
-  const int64_t h_rows = nmax + (a->S ? a->Tmax : 0);
-  const int occupancy_wgs = 4;  // resident workgroups per CU the persistent grids aim for
-
-  if (dt == kF32) {
-    F32Params g{};
-    g.mtiles = a->mtiles;
-    g.num_mtiles = a->num_mtiles;
-    g.sorted_assign = a->sorted_assign;
-    g.top_k = K;
-    g.shared_row0 = (int32_t)nmax;
-    g.gather = 1;
-    g.a = (const float*)hidden;
-    g.w0 = (const float*)a->w->gu;
-    g.w1 = (const float*)a->w->up;
-    g.kdim = H;
-    g.ndim = I;
-    g.c = (float*)a->h;
-    int grid = (int)std::min<int64_t>(mt_bound * ((I + 63) / 64), (int64_t)cus * occupancy_wgs);
-    AFD_HIP(launch_gemm_f32(true, g, grid, s));
-    if ((st = mark(3))) return st;
-    g.gather = 0;
-    g.a = (const float*)a->h;
-    g.w0 = (const float*)a->w->dn;
-    g.w1 = nullptr;
-    g.kdim = I;
-    g.ndim = H;
-    g.c = (float*)a->y;
-    grid = (int)std::min<int64_t>(mt_bound * ((H + 63) / 64), (int64_t)cus * occupancy_wgs);
-    AFD_HIP(launch_gemm_f32(false, g, grid, s));
-    if ((st = mark(4))) return st;
-  } else {
-    const int es = esize_of(dt);
-    GemmParams g{};
-    g.mtiles = a->mtiles;
-    g.num_mtiles = a->num_mtiles;
-    g.sorted_assign = a->sorted_assign;
-    g.top_k = K;
-    g.shared_row0 = (int32_t)nmax;
-    // gate/up: A = hidden rows gathered by token
-    g.gather = 1;
-    g.a = (const uint8_t*)hidden;
-    g.a_bytes = (int64_t)T * H * es;
-    g.a_row_bytes = (int64_t)H * es;
-    g.a_scales = a->x_scales;  // gathered by gather_scales_kernel
-    g.a_scale_bytes = fp8 ? (int64_t)(H / 128) * a->h_rows * 4 : 0;
-    g.a_scale_ld = (int32_t)a->h_rows;
-    g.b = a->w->gu;
-    g.b_expert_bytes = a->w->gu_expert_bytes;
-    g.b_panel_bytes = a->w->gu_panel_bytes;
-    g.b_scales0 = a->w->sg;
-    g.b_scale_bytes = a->w->scale_bytes;
-    g.b_scales1 = a->w->su;
-    g.b_scale_rows = H / 128;
-    g.b_scale_cols = I / 128;
-    g.k_steps = (int32_t)((int64_t)H * es / kStepBytes);
-    g.n_panels = I / 32;
-    g.n_groups = I / 128;
-    g.c = a->h;
-    g.c_row_bytes = rows_ld_h;
-    g.c_scales = a->h_scales;
-    g.c_scale_ld = (int32_t)a->h_rows;
-    GemmParams gu_light = g;
-    GemmParams gu_heavy = g;
-    gu_heavy.mtiles = a->mtiles_heavy;
-    gu_heavy.num_mtiles = a->num_mtiles + 1;
-    gu_heavy.n_groups = (2 * I / 32 + tiled_panels() - 1) / tiled_panels();  // bf16 only
-    // down: A = h rows in sorted order
-    g.gather = 0;
-    g.a = a->h;
-    g.a_bytes = h_rows * rows_ld_h;
-    g.a_row_bytes = rows_ld_h;
-    g.a_scales = a->h_scales;
-    g.a_scale_bytes = fp8 ? h_rows * (I / 128) * 4 : 0;
-    g.a_scale_ld = (int32_t)a->h_rows;
-    g.b = a->w->dn;
-    g.b_expert_bytes = a->w->dn_expert_bytes;
-    g.b_panel_bytes = a->w->dn_panel_bytes;
-    g.b_scales0 = a->w->sd;
-    g.b_scales1 = a->w->sd;
-    g.b_scale_rows = I / 128;
-    g.b_scale_cols = H / 128;
-    g.k_steps = (int32_t)((int64_t)I * es / kStepBytes);
-    g.n_panels = H / 32;
-    // light tasks of the down GEMM: down_panels_per_task(mr) H panels (bf16
-    // streaming GEMM) or 8 (block-FP8 ring GEMM, both lists)
-    const int dn_panels = fp8 ? 8 : down_panels_per_task(mr);
-    g.n_groups = (H / 32 + dn_panels - 1) / dn_panels;
-    g.c = a->y;
-    g.c_row_bytes = (int64_t)H * 2;
-    g.c_scales = nullptr;
-    g.c_scale_ld = 0;
-    GemmParams dn_light = g;
-    GemmParams dn_heavy = g;
-    dn_heavy.mtiles = a->mtiles_heavy;
-    dn_heavy.num_mtiles = a->num_mtiles + 1;
-    dn_heavy.n_groups = (H / 32 + tiled_panels() - 1) / tiled_panels();  // bf16 only
-
-    // One launch per GEMM (two gated ones where the dispatch chooses).  bf16:
-    // the light list alone (streaming kernel, several workgroups per CU) or,
-    // once heavy experts occur, the mixed kernel:
-    // one workgroup per CU, the dispatch's share of them streaming the light
-    // list while the rest run the heavy tiles (HBM-bound and MFMA-bound work
-    // side by side; a heavy workgroup leaves no room for a light one on its
-    // CU, so the split is by CU).  Block-FP8 runs both lists in one launch of
-    // the ring GEMM.
-    auto stage = [&](bool gate_up, const GemmParams& light, const GemmParams& heavy) -> hipError_t {
-      if (fp8) {
-        GemmParams both = light;
-        both.mtiles2 = heavy.mtiles;
-        both.num_mtiles2 = heavy.num_mtiles;
-        return launch_gemm_ring(gate_up, a->concurrency == 1, both, (mt_bound + mth_bound) * light.n_groups, cus, s);
-      }
-      if (auto_launch) {
-        GemmParams lo = light, mx = light;
-        lo.only_launch = kLaunchLight;
-        mx.only_launch = kLaunchMixed;
-        if (!gate_up) lo.n_groups = (H / 32 + down_panels_per_task(mr_lo) - 1) / down_panels_per_task(mr_lo);
-        const hipError_t e = launch_gemm(dt, gate_up, mr_lo, lo, mt_bound * lo.n_groups, cus, s);
-        if (e != hipSuccess) return e;
-        return launch_gemm_mixed(gate_up, mr, heavy, mx, cus, s);
-      }
-      return launch_gemm_mixed(gate_up, mr, heavy, light, cus, s);
-    };
-    AFD_HIP(stage(true, gu_light, gu_heavy));
-    if ((st = mark(3))) return st;
-    AFD_HIP(stage(false, dn_light, dn_heavy));
-    if ((st = mark(4))) return st;
-  }
-
-  CombineParams cp{};
-  cp.y = a->y;
-  cp.y_bytes = (nmax + (a->S ? a->Tmax : 0)) * (int64_t)H * (dt == kF32 ? 4 : 2);
-  cp.row_of = a->row_of;
-  cp.weights = topk_weights;
-  cp.top_k = K;
-  cp.hidden = H;
-  cp.shared_row0 = a->S ? (int32_t)nmax : -1;
-  cp.out = (uint8_t*)out;
-  AFD_HIP(launch_combine(dt == kF32 ? kF32 : kBF16, cp, T, s));
-  if ((st = mark(5))) return st;
-  if (tmask) a->ev_pending.push_back(ev);
-  return AFD_OK;
+  afd_status st = check_forward_args(a, T, a ? a->Tmax : 0, hidden, hidden_scales, topk_ids, topk_weights, out);
+  if (st) return st;
+  st = forward_impl(a, a->ws, true, T, hidden, hidden_scales, topk_ids, topk_weights, out, stream);
+  if (st == AFD_OK) a->last_T = T;
+  return st;
 }
 
 afd_status afd_ffn_debug_dispatch(afd_ffn_t* a, int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
@@ -651,10 +688,11 @@ afd_status afd_ffn_debug_dispatch(afd_ffn_t* a, int32_t* counts, int32_t* offset
   DeviceGuard dg(a->device);
   hipStream_t s = (hipStream_t)stream;
   const int64_t n = (int64_t)a->last_T * a->K;
-  if (counts) AFD_HIP(hipMemcpyAsync(counts, a->counts, 4ll * a->E, hipMemcpyDeviceToDevice, s));
-  if (offsets) AFD_HIP(hipMemcpyAsync(offsets, a->offsets, 4ll * (a->E + 1), hipMemcpyDeviceToDevice, s));
-  if (sorted_assign && n) AFD_HIP(hipMemcpyAsync(sorted_assign, a->sorted_assign, 4 * n, hipMemcpyDeviceToDevice, s));
-  if (row_of && n) AFD_HIP(hipMemcpyAsync(row_of, a->row_of, 4 * n, hipMemcpyDeviceToDevice, s));
+  const Workspace& w = a->ws;
+  if (counts) AFD_HIP(hipMemcpyAsync(counts, w.counts, 4ll * a->E, hipMemcpyDeviceToDevice, s));
+  if (offsets) AFD_HIP(hipMemcpyAsync(offsets, w.offsets, 4ll * (a->E + 1), hipMemcpyDeviceToDevice, s));
+  if (sorted_assign && n) AFD_HIP(hipMemcpyAsync(sorted_assign, w.sorted_assign, 4 * n, hipMemcpyDeviceToDevice, s));
+  if (row_of && n) AFD_HIP(hipMemcpyAsync(row_of, w.row_of, 4 * n, hipMemcpyDeviceToDevice, s));
   return AFD_OK;
 }
 
@@ -663,7 +701,7 @@ afd_status afd_ffn_routing_errors(afd_ffn_t* a, int32_t* count, void* stream) {
   if (!a || !count) return fail(AFD_ERR_INVALID_ARG, "NULL argument");
   DeviceGuard dg(a->device);
   hipStream_t s = (hipStream_t)stream;
-  AFD_HIP(hipMemcpyAsync(count, a->err, 4, hipMemcpyDeviceToHost, s));
+  AFD_HIP(hipMemcpyAsync(count, a->ws.err, 4, hipMemcpyDeviceToHost, s));
   AFD_HIP(hipStreamSynchronize(s));
   return *count > 0 ? fail(AFD_ERR_BAD_ROUTING, "%d ids outside [-1, %d)", *count, a->E) : AFD_OK;
 }

@@ -160,6 +160,31 @@ afd_status afd_ffn_forward(afd_ffn_t *handle, int32_t num_tokens, const void *hi
                            const float *hidden_scales, const int32_t *topk_ids,
                            const float *topk_weights, void *out, void *stream);
 
+/*
+ * For callers that cannot allocate device memory when they run a layer: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same forward as afd_ffn_forward (same arguments, kernels and
+ * results, bit for bit), except that its workspace (dispatch arrays, tile
+ * lists, h, y and the FP8 activation scales) lies in a static device array of
+ * the library, AFD_FFN_NOALLOC_SCRATCH_BYTES bytes per device, instead of the
+ * handle's workspace.  It calls no allocating routine; the array's device
+ * address is looked up once per device, at the first such call there (a
+ * device holds the array until the process ends).  0 <= T is limited by that size, not by max_tokens: a call
+ * whose workspace would exceed it returns AFD_ERR_UNSUPPORTED before any GPU
+ * work (about 23 MiB for 256 tokens of H = 4096, I = 1536, K = 8 bf16; about
+ * 150 KiB per token of H = 7168, I = 2048, K = 8 block-FP8 with a shared
+ * expert).  No part of the array needs clearing: every element a call reads is
+ * written earlier by that call.  Every such call on a device shares that
+ * device's array, so calls that overlap on one device (on two streams, or a
+ * replay beside an eager call) race and give wrong results; calls on one
+ * stream one after another are fine.  Timing (afd_ffn_set_timing) and
+ * afd_ffn_debug_dispatch do not apply to these calls.
+ */
+#define AFD_FFN_NOALLOC_SCRATCH_BYTES (64u << 20)
+afd_status afd_ffn_forward_noalloc(afd_ffn_t *handle, int32_t num_tokens, const void *hidden,
+                                   const float *hidden_scales, const int32_t *topk_ids,
+                                   const float *topk_weights, void *out, void *stream);
+
 /* Release a handle (NULL is accepted).  Packed weights are freed when their
  * last sharer is destroyed.  Call only after the handle's stream work has
  * completed. */

@@ -26,6 +26,7 @@ STAGE_NAMES = ("dispatch_count_scan", "dispatch_scatter", "gemm_gate_up_swiglu",
 DTYPE_CODES = {"f32": AFD_DTYPE_F32, "bf16": AFD_DTYPE_BF16, "fp8": AFD_DTYPE_FP8_BLOCK}
 
 EXPORTS = ("afd_ffn_validate_config", "afd_ffn_create", "afd_ffn_clone", "afd_ffn_forward",
+           "afd_ffn_forward_noalloc",
            "afd_ffn_destroy", "afd_ffn_status_string", "afd_ffn_last_error", "afd_ffn_debug_dispatch",
            "afd_ffn_routing_errors", "afd_ffn_set_timing", "afd_ffn_set_timing_stages", "afd_ffn_get_timing",
            "afd_ffn_set_concurrency")
@@ -61,6 +62,7 @@ def load(path: str = LIB_PATH):
     lib.afd_ffn_create.argtypes = [ctypes.POINTER(afd_ffn_config), ctypes.POINTER(vp)]
     lib.afd_ffn_clone.argtypes = [vp, ctypes.POINTER(vp)]
     lib.afd_ffn_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
+    lib.afd_ffn_forward_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
     lib.afd_ffn_destroy.argtypes = [vp]
     lib.afd_ffn_status_string.argtypes = [ctypes.c_int]
     lib.afd_ffn_status_string.restype = ctypes.c_char_p
@@ -136,6 +138,13 @@ def afd_ffn_forward(handle, num_tokens: int, hidden, hidden_scales, topk_ids, to
                     stream=None) -> None:
     _check(load().afd_ffn_forward(handle, int(num_tokens), _ptr(hidden), _ptr(hidden_scales), _ptr(topk_ids),
                                   _ptr(topk_weights), _ptr(out), _stream(stream)))
+
+
+def afd_ffn_forward_noalloc(handle, num_tokens: int, hidden, hidden_scales, topk_ids, topk_weights, out,
+                            stream=None) -> None:
+    """The forward on the library's static device scratch (allocates nothing)."""
+    _check(load().afd_ffn_forward_noalloc(handle, int(num_tokens), _ptr(hidden), _ptr(hidden_scales),
+                                          _ptr(topk_ids), _ptr(topk_weights), _ptr(out), _stream(stream)))
 
 
 def afd_ffn_destroy(handle) -> None:

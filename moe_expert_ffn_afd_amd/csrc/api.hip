@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <array>
 #include <atomic>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -21,6 +22,16 @@
 #include "afd_internal.h"
 
 using namespace afd;
+
+// Device scratch of afd_ffn_forward_noalloc: the workspace of such a forward is
+// carved out of this array instead of the handle's allocation.  Host code
+// never passes the name itself to a kernel or a copy (on the host it is only a
+// stand-in for the symbol): it uses the device address hipGetSymbolAddress
+// returns, one per device (each device holds its own copy of the array).
+// The array has external linkage: a `static` one stays a local symbol of the
+// code object (this library is compiled without relocatable device code),
+// which the runtime's lookup by name does not find.
+__device__ __attribute__((used)) __align__(256) uint8_t afd_ffn_noalloc_scratch[AFD_FFN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -75,6 +86,34 @@ struct WeightStore {
 };
 
 int esize_of(int dtype) { return dtype == kF32 ? 4 : dtype == kBF16 ? 2 : 1; }
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_addr[kMaxScratchDevices];  // device address of the scratch array, per device ordinal
+
+// Device address of the scratch array on `device`, which must be the current
+// device; looked up once per device, at the first allocation-free forward there
+// (the library's code object is loaded by then: handle creation ran its
+// packing kernel on the device).
+afd_status scratch_address(int device, uint8_t** out) {
+  *out = nullptr;
+  if (device < 0 || device >= kMaxScratchDevices)
+    return fail(AFD_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", device,
+                kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(afd_ffn_noalloc_scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(AFD_ERR_HIP, "hipGetSymbolAddress(afd_ffn_noalloc_scratch) on device %d failed: %s", device,
+                  hipGetErrorString(e));
+    }
+    g_scratch_addr[device] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_addr[device];
+  return AFD_OK;
+}
 
 }  // namespace
 
@@ -679,6 +718,24 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   st = forward_impl(a, a->ws, true, T, hidden, hidden_scales, topk_ids, topk_weights, out, stream);
   if (st == AFD_OK) a->last_T = T;
   return st;
+}
+
+afd_status afd_ffn_forward_noalloc(afd_ffn_t* a, int32_t T, const void* hidden, const float* hidden_scales,
+                                   const int32_t* topk_ids, const float* topk_weights, void* out, void* stream) {
+  g_last_error.clear();
+  afd_status st = check_forward_args(a, T, 0x7fffffff, hidden, hidden_scales, topk_ids, topk_weights, out);
+  if (st) return st;
+  const int64_t need = layout_workspace(a, T, nullptr, nullptr);
+  if (need > (int64_t)AFD_FFN_NOALLOC_SCRATCH_BYTES)
+    return fail(AFD_ERR_UNSUPPORTED, "a forward of %d tokens needs %lld bytes of workspace; the static scratch holds %lld",
+                T, (long long)need, (long long)AFD_FFN_NOALLOC_SCRATCH_BYTES);
+  DeviceGuard dg(a->device);
+  if (!dg.ok) return fail(AFD_ERR_HIP, "cannot select device %d", a->device);
+  uint8_t* base = nullptr;
+  if ((st = scratch_address(a->device, &base))) return st;
+  Workspace w;
+  layout_workspace(a, T, base, &w);
+  return forward_impl(a, w, false, T, hidden, hidden_scales, topk_ids, topk_weights, out, stream);
 }
 
 afd_status afd_ffn_debug_dispatch(afd_ffn_t* a, int32_t* counts, int32_t* offsets, int32_t* sorted_assign,

@@ -2,6 +2,7 @@
 with the fp64 oracle on the same seeded inputs."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -32,8 +33,13 @@ def run_layer(p: dict, layer=None, stream=None, max_tokens=None):
     return layer, out
 
 
+# the oracle's threads: the host cores this process may use, at most 16 (a GPU
+# box's share of its host)
+ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def oracle_out(p_host: dict, tokens=None):
-    return orc.forward(p_host, tokens=tokens)
+    return orc.forward(p_host, tokens=tokens, nthreads=ORACLE_THREADS)
 
 
 def compare(gpu_out: torch.Tensor, ref: np.ndarray, dtype: str, tokens=None, what=""):
@@ -60,3 +66,60 @@ def check_dispatch(layer, p: dict):
 
 def problem(cfg: dict, seed=0, routing=None):
     return inputs.make_problem(cfg, seed=seed, device="cuda", routing=routing)
+
+
+# ---------------------------------------------------------------------------
+# m-tiles of a batch, for choosing compared tokens
+# ---------------------------------------------------------------------------
+
+def tile_lists(dtype: str, T: int, E: int, K: int, counts, shared: bool):
+    """The library's two m-tile lists for a batch, from the oracle's per-expert
+    counts and the tile policy the library documents (include/afd_ffn.h,
+    api.hip): fp32 has one list of 32-row tiles.  Otherwise light tiles hold
+    32*mr rows (mr = 1 up to 32 routed rows per expert on average, else 2) and
+    experts with more rows go to the heavy list (256-row bf16 tiles, 128-row
+    block-FP8 tiles), the shared expert too once T exceeds a light tile.  bf16
+    batches with no shared expert and at most 32 rows per expert on average keep
+    every expert light (tiles of 32, or of 64 past 16 rows per expert on
+    average) unless the largest expert exceeds two such tiles.
+    Returns {"light": [...], "heavy": [...]}, each tile (expert, first row in
+    the expert, rows); the shared expert is expert E, its rows are tokens."""
+    counts = np.asarray(counts)
+    n_flat = T * K
+    if dtype == "f32":
+        bm, bm_heavy, heavy_min = 32, 32, 1 << 30
+    else:
+        mr = 1 if n_flat <= 32 * E else 2
+        bm = 32 * mr
+        bm_heavy = 128 if dtype == "fp8" else 256
+        heavy_min = bm + 1
+        if dtype == "bf16" and not shared and n_flat <= 32 * E:
+            mr_lo = 1 if n_flat <= 16 * E else 2
+            if counts.max(initial=0) < 2 * 32 * mr_lo + 1:
+                bm, heavy_min = 32 * mr_lo, 1 << 30
+    lists = {"light": [], "heavy": []}
+    sizes = list(enumerate(counts.tolist())) + ([(E, T)] if shared else [])
+    for e, n in sizes:
+        heavy = n >= heavy_min
+        b = bm_heavy if heavy else bm
+        for r0 in range(0, n, b):
+            lists["heavy" if heavy else "light"].append((e, r0, min(b, n - r0)))
+    return lists
+
+
+def tile_covering_tokens(dtype: str, T: int, E: int, K: int, ids, shared: bool, max_tiles=None, seed=0):
+    """Tokens whose rows include the first and the last row of every m-tile of
+    both lists (of up to max_tiles tiles per list, chosen at random, when
+    given), and how many tiles of each list that covers."""
+    d = orc.dispatch(np.asarray(ids), E)
+    lists = tile_lists(dtype, T, E, K, d["counts"], shared)
+    rng = np.random.default_rng(seed)
+    tokens, covered = set(), {}
+    for name, tiles in lists.items():
+        if max_tiles is not None and len(tiles) > max_tiles:
+            tiles = [tiles[i] for i in sorted(rng.choice(len(tiles), max_tiles, replace=False))]
+        for e, r0, n in tiles:
+            for r in (r0, r0 + n - 1):
+                tokens.add(r if e == E else int(d["sorted_assign"][d["offsets"][e] + r]) // K)
+        covered[name] = (len(tiles), len(lists[name]))
+    return np.array(sorted(tokens), dtype=np.int64), covered

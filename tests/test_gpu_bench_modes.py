@@ -1,12 +1,20 @@
 """bench.py's other modes on the GPU, at the tiny fp32 workload: the step
 replayed from a HIP graph (graph_ms_per_step next to the eager line) and the
-batch-size sweep (one JSON line per T, every T of the sweep that fits)."""
+batch-size sweep (one JSON line per T, every T of the sweep that fits; the
+sweep's own path, one handle for the largest T running prefixes of one batch,
+checked against the oracle)."""
+import importlib.util
 import json
 import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
+import torch
+
+from gpu_util import check_dispatch, compare, oracle_out, say, to_host_problem
+from moe_expert_ffn_afd_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -31,3 +39,24 @@ def test_sweep_lines():
     assert [d["T"] for d in lines] == [64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384]
     for d in lines:
         assert d["routed_rows"] == 2 * d["T"] and d["ms_per_step"] > 0
+
+
+def test_sweep_path_matches_oracle():
+    """The sweep's handle (sized for T=16384) and batch, at the smallest and the
+    largest T: dispatch bit-exact and every token against the oracle."""
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    cfg, sizes, p, layer = bench.sweep_setup("tiny", 0)
+    ids = p["ids"].cpu().numpy()
+    for T in (sizes[0], sizes[-1]):
+        say("sweep prefix T =", T)
+        q = inputs.slice_tokens(p, 0, T)
+        out = layer.out_like(T)
+        layer.forward(q["hidden"], q["hidden_scales"], q["ids"], q["weights"], out=out)
+        torch.cuda.synchronize()
+        check_dispatch(layer, q)
+        assert int((ids[:T] >= 0).sum()) == bench.algorithmic_units(dict(cfg, T=T), ids[:T])["N"]
+        compare(out, oracle_out(to_host_problem(q)), cfg["dtype"], what="sweep T=%d" % T)
+        assert np.isfinite(out.cpu().numpy()).all()
+    layer.close()

@@ -1,11 +1,13 @@
 """Benchmark of the FFN-side MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fp8_shared]
 
 A step is one forward of the whole layer (dispatch count+scan, scatter,
 grouped GEMM gate/up + SwiGLU, grouped GEMM down, combine) over one batch of
 seeded synthetic tokens already resident in HBM; the verify_shard workload
-runs its two microbatches on two streams per step.  Prints one JSON line with
+runs its two microbatches on two streams per step.  The default workload is
+the largest one-GPU configuration: block-FP8 experts with a shared expert,
+T=2048, H=7168, E=256, I=2048, top-8.  Prints one JSON line with
 routed tokens/s, the roofline of the dominant kernel (timed with HIP events
 on its own stream inside the timed region, the only stage timed there) and
 the oracle's CPU baseline; the per-stage breakdown comes from up to 20 further
@@ -117,25 +119,34 @@ def cpu_baseline(p: dict, cfg: dict, budget_s: float = 12.0) -> dict:
 SWEEP_TOKENS = (64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384)
 
 
+def sweep_setup(workload: str, seed: int):
+    """The sweep's batch sizes, its one seeded batch of the largest size and one
+    handle sized for it (each T of the sweep runs the first T tokens)."""
+    from moe_expert_ffn_afd_amd import afd, inputs
+
+    base = inputs.workload(workload)
+    if base.get("microbatches", 1) != 1:
+        sys.exit("--sweep takes a one-microbatch workload")
+    H, K = base["H"], base["K"]
+    out_row = 4 if base["dtype"] == "f32" else 2
+    rows_per_token = K + (1 if base.get("shared_inter") else 0)
+    # down outputs [rows, H] stay within 32-bit buffer offsets
+    sizes = [t for t in SWEEP_TOKENS if t * rows_per_token * H * out_row < (1 << 31)]
+    cfg = dict(base, T=max(sizes))
+    p = inputs.make_problem(cfg, seed=seed, device="cuda")
+    layer = afd.Layer(p, max_tokens=cfg["T"])
+    return cfg, sizes, p, layer
+
+
 def sweep(args) -> None:
     """Layer time against the batch size at one workload's shape: one handle
     sized for the largest T, one seeded batch of that size, and each T taking
     its first T tokens (the routing's distribution does not change with T)."""
     import torch
 
-    from moe_expert_ffn_afd_amd import afd, inputs
+    from moe_expert_ffn_afd_amd import inputs
 
-    base = inputs.workload(args.workload)
-    if base.get("microbatches", 1) != 1:
-        sys.exit("--sweep takes a one-microbatch workload")
-    H, I, K = base["H"], base["I"], base["K"]
-    out_row = 4 if base["dtype"] == "f32" else 2
-    rows_per_token = K + (1 if base.get("shared_inter") else 0)
-    # down outputs [rows, H] stay within 32-bit buffer offsets
-    sizes = [t for t in SWEEP_TOKENS if t * rows_per_token * H * out_row < (1 << 31)]
-    cfg = dict(base, T=max(sizes))
-    p = inputs.make_problem(cfg, seed=args.seed, device="cuda")
-    layer = afd.Layer(p, max_tokens=cfg["T"])
+    cfg, sizes, p, layer = sweep_setup(args.workload, args.seed)
     ids_np = p["ids"].cpu().numpy()
     stream = torch.cuda.current_stream()
     for T in sizes:
@@ -167,7 +178,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode",
+    ap.add_argument("--workload", default="fp8_shared",
                     choices=["tiny", "decode", "aggregated", "fp8_shared", "verify_shard"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -318,20 +329,30 @@ def main():
     launches_per_step = mbs
     gu_bytes = units["gu_bytes"] / launches_per_step
     gu_flops = units["gu_flops"] / launches_per_step
+    hbm_ach = gu_bytes / gu_launch_s / 1e9
+    mfma_ach = gu_flops / gu_launch_s / 1e12
+    # the bound follows the layer's arithmetic intensity against the ridge
     ai = units["layer_flops"] / units["layer_bytes"]
     ridge = PEAK_TFLOPS[dt] * 1e12 / (PEAK_HBM_GBS * 1e9)
     if ai < ridge:
-        ach = gu_bytes / gu_launch_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4)}
+        roof = {"bound": "hbm", "achieved": round(hbm_ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(hbm_ach / PEAK_HBM_GBS, 4)}
     else:
-        ach = gu_flops / gu_launch_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_TFLOPS[dt], 4)}
+        roof = {"bound": "mfma", "achieved": round(mfma_ach, 1), "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s",
+                "frac": round(mfma_ach / PEAK_TFLOPS[dt], 4)}
+    # both fractions of the same launch, whichever bound the layer sits at
+    roof["hbm_frac"] = round(hbm_ach / PEAK_HBM_GBS, 4)
+    roof["mfma_frac"] = round(mfma_ach / PEAK_TFLOPS[dt], 4)
     roof["kernel"] = gate_up_kernels(cfg, T // mbs)
     roof["launch_ms"] = round(gu_launch_ms, 4)
     # launches of this kernel running at once, each on its share of the CUs
     roof["concurrent_launches"] = 1 if serial else mbs
+    if not serial and mbs > 1:
+        # the concurrent launches start together on disjoint CU shares: their
+        # bytes together over their mean duration (the window they share)
+        agg = units["gu_bytes"] / gu_launch_s / 1e9
+        roof["aggregate_hbm_gbs"] = round(agg, 1)
+        roof["aggregate_hbm_frac"] = round(agg / PEAK_HBM_GBS, 4)
     traffic = None
     try:
         with open(TRAFFIC_FILE) as f:

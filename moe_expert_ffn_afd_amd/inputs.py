@@ -4,9 +4,11 @@ This module is shared by the HIP path's tests and benchmark and by the oracle
 tests.  It holds none of the layer's own arithmetic: only the draws that on
 the pages happen before the expert GPU sees the data -- top-k routing chosen
 on the attention side ("FastAFD" summary, System Design item 1), the token
-hidden states, and the expert weights -- plus their block-FP8 encoding
+hidden states, and the expert weights -- plus their 8-bit encodings: block-FP8
 (attention GPUs publish FP8 tokens, System Design item 2; experts are kept in
-block-FP8, item 1).  FP8 encoding uses torch's own E4M3FN cast.
+block-FP8, item 1), with torch's own E4M3FN cast, and W8A8 int8 (the expert
+precision of the vLLM AFD plugin blog's decode benchmark), with torch's
+round-half-to-even.
 
 Workloads (synthetic stand-ins for the pages' models and prompts, which are
 not available here; the pages print no layer shapes):
@@ -21,6 +23,9 @@ not available here; the pages print no layer shapes):
                 H=7168, the 32 local experts [0,32) of 256 global ones,
                 I=2048, top-8 over the 256 with non-local slots set to -1;
                 run as two microbatches of 2048 tokens
+  w8a8_shared   W8A8 int8 (per-channel weight scales, per-token activation
+                scales), the fp8_shared shape: T=2048, H=7168, E=256, I=2048,
+                top-8, plus one shared expert (I=2048)
 
 Hidden ~ N(0,1); weights ~ N(0, 0.02); router logits ~ N(0,1) (+ log Zipf
 prior for `aggregated`); softmax, top-k (ties to the lower expert index),
@@ -35,6 +40,7 @@ import torch
 
 FP8_MAX = 448.0  # largest finite OCP E4M3FN value
 FP8_GROUP = 128  # activation group (1 x 128) and weight block (128 x 128) edge
+I8_MAX = 127.0   # largest int8 code of the symmetric W8A8 encoding
 
 WORKLOADS = {
     "tiny": dict(dtype="f32", T=64, H=256, E=8, I=512, K=2, routing="uniform"),
@@ -45,6 +51,8 @@ WORKLOADS = {
                        shared_inter=2048),
     "verify_shard": dict(dtype="fp8", T=4096, H=7168, E=32, I=2048, K=8, routing="local_shard",
                          global_experts=256, microbatches=2, draft_q=4),
+    "w8a8_shared": dict(dtype="w8a8", T=2048, H=7168, E=256, I=2048, K=8, routing="uniform",
+                        shared_inter=2048),
 }
 
 WORKLOAD_TITLES = {
@@ -53,6 +61,7 @@ WORKLOAD_TITLES = {
     "aggregated": "aggregated_zipf1.2_bf16_T4096_H4096_E128_I1536_top8",
     "fp8_shared": "blockfp8_shared_T2048_H7168_E256+1_I2048_top8",
     "verify_shard": "blockfp8_verify_q4_T4096_H7168_E32of256_I2048_top8_2x2048",
+    "w8a8_shared": "w8a8_shared_T2048_H7168_E256+1_I2048_top8",
 }
 
 
@@ -135,6 +144,32 @@ def quantize_fp8_block(w: torch.Tensor):
 
 
 # --------------------------------------------------------------------------
+# W8A8 encoding (symmetric int8, round half to even)
+# --------------------------------------------------------------------------
+
+def _int8_codes(v: torch.Tensor, scale: torch.Tensor) -> torch.Tensor:
+    return torch.round(v / scale).clamp(-I8_MAX, I8_MAX).to(torch.int8)
+
+
+def quantize_int8_rows(x: torch.Tensor):
+    """x [T,H] fp32 -> (codes int8 [T,H], scales fp32 [T]); one scale per
+    token: amax/127 (1 when the row is all zero)."""
+    x = x.float()
+    amax = x.abs().amax(dim=1)
+    scale = torch.where(amax > 0, amax / I8_MAX, torch.ones_like(amax))
+    return _int8_codes(x, scale[:, None]).contiguous(), scale.contiguous()
+
+
+def quantize_int8_cols(w: torch.Tensor):
+    """w [R,C] fp32 -> (codes int8 [R,C], scales fp32 [C]); one scale per
+    output channel (column): amax/127 (1 when the column is all zero)."""
+    w = w.float()
+    amax = w.abs().amax(dim=0)
+    scale = torch.where(amax > 0, amax / I8_MAX, torch.ones_like(amax))
+    return _int8_codes(w, scale[None, :]).contiguous(), scale.contiguous()
+
+
+# --------------------------------------------------------------------------
 # tensors
 # --------------------------------------------------------------------------
 
@@ -151,15 +186,18 @@ def make_hidden(T: int, H: int, dtype: str, seed: int = 0, device="cpu"):
         return x, None
     if dtype == "bf16":
         return x.to(torch.bfloat16), None
+    if dtype == "w8a8":
+        return quantize_int8_rows(x)
     return quantize_fp8_rows(x)
 
 
 def make_expert_weights(E: int, H: int, I: int, dtype: str, seed: int = 0, device="cpu",
                         stream: int = 2, std: float = 0.02):
     """Wg, Wu [E,H,I], Wd [E,I,H] ~ N(0, std), encoded; FP8 also returns the
-    [E,H/128,I/128], [E,H/128,I/128], [E,I/128,H/128] block scales."""
+    [E,H/128,I/128], [E,H/128,I/128], [E,I/128,H/128] block scales, W8A8 the
+    [E,I], [E,I], [E,H] per-output-channel scales."""
     g = _gen(device, seed, stream)
-    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[dtype]
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8, "w8a8": torch.int8}[dtype]
     wg = torch.empty((E, H, I), dtype=tdt, device=device)
     wu = torch.empty((E, H, I), dtype=tdt, device=device)
     wd = torch.empty((E, I, H), dtype=tdt, device=device)
@@ -168,11 +206,14 @@ def make_expert_weights(E: int, H: int, I: int, dtype: str, seed: int = 0, devic
         scales = (torch.empty((E, H // FP8_GROUP, I // FP8_GROUP), device=device),
                   torch.empty((E, H // FP8_GROUP, I // FP8_GROUP), device=device),
                   torch.empty((E, I // FP8_GROUP, H // FP8_GROUP), device=device))
+    elif dtype == "w8a8":
+        scales = (torch.empty((E, I), device=device), torch.empty((E, I), device=device),
+                  torch.empty((E, H), device=device))
     for e in range(E):  # one expert at a time keeps the fp32 staging small
         for j, (dst, shape) in enumerate(((wg, (H, I)), (wu, (H, I)), (wd, (I, H)))):
             w = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
-            if dtype == "fp8":
-                q, s = quantize_fp8_block(w)
+            if dtype in ("fp8", "w8a8"):
+                q, s = quantize_fp8_block(w) if dtype == "fp8" else quantize_int8_cols(w)
                 dst[e].copy_(q)
                 scales[j][e].copy_(s)
             else:
@@ -229,5 +270,6 @@ def ceil_div(a: int, b: int) -> int:
 
 
 __all__ = ["WORKLOADS", "WORKLOAD_TITLES", "workload", "make_routing", "quantize_fp8_rows",
-           "quantize_fp8_block", "make_hidden", "make_expert_weights", "make_problem",
+           "quantize_fp8_block", "quantize_int8_rows", "quantize_int8_cols", "I8_MAX", "make_hidden",
+           "make_expert_weights", "make_problem",
            "slice_tokens", "FP8_MAX", "FP8_GROUP", "ceil_div", "expected_routed_rows"]

@@ -27,6 +27,12 @@
  * scale (1x128 groups along H for activations, 128x128 blocks for weights).
  * The intermediate activation is kept exact (no re-quantisation).
  *
+ * W8A8 (the "W8A8" expert precision of the vLLM AFD plugin blog's decode
+ * benchmark; the page names only "W8A8", so the format is a reading): int8
+ * codes, symmetric, weights with one fp32 scale per output channel (per
+ * column of Wg, Wu [H, I] and of Wd [I, H]), activations with one fp32 scale
+ * per token; a value is code times its scale, decoded exactly to fp64 here.
+ *
  * Dispatch (the expert-major permutation the GPU builds) is given by its
  * definition: per-expert counts, exclusive prefix sums, and the flat
  * assignment indices t*K+k listed expert by expert in ascending flat order.
@@ -42,18 +48,19 @@
 #include <string.h>
 #include <unistd.h>
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8 = 2, ORACLE_W8A8 = 3 };
 
 typedef struct {
     int32_t T, H, I, E, K;   /* tokens, hidden, intermediate, experts, top-k     */
     int32_t shared_inter;    /* 0: no shared expert; else its intermediate size  */
-    int32_t dtype;           /* ORACLE_F32 / ORACLE_BF16 / ORACLE_FP8             */
-    const void *hidden;      /* [T,H] f32 | bf16 bits | e4m3 codes                */
-    const float *hidden_scales; /* FP8: [T, H/128]                                */
+    int32_t dtype;           /* ORACLE_F32 / ORACLE_BF16 / ORACLE_FP8 / ORACLE_W8A8 */
+    const void *hidden;      /* [T,H] f32 | bf16 bits | e4m3 codes | int8 codes   */
+    const float *hidden_scales; /* FP8: [T, H/128]; W8A8: [T] (one per token)     */
     const int32_t *ids;      /* [T,K], -1 = not here                              */
     const float *weights;    /* [T,K]                                             */
     const void *w_gate, *w_up, *w_down;   /* [E,H,I], [E,H,I], [E,I,H]            */
-    const float *s_gate, *s_up, *s_down;  /* FP8: [E,H/128,I/128] x2, [E,I/128,H/128] */
+    const float *s_gate, *s_up, *s_down;  /* FP8: [E,H/128,I/128] x2, [E,I/128,H/128];
+                                             W8A8: [E,I] x2, [E,H] (per output column) */
     const void *sh_gate, *sh_up, *sh_down;    /* shared: [H,Is], [H,Is], [Is,H]   */
     const float *sh_s_gate, *sh_s_up, *sh_s_down;
 } afd_oracle_problem;
@@ -84,8 +91,15 @@ double afd_oracle_e4m3_to_f64(uint8_t c)
     return s ? -v : v;
 }
 
+double afd_oracle_i8_to_f64(uint8_t raw)
+{
+    /* two's complement: bytes 128..255 are -128..-1 */
+    return (double)(raw < 128 ? (int)raw : (int)raw - 256);
+}
+
 /* Element (r, c) of a row-major [rows, cols] matrix, decoded.  For FP8,
- * `scales` is the [rows/128, cols/128] block-scale grid of that matrix. */
+ * `scales` is the [rows/128, cols/128] block-scale grid of that matrix; for
+ * W8A8 its [cols] per-column scales. */
 static double elem(int dtype, const void *base, size_t off, int cols,
                    const float *scales, int r, int c)
 {
@@ -95,6 +109,8 @@ static double elem(int dtype, const void *base, size_t off, int cols,
         return (double)((const float *)base)[i];
     case ORACLE_BF16:
         return afd_oracle_bf16_to_f64(((const uint16_t *)base)[i]);
+    case ORACLE_W8A8:
+        return afd_oracle_i8_to_f64(((const uint8_t *)base)[i]) * (double)scales[c];
     default: {
         int bc = cols / 128;
         return afd_oracle_e4m3_to_f64(((const uint8_t *)base)[i]) *
@@ -147,7 +163,7 @@ typedef struct {
     int dtype, H, Is;
     const void *wg, *wu, *wd;
     size_t og, ou, od;             /* element offset of this expert's matrices */
-    const float *sg, *su, *sd;     /* this expert's scale grids (FP8)           */
+    const float *sg, *su, *sd;     /* this expert's scales (FP8 grids, W8A8 columns) */
 } ffn_view;
 
 /* f[H] = Wd^T (silu(Wg^T x) .* (Wu^T x)), all in fp64. g, u: scratch [Is]. */
@@ -192,6 +208,10 @@ static ffn_view routed_view(const afd_oracle_problem *p, int e)
         v.sg = p->s_gate + (size_t)e * sblk;
         v.su = p->s_up + (size_t)e * sblk;
         v.sd = p->s_down + (size_t)e * sblk;
+    } else if (p->dtype == ORACLE_W8A8) {
+        v.sg = p->s_gate + (size_t)e * I;
+        v.su = p->s_up + (size_t)e * I;
+        v.sd = p->s_down + (size_t)e * H;
     } else {
         v.sg = v.su = v.sd = NULL;
     }
@@ -227,6 +247,10 @@ static void token_output(const afd_oracle_problem *p, int t, double *x, double *
             break;
         case ORACLE_BF16:
             x[h] = afd_oracle_bf16_to_f64(((const uint16_t *)p->hidden)[i]);
+            break;
+        case ORACLE_W8A8:
+            x[h] = afd_oracle_i8_to_f64(((const uint8_t *)p->hidden)[i]) *
+                   (double)p->hidden_scales[t];
             break;
         default:
             x[h] = afd_oracle_e4m3_to_f64(((const uint8_t *)p->hidden)[i]) *
@@ -295,7 +319,8 @@ int afd_oracle_forward(const afd_oracle_problem *p, int32_t ntok, const int32_t 
                        double *out, int32_t nthreads)
 {
     if (!p || p->T < 0 || p->H <= 0 || p->I <= 0 || p->E <= 0 || p->K <= 0 ||
-        p->shared_inter < 0 || ntok < 0 || (ntok > 0 && (!tokens || !out)))
+        p->shared_inter < 0 || p->dtype < ORACLE_F32 || p->dtype > ORACLE_W8A8 || ntok < 0 ||
+        (ntok > 0 && (!tokens || !out)))
         return -1;
     if (p->dtype == ORACLE_FP8 && (p->H % 128 || p->I % 128 || p->shared_inter % 128))
         return -1;

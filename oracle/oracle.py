@@ -21,7 +21,7 @@ _LIB = os.path.join(_HERE, "libafd_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
+DTYPES = {"f32": 0, "bf16": 1, "fp8": 2, "w8a8": 3}
 
 
 def library_path() -> str:
@@ -70,6 +70,8 @@ def load(path: str | None = None):
         lib.afd_oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
         lib.afd_oracle_e4m3_to_f64.restype = ctypes.c_double
         lib.afd_oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        lib.afd_oracle_i8_to_f64.restype = ctypes.c_double
+        lib.afd_oracle_i8_to_f64.argtypes = [ctypes.c_uint8]
         if path is None:
             _lib = lib
         return lib
@@ -101,6 +103,11 @@ def e4m3_decode(code: int, lib=None) -> float:
     return (lib or load()).afd_oracle_e4m3_to_f64(int(code))
 
 
+def i8_decode(raw: int, lib=None) -> float:
+    """Value of an int8 code given as its raw byte 0..255."""
+    return (lib or load()).afd_oracle_i8_to_f64(int(raw))
+
+
 def bf16_decode(bits: int, lib=None) -> float:
     return (lib or load()).afd_oracle_bf16_to_f64(int(bits))
 
@@ -114,10 +121,10 @@ def _as_raw(a, dtype: str):
         t = a.detach().cpu().contiguous()
         if t.dtype == torch.bfloat16 or t.dtype == torch.float16:
             t = t.view(torch.int16)
-        elif t.dtype == torch.float8_e4m3fn:
+        elif t.dtype == torch.float8_e4m3fn or t.dtype == torch.int8:
             t = t.view(torch.uint8)
         a = t.numpy()
-    want = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dtype]
+    want = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "w8a8": np.uint8}[dtype]
     a = np.ascontiguousarray(a)
     if a.dtype != want:
         a = a.view(want) if a.dtype.itemsize == np.dtype(want).itemsize else a.astype(want)
@@ -135,9 +142,11 @@ def _f32(a):
 def forward(p: dict, tokens=None, nthreads: int = 0, lib=None) -> np.ndarray:
     """fp64 outputs [len(tokens), H] for the problem dict ``p``.
 
-    ``p`` holds: dtype ('f32'|'bf16'|'fp8'), hidden [T,H], hidden_scales (fp8),
-    ids [T,K] int32, weights [T,K] fp32, w_gate/w_up [E,H,I], w_down [E,I,H],
-    s_gate/s_up/s_down (fp8), optionally sh_gate/sh_up/sh_down (+ sh_s_*).
+    ``p`` holds: dtype ('f32'|'bf16'|'fp8'|'w8a8'), hidden [T,H], hidden_scales
+    (fp8 [T,H/128], w8a8 [T]), ids [T,K] int32, weights [T,K] fp32, w_gate/w_up
+    [E,H,I], w_down [E,I,H], s_gate/s_up/s_down (fp8 block grids, w8a8
+    [E,I], [E,I], [E,H] per output column), optionally sh_gate/sh_up/sh_down
+    (+ sh_s_*).
     Arrays may be numpy or torch (any device; copied to host).
     """
     lib = lib or load()
@@ -153,7 +162,7 @@ def forward(p: dict, tokens=None, nthreads: int = 0, lib=None) -> np.ndarray:
     prob = _Problem(T=T, H=H, I=I, E=E, K=K, shared_inter=0, dtype=DTYPES[dt])
     prob.hidden, prob.ids, prob.weights = _ptr(hidden), _ptr(ids), _ptr(wts)
     prob.w_gate, prob.w_up, prob.w_down = _ptr(wg), _ptr(wu), _ptr(wd)
-    if dt == "fp8":
+    if dt in ("fp8", "w8a8"):
         hs, sg, su, sd = (_f32(p[n]) for n in ("hidden_scales", "s_gate", "s_up", "s_down"))
         keep += [hs, sg, su, sd]
         prob.hidden_scales, prob.s_gate, prob.s_up, prob.s_down = _ptr(hs), _ptr(sg), _ptr(su), _ptr(sd)
@@ -162,7 +171,7 @@ def forward(p: dict, tokens=None, nthreads: int = 0, lib=None) -> np.ndarray:
         keep += [shg, shu, shd]
         prob.shared_inter = shg.shape[1]
         prob.sh_gate, prob.sh_up, prob.sh_down = _ptr(shg), _ptr(shu), _ptr(shd)
-        if dt == "fp8":
+        if dt in ("fp8", "w8a8"):
             ssg, ssu, ssd = (_f32(p[n]) for n in ("sh_s_gate", "sh_s_up", "sh_s_down"))
             keep += [ssg, ssu, ssd]
             prob.sh_s_gate, prob.sh_s_up, prob.sh_s_down = _ptr(ssg), _ptr(ssu), _ptr(ssd)

@@ -5,8 +5,8 @@ deliberately broken build of it) and raises AssertionError when the oracle
 disagrees with:
 
 * library routines: numpy's bincount / cumsum / stable argsort for the
-  dispatch, torch's bf16 and E4M3FN decoders, torch fp64 matrix products for
-  the one-expert case (a plain SwiGLU FFN);
+  dispatch, torch's bf16, E4M3FN and int8 decoders, torch fp64 matrix
+  products for the one-expert case (a plain SwiGLU FFN);
 * a dense brute-force formulation on tiny inputs: every expert applied to
   every token, masked by a [T,E] routing-weight matrix (no gather, no per-slot
   loop, no shared code with the oracle);
@@ -43,14 +43,19 @@ def torch_decode(a, dtype):
         return t.double().numpy()
     if dtype == "bf16":
         return t.view(torch.bfloat16).double().numpy() if t.dtype != torch.bfloat16 else t.double().numpy()
+    if dtype == "w8a8":
+        return t.view(torch.int8).double().numpy()
     return t.view(torch.float8_e4m3fn).double().numpy()
 
 
 def dequant(codes, scales, dtype):
     v = torch_decode(codes, dtype)
-    if dtype != "fp8":
+    if dtype not in ("fp8", "w8a8"):
         return v
     s = scales.cpu().double().numpy() if isinstance(scales, torch.Tensor) else np.asarray(scales, np.float64)
+    if dtype == "w8a8":
+        # one scale per output column, the same for every row of the matrix
+        return v * np.expand_dims(s, -2)
     # expand the block grid over the last two axes
     s = np.repeat(np.repeat(s, 128, axis=-2), 128, axis=-1) if s.ndim >= 2 else s
     return v * s
@@ -63,6 +68,8 @@ def dense_reference(p):
     if dt == "fp8":
         hs = p["hidden_scales"].cpu().double().numpy()
         X = X * np.repeat(hs, 128, axis=1)
+    if dt == "w8a8":
+        X = X * p["hidden_scales"].cpu().double().numpy()[:, None]
     Wg = dequant(p["w_gate"], p["s_gate"], dt)
     Wu = dequant(p["w_up"], p["s_up"], dt)
     Wd = dequant(p["w_down"], p["s_down"], dt)
@@ -151,17 +158,22 @@ def pin_decoders(lib):
     refb = torch.from_numpy(bits.astype(np.int32)).to(torch.int16).view(torch.bfloat16).double().numpy()
     gotb = np.array([orc.bf16_decode(int(b), lib=lib) for b in bits])
     assert np.array_equal(gotb, refb), "bf16 values"
+    refi = codes.view(torch.int8).double().numpy()
+    goti = np.array([orc.i8_decode(c, lib=lib) for c in range(256)])
+    assert np.array_equal(goti, refi), "int8 values"
 
 
 def pin_single_expert_dense(lib):
     """E=1, K=1, w=1: the layer is one dense SwiGLU FFN (torch fp64 matmuls)."""
-    for dt, H, I in (("f32", 96, 160), ("bf16", 128, 192), ("fp8", 256, 384)):
+    for dt, H, I in (("f32", 96, 160), ("bf16", 128, 192), ("fp8", 256, 384), ("w8a8", 128, 192)):
         T = 6
         routing = (np.zeros((T, 1), np.int32), np.ones((T, 1), np.float32))
         p = tiny_problem(dt, T=T, H=H, I=I, E=1, K=1, routing=routing)
         x = torch.from_numpy(torch_decode(p["hidden"], dt))
         if dt == "fp8":
             x = x * torch.from_numpy(np.repeat(p["hidden_scales"].double().numpy(), 128, axis=1))
+        if dt == "w8a8":
+            x = x * p["hidden_scales"].double()[:, None]
         Wg = torch.from_numpy(dequant(p["w_gate"], p["s_gate"], dt)[0])
         Wu = torch.from_numpy(dequant(p["w_up"], p["s_up"], dt)[0])
         Wd = torch.from_numpy(dequant(p["w_down"], p["s_down"], dt)[0])
@@ -174,7 +186,8 @@ def pin_brute_force(lib):
     """Random tiny problems, all dtypes, duplicates, -1 slots, shared expert."""
     rng = np.random.default_rng(5)
     for dt, H, I, shared in (("f32", 64, 96, 0), ("bf16", 64, 128, 0), ("fp8", 256, 384, 0),
-                             ("f32", 64, 96, 96), ("fp8", 128, 256, 256)):
+                             ("f32", 64, 96, 96), ("fp8", 128, 256, 256), ("w8a8", 64, 96, 0),
+                             ("w8a8", 64, 96, 160)):
         T, E, K = 10, 4, 3
         ids = rng.integers(-1, E, size=(T, K)).astype(np.int32)
         ids[0] = [1, 1, 1]             # duplicate ids in one row

@@ -52,6 +52,31 @@ def test_fp8_rows_and_blocks():
     assert qw.view(torch.float8_e4m3fn).float().abs().max() <= 448.0
 
 
+def test_int8_rows_and_columns():
+    x = torch.randn(5, 96) * 3
+    x[2] = 0.0
+    q, s = inputs.quantize_int8_rows(x)
+    assert q.dtype == torch.int8 and s.shape == (5,)
+    assert s[2] == 1.0 and torch.all(q[2] == 0)
+    amax = x.abs().amax(1)
+    assert torch.allclose(s[amax > 0], amax[amax > 0] / 127.0)
+    assert q.abs().max() == 127 and torch.all(q.int().abs() <= 127)
+    # round to nearest: every value within half a step of its code
+    dec = q.float() * s[:, None]
+    assert torch.all((dec - x).abs() <= 0.5 * s[:, None] * (1 + 1e-6))
+    # the largest element of each row lands exactly on +-127
+    assert torch.all(q.gather(1, x.abs().argmax(1, keepdim=True)).abs()[amax > 0] == 127)
+    w = torch.randn(200, 48) * 0.02
+    w[:, 7] = 0.0
+    qw, sw = inputs.quantize_int8_cols(w)
+    assert qw.shape == (200, 48) and sw.shape == (48,) and sw[7] == 1.0 and torch.all(qw[:, 7] == 0)
+    assert torch.allclose(sw[torch.arange(48) != 7], w.abs().amax(0)[torch.arange(48) != 7] / 127.0)
+    assert torch.all((qw.float() * sw[None, :] - w).abs() <= 0.5 * sw[None, :] * (1 + 1e-6))
+    # ties go to the even code (torch.round): 2.5 steps -> 2, 3.5 steps -> 4
+    qt, st = inputs.quantize_int8_rows(torch.tensor([[127.0, 2.5, 3.5, -2.5]]))
+    assert st.item() == 1.0 and qt.tolist() == [[127, 2, 4, -2]]
+
+
 def test_make_problem_shapes():
     cfg = dict(dtype="fp8", T=8, H=256, I=384, E=3, K=2, routing="uniform", shared_inter=256)
     p = inputs.make_problem(cfg, seed=1)
@@ -61,6 +86,11 @@ def test_make_problem_shapes():
     assert p["sh_gate"].shape == (256, 256) and p["sh_s_down"].shape == (2, 2)
     q = inputs.make_problem(cfg, seed=1)
     assert torch.equal(p["w_up"], q["w_up"]) and torch.equal(p["hidden"], q["hidden"])
+    cfg = dict(dtype="w8a8", T=8, H=256, I=384, E=3, K=2, routing="uniform", shared_inter=256)
+    p = inputs.make_problem(cfg, seed=1)
+    assert p["hidden"].dtype == torch.int8 and p["hidden_scales"].shape == (8,)
+    assert p["w_gate"].dtype == torch.int8 and p["s_gate"].shape == (3, 384) and p["s_down"].shape == (3, 256)
+    assert p["sh_gate"].shape == (256, 256) and p["sh_s_gate"].shape == (256,) and p["sh_s_down"].shape == (256,)
 
 
 def test_workload_table():

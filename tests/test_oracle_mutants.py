@@ -33,6 +33,10 @@ MUTANTS = {
     "dispatch_inclusive": ("offsets[e + 1] = offsets[e] + counts[e];",
                            "offsets[e + 1] = offsets[e] + counts[e] + (e == 0);"),
     "row_of_skipped": ("row_of[f] = -1;", "row_of[f] = 0;"),
+    "i8_unsigned": ("return (double)(raw < 128 ? (int)raw : (int)raw - 256);", "return (double)raw;"),
+    "i8_scale_by_row": ("afd_oracle_i8_to_f64(((const uint8_t *)base)[i]) * (double)scales[c];",
+                        "afd_oracle_i8_to_f64(((const uint8_t *)base)[i]) * (double)scales[r % cols];"),
+    "i8_token_scale_dropped": ("(double)p->hidden_scales[t];", "1.0;"),
 }
 
 

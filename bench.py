@@ -35,12 +35,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3, "w8a8": 5033.2}  # w8a8: dense int8 TOP/s
 METRIC = "routed tokens/s per MoE layer on 1 MI355X; % of MFMA/HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GATE_UP_STAGE = 2  # stage index of the grouped GEMM gate/up + SwiGLU in the library's timing
 STAGE_STEPS = 20   # steps with every stage timed, after the timed steps, for the per-stage breakdown
-KERNEL_SOURCES = ("gemm.hip", "gemm_stream.h", "gemm_tiled.hip", "gemm_ring.hip", "afd_device.h", "afd_internal.h")
+KERNEL_SOURCES = ("gemm.hip", "gemm_stream.h", "gemm_tiled.hip", "gemm_ring.hip", "quant.hip", "afd_device.h",
+                  "afd_internal.h")
 
 
 def kernel_source_hash() -> str:
@@ -55,6 +56,9 @@ def gate_up_kernels(cfg: dict, t_mb: int) -> str:
     """Which launches make up the timed gate/up + SwiGLU stage (the library's tile policy)."""
     if cfg["dtype"] == "fp8":
         return "gate/up + SwiGLU stage: gemm_ring_kernel<true> (heavy and light tiles in one launch)"
+    if cfg["dtype"] == "w8a8":
+        return ("gate/up + SwiGLU stage: gemm_ring_kernel<true, int8> (heavy and light tiles in one launch), "
+                "then quant_rows_kernel (h to int8 per row)")
     if cfg["dtype"] == "f32":
         return "gate/up + SwiGLU stage: gemm_f32_kernel<true> (one launch)"
     if not cfg.get("shared_inter") and t_mb * cfg["K"] <= 32 * cfg["E"]:
@@ -73,7 +77,7 @@ def algorithmic_units(cfg: dict, ids) -> dict:
 
     T, H, I, E, K = cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["K"]
     dt = cfg["dtype"]
-    bw = {"f32": 4, "bf16": 2, "fp8": 1}[dt]
+    bw = {"f32": 4, "bf16": 2, "fp8": 1, "w8a8": 1}[dt]
     by = 4 if dt == "f32" else 2
     S = 1 if cfg.get("shared_inter") else 0
     ids = np.asarray(ids)
@@ -81,11 +85,17 @@ def algorithmic_units(cfg: dict, ids) -> dict:
     N = int(counts.sum())
     Ns = N + S * T
     ne = int((counts > 0).sum()) + S
-    sc = 4.0 / (128 * 128) if dt == "fp8" else 0.0          # weight block scales per weight
-    xs = 4.0 / 128 if dt == "fp8" else 0.0                  # activation scales per element
-    gu_bytes = ne * 2 * H * I * (bw + sc) + T * H * (bw + xs) + Ns * I * (bw + xs)
-    dn_bytes = ne * I * H * (bw + sc) + Ns * I * (bw + xs) + Ns * H * by
-    layer_bytes = ne * 3 * H * I * (bw + sc) + T * H * (bw + xs) + T * H * by + T * K * 8
+    # scales per weight and per activation element: block-FP8 one per 128 x 128
+    # weights and per 1 x 128 activations; W8A8 one per output channel (gate/up:
+    # per column of H weights, down: per column of I) and per token row
+    sc_gu = sc_dn = 4.0 / (128 * 128) if dt == "fp8" else 0.0
+    xs = hs = 4.0 / 128 if dt == "fp8" else 0.0
+    if dt == "w8a8":
+        sc_gu, sc_dn, xs, hs = 4.0 / H, 4.0 / I, 4.0 / H, 4.0 / I
+    gu_bytes = ne * 2 * H * I * (bw + sc_gu) + T * H * (bw + xs) + Ns * I * (bw + hs)
+    dn_bytes = ne * I * H * (bw + sc_dn) + Ns * I * (bw + hs) + Ns * H * by
+    layer_bytes = (ne * H * I * (2 * (bw + sc_gu) + bw + sc_dn) + T * H * (bw + xs) + T * H * by +
+                   T * K * 8)
     return dict(N=N, Ns=Ns, nonempty=ne, gu_bytes=gu_bytes, dn_bytes=dn_bytes, layer_bytes=layer_bytes,
                 gu_flops=4.0 * H * I * Ns, dn_flops=2.0 * H * I * Ns, layer_flops=6.0 * H * I * Ns)
 
@@ -179,7 +189,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_shared",
-                    choices=["tiny", "decode", "aggregated", "fp8_shared", "verify_shard"])
+                    choices=["tiny", "decode", "aggregated", "fp8_shared", "verify_shard", "w8a8_shared"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -374,7 +384,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3_block128", "f32": "f32"}[dt],
+        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3_block128", "f32": "f32", "w8a8": "int8_w8a8"}[dt],
         "data": "synthetic (seeded; random-init expert weights N(0,0.02), hidden N(0,1))",
         "config": {"workload": inputs.WORKLOAD_TITLES[args.workload], "T": T, "H": cfg["H"], "I": cfg["I"],
                    "E": cfg["E"], "top_k": cfg["K"], "shared_inter": cfg.get("shared_inter", 0),

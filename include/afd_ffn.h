@@ -57,10 +57,15 @@ typedef enum {
 typedef enum {
     AFD_DTYPE_F32 = 0,       /* fp32 activations, weights and output            */
     AFD_DTYPE_BF16 = 1,      /* bf16 activations, weights and output            */
-    AFD_DTYPE_FP8_BLOCK = 2  /* OCP E4M3FN codes with fp32 scales: activations
+    AFD_DTYPE_FP8_BLOCK = 2, /* OCP E4M3FN codes with fp32 scales: activations
                                 per 1x128 group along H, weights per 128x128
                                 block; output bf16 ("block-FP8" experts and FP8
                                 tokens, FastAFD System Design items 1-2)        */
+    AFD_DTYPE_W8A8 = 3       /* symmetric int8 codes with fp32 scales:
+                                activations one per token, weights one per output
+                                channel; int32 accumulation, h re-quantised per
+                                row, output bf16 (the "W8A8" experts of the vLLM
+                                AFD plugin blog's decode benchmark)             */
 } afd_dtype;
 
 /*
@@ -70,20 +75,23 @@ typedef enum {
  * Weights (device, read only during afd_ffn_create, which copies and
  * re-lays them out into library-owned memory; the caller may free them as
  * soon as create returns):
- *   w_gate, w_up  [E, H, I]   element type per dtype (fp32 | bf16 | e4m3 code)
+ *   w_gate, w_up  [E, H, I]   element type per dtype (fp32 | bf16 | e4m3 code | int8)
  *   w_down        [E, I, H]
- *   s_gate, s_up  [E, H/128, I/128] fp32   (AFD_DTYPE_FP8_BLOCK only, else NULL)
- *   s_down        [E, I/128, H/128] fp32   (AFD_DTYPE_FP8_BLOCK only, else NULL)
+ *   s_gate, s_up  [E, H/128, I/128] fp32 block scales (AFD_DTYPE_FP8_BLOCK),
+ *                 [E, I] fp32 per-column scales (AFD_DTYPE_W8A8), else NULL
+ *   s_down        [E, I/128, H/128] (AFD_DTYPE_FP8_BLOCK), [E, H] (AFD_DTYPE_W8A8),
+ *                 else NULL
  * Optional shared expert (shared_inter > 0; applied to every token with
  * weight 1 after the routed sum; shared_inter must equal inter):
  *   sh_gate, sh_up [H, shared_inter], sh_down [shared_inter, H], and for FP8
- *   sh_s_gate, sh_s_up [H/128, shared_inter/128], sh_s_down [shared_inter/128, H/128].
+ *   sh_s_gate, sh_s_up [H/128, shared_inter/128], sh_s_down [shared_inter/128, H/128]
+ *   (W8A8: sh_s_gate, sh_s_up [shared_inter], sh_s_down [H]).
  *
  * Alignment: bf16 and e4m3 weights 16-byte aligned, fp32 weights and all
  * scale arrays 4-byte aligned (otherwise AFD_ERR_INVALID_ARG).
  *
  * Limits: 1 <= E <= 512, 1 <= K <= 32, 1 <= max_tokens, max_tokens*K < 2^26;
- * H and I multiples of 128 for every dtype (block-FP8: at most 16384); the
+ * H and I multiples of 128 for every dtype (block-FP8 and W8A8: at most 16384); the
  * activation buffers (max_tokens*K (+ max_tokens with a shared expert) rows of
  * max(H, I) elements and of H bf16/fp32 outputs, and max_tokens rows of H)
  * below 2^31 - 2^24 bytes each.
@@ -135,8 +143,9 @@ afd_status afd_ffn_set_concurrency(afd_ffn_t *handle, int32_t streams);
 
 /*
  * One layer forward for T = num_tokens tokens (0 <= T <= max_tokens):
- *   hidden         device [T, H]: fp32 | bf16 | e4m3 codes (per dtype)
- *   hidden_scales  device [T, H/128] fp32 for AFD_DTYPE_FP8_BLOCK, else NULL
+ *   hidden         device [T, H]: fp32 | bf16 | e4m3 codes | int8 codes (per dtype)
+ *   hidden_scales  device fp32: [T, H/128] for AFD_DTYPE_FP8_BLOCK, [T] (one per
+ *                  token) for AFD_DTYPE_W8A8, else NULL
  *   topk_ids       device [T, K] int32; each in [0, E) or -1 ("expert not on
  *                  this GPU": contributes nothing).  Duplicate ids in a row
  *                  are separate assignments.  Ids outside [-1, E) are treated

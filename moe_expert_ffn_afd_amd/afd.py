@@ -20,10 +20,10 @@ import torch  # noqa: F401  (must precede loading the library: one HIP runtime)
 LIB_PATH = os.environ.get("AFD_FFN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libafd_ffn.so")
 
 AFD_OK, AFD_ERR_INVALID_ARG, AFD_ERR_UNSUPPORTED, AFD_ERR_OUT_OF_MEMORY, AFD_ERR_HIP, AFD_ERR_BAD_ROUTING = range(6)
-AFD_DTYPE_F32, AFD_DTYPE_BF16, AFD_DTYPE_FP8_BLOCK = 0, 1, 2
+AFD_DTYPE_F32, AFD_DTYPE_BF16, AFD_DTYPE_FP8_BLOCK, AFD_DTYPE_W8A8 = 0, 1, 2, 3
 AFD_NUM_STAGES = 5
 STAGE_NAMES = ("dispatch_count_scan", "dispatch_scatter", "gemm_gate_up_swiglu", "gemm_down", "combine")
-DTYPE_CODES = {"f32": AFD_DTYPE_F32, "bf16": AFD_DTYPE_BF16, "fp8": AFD_DTYPE_FP8_BLOCK}
+DTYPE_CODES = {"f32": AFD_DTYPE_F32, "bf16": AFD_DTYPE_BF16, "fp8": AFD_DTYPE_FP8_BLOCK, "w8a8": AFD_DTYPE_W8A8}
 
 EXPORTS = ("afd_ffn_validate_config", "afd_ffn_create", "afd_ffn_clone", "afd_ffn_forward",
            "afd_ffn_forward_noalloc",
@@ -198,7 +198,7 @@ def afd_ffn_get_timing(handle):
 
 def _check_inputs(layer, T, hidden, hidden_scales, ids, weights, out):
     """Host-side shape/dtype/device checks of the tensors behind the raw pointers."""
-    esz = {"f32": 4, "bf16": 2, "fp8": 1}[layer.dtype]
+    esz = {"f32": 4, "bf16": 2, "fp8": 1, "w8a8": 1}[layer.dtype]
     H, K = layer.H, layer.K
     def need(ok, what):
         if not ok:
@@ -210,11 +210,13 @@ def _check_inputs(layer, T, hidden, hidden_scales, ids, weights, out):
         need(tuple(t.shape) == shape, "%s shape %s != %s" % (name, tuple(t.shape), shape))
         need(t.is_contiguous() and t.element_size() == size, name + " must be contiguous with %d-byte elements" % size)
     need(ids.dtype == torch.int32 and weights.dtype == torch.float32, "ids int32 and weights float32")
-    if layer.dtype == "fp8":
-        need(hidden_scales is not None and tuple(hidden_scales.shape) == (T, H // 128) and
-             hidden_scales.dtype == torch.float32 and hidden_scales.is_contiguous(), "hidden_scales [T, H/128] fp32")
+    if layer.dtype in ("fp8", "w8a8"):
+        shape = (T, H // 128) if layer.dtype == "fp8" else (T,)
+        need(hidden_scales is not None and tuple(hidden_scales.shape) == shape and
+             hidden_scales.dtype == torch.float32 and hidden_scales.is_contiguous(),
+             "hidden_scales %s fp32" % ("[T, H/128]" if layer.dtype == "fp8" else "[T]"))
     else:
-        need(hidden_scales is None, "hidden_scales only for fp8")
+        need(hidden_scales is None, "hidden_scales only for fp8 and w8a8")
 
 
 class Layer:

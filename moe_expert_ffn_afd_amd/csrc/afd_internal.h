@@ -44,6 +44,12 @@
 //    hs  [I/128][N_max + T_max]       h's 1x128 scales
 //    y   [N_max + T_max, H]           expert outputs (unweighted), same rows;
 //                                     bf16 | fp32
+//  W8A8 layers (one scale per token and per output channel): h is bf16 as
+//  the gate/up GEMM writes it, then h8 [N_max + T_max, I] int8 codes with
+//  hs [N_max + T_max] one scale per row (quant.hip), xs [N_max + T_max] the
+//  caller's per-token hidden scales in sorted-row order, and
+//  pamax [I/128][N_max + T_max] each row's amax per 128-column task.  Weight
+//  scales are copied as gate, up [E+S][I] and down [E+S][H].
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -51,7 +57,7 @@
 
 namespace afd {
 
-enum Dtype : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+enum Dtype : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kW8A8 = 3 };
 
 constexpr int kPanelCols = 32;         // output columns per panel
 constexpr int kStepBytes = 128;        // bytes of K per super-step and row
@@ -147,6 +153,21 @@ struct GemmParams {
   int32_t c_scale_ld;
 };
 
+// W8A8: h (bf16) -> int8 codes with one scale per row (quant.hip)
+struct QuantParams {
+  const uint8_t* h;        // [ld rows][inter] bf16
+  const float* pamax;      // [inter / 128][ld]: each row's amax over each 128-column group
+  int32_t ld;              // rows of the buffers
+  int32_t inter;           // I
+  const int32_t* offsets;  // offsets[num_experts] = routed rows of this call
+  int32_t num_experts;
+  int32_t routed_max;      // T * K (upper bound of the routed rows)
+  int32_t shared_row0;     // first shared-expert row, -1 if none
+  int32_t shared_rows;     // T with a shared expert, else 0
+  int8_t* h8;              // [ld rows][inter] codes
+  float* hsc;              // [ld] per-row scales
+};
+
 struct ScaleGatherParams {
   const float* src;              // caller's hidden scales [T][ks]
   int32_t ks;                    // H / 128
@@ -206,10 +227,13 @@ int tiled_panels();         // weight panels of one LDS-tiled task
 // the heavy list (mtiles2, m-tiles of up to ring_rows(true) rows) and then the
 // light list (mtiles, up to ring_rows(false) rows)
 // stream_weights: weight copies non-temporal (no other forward runs beside this one)
-hipError_t launch_gemm_ring(bool gate_up, bool stream_weights, const GemmParams& p, int64_t max_tasks, int num_cus,
-                            hipStream_t s);
+// int8: W8A8 codes (int8 MFMA, int32 accumulation, per-token and per-channel
+// scales in the epilogue; gate/up writes bf16 h and per-row amax per task)
+hipError_t launch_gemm_ring(bool gate_up, bool stream_weights, bool int8, const GemmParams& p, int64_t max_tasks,
+                            int num_cus, hipStream_t s);
 int ring_rows(bool heavy);
 hipError_t launch_gemm_f32(bool gate_up, const F32Params& p, int grid, hipStream_t s);
+hipError_t launch_quant_rows(const QuantParams& p, hipStream_t s);
 hipError_t launch_combine(int dtype, const CombineParams& p, int tokens, hipStream_t s);
 hipError_t launch_pack(int dtype, bool gate_up, const void* w_first, const void* w_second,
                        int64_t expert_in_stride_elems, int experts, int kdim, int ndim,

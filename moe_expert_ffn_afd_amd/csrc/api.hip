@@ -69,7 +69,7 @@ int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 struct WeightStore {
   std::atomic<int> refs{1};
   int device = 0;
-  // bf16 / fp8: packed gate+up and down; f32: plain gate, up, down
+  // bf16 / fp8 / w8a8: packed gate+up and down; f32: plain gate, up, down
   uint8_t* gu = nullptr;
   uint8_t* up = nullptr;  // f32 only
   uint8_t* dn = nullptr;
@@ -78,7 +78,8 @@ struct WeightStore {
   float* sd = nullptr;
   int64_t gu_expert_bytes = 0, dn_expert_bytes = 0;
   int64_t gu_panel_bytes = 0, dn_panel_bytes = 0;
-  int64_t scale_bytes = 0;  // fp8: bytes of each of sg, su, sd
+  int64_t scale_bytes = 0;     // block-FP8: bytes of each of sg, su, sd; W8A8: of sg and su
+  int64_t dn_scale_bytes = 0;  // bytes of sd
   ~WeightStore() {
     for (void* p : {(void*)gu, (void*)up, (void*)dn, (void*)sg, (void*)su, (void*)sd})
       if (p) (void)hipFree(p);
@@ -126,9 +127,11 @@ struct Workspace {
   int32_t *chunk_base = nullptr, *sorted_assign = nullptr, *row_of = nullptr;
   int4* mtiles = nullptr;
   int4* mtiles_heavy = nullptr;
-  uint8_t* h = nullptr;
-  float* h_scales = nullptr;  // FP8: [I/128][h_rows] step-major
-  float* x_scales = nullptr;  // FP8: [H/128][h_rows] hidden scales in sorted-row order
+  uint8_t* h = nullptr;       // bf16 | e4m3 | fp32 (W8A8: bf16, before re-quantisation)
+  float* h_scales = nullptr;  // FP8: [I/128][h_rows] step-major; W8A8: [h_rows]
+  float* x_scales = nullptr;  // FP8: [H/128][h_rows] hidden scales in sorted-row order; W8A8: [h_rows]
+  uint8_t* h8 = nullptr;      // W8A8: [h_rows, I] int8 codes of h
+  float* pamax = nullptr;     // W8A8: [I/128][h_rows] per-row amax of each gate/up task's columns
   uint8_t* y = nullptr;
   int64_t nmax = 0;    // routed-row capacity tcap * K; the shared expert's rows start here
   int64_t h_rows = 0;  // rows of h and y: nmax (+ tcap with a shared expert)
@@ -161,13 +164,15 @@ int chunk_shift_for(int64_t n_flat, int E) {
 
 afd_status check_config(const afd_ffn_config* c) {
   if (!c) return fail(AFD_ERR_INVALID_ARG, "config is NULL");
-  if (c->dtype < 0 || c->dtype > 2) return fail(AFD_ERR_UNSUPPORTED, "unknown dtype %d", c->dtype);
+  if (c->dtype < 0 || c->dtype > 3) return fail(AFD_ERR_UNSUPPORTED, "unknown dtype %d", c->dtype);
   if (c->hidden <= 0 || c->inter <= 0 || c->num_experts <= 0 || c->top_k <= 0 || c->max_tokens <= 0)
     return fail(AFD_ERR_INVALID_ARG, "hidden, inter, num_experts, top_k and max_tokens must be positive");
   if (c->hidden % 128 || c->inter % 128)
     return fail(AFD_ERR_UNSUPPORTED, "hidden (%d) and inter (%d) must be multiples of 128", c->hidden, c->inter);
   if (c->dtype == kFP8 && (c->hidden > 16384 || c->inter > 16384))
     return fail(AFD_ERR_UNSUPPORTED, "block-FP8 reductions are limited to 128 blocks (hidden, inter <= 16384)");
+  if (c->dtype == kW8A8 && (c->hidden > 16384 || c->inter > 16384))
+    return fail(AFD_ERR_UNSUPPORTED, "W8A8 reductions are limited to 16384 (int32 accumulation)");
   if (c->num_experts > kMaxExperts) return fail(AFD_ERR_UNSUPPORTED, "num_experts %d > %d", c->num_experts, kMaxExperts);
   if (c->top_k > kMaxTopK) return fail(AFD_ERR_UNSUPPORTED, "top_k %d > %d", c->top_k, kMaxTopK);
   if ((int64_t)c->max_tokens * c->top_k >= (1ll << 26))
@@ -180,17 +185,18 @@ afd_status check_config(const afd_ffn_config* c) {
     const int64_t rows = (int64_t)c->max_tokens * c->top_k + (c->shared_inter > 0 ? c->max_tokens : 0);
     const int64_t lim = (1ll << 31) - (1ll << 24);
     const int64_t ys = c->dtype == kF32 ? 4 : 2;  // expert outputs y are bf16 | fp32
+    const int64_t hs = c->dtype == kW8A8 ? 2 : es;  // W8A8 keeps h in bf16 before re-quantising it
     if (rows * std::max(c->hidden, c->inter) * es > lim || (int64_t)c->max_tokens * c->hidden * es > lim ||
-        rows * c->hidden * ys > lim)
+        rows * c->hidden * ys > lim || rows * c->inter * hs > lim)
       return fail(AFD_ERR_UNSUPPORTED, "activation buffers of max_tokens=%d exceed 2 GiB", c->max_tokens);
   }
   if (c->device < 0) return fail(AFD_ERR_INVALID_ARG, "device must be >= 0");
   if (!c->w_gate || !c->w_up || !c->w_down) return fail(AFD_ERR_INVALID_ARG, "weight pointer is NULL");
-  const bool fp8 = c->dtype == kFP8;
+  const bool fp8 = c->dtype == kFP8 || c->dtype == kW8A8;  // 8-bit codes with fp32 scales
   if (fp8 && (!c->s_gate || !c->s_up || !c->s_down))
-    return fail(AFD_ERR_INVALID_ARG, "block-FP8 weights need s_gate, s_up and s_down");
+    return fail(AFD_ERR_INVALID_ARG, "block-FP8 and W8A8 weights need s_gate, s_up and s_down");
   if (!fp8 && (c->s_gate || c->s_up || c->s_down))
-    return fail(AFD_ERR_INVALID_ARG, "weight scales are only used with AFD_DTYPE_FP8_BLOCK");
+    return fail(AFD_ERR_INVALID_ARG, "weight scales are only used with AFD_DTYPE_FP8_BLOCK and AFD_DTYPE_W8A8");
   auto mis = [](const void* q, uintptr_t a) { return q && (reinterpret_cast<uintptr_t>(q) & (a - 1)); };
   {
     // bf16 / e4m3 weights are packed with 16-byte vector loads; fp32 ones are copied
@@ -219,14 +225,17 @@ int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w
   const int64_t max_mtiles = nmax / 32 + a->E + (a->S ? (tcap + 31) / 32 : 0) + 1;
   const int es = esize_of(a->dtype);
   const int ys = a->dtype == kF32 ? 4 : 2;
+  const bool w8 = a->dtype == kW8A8;
   int64_t off = 0;
   auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + bytes, 256); return o; };
   const int64_t o_counts = take(4ll * a->E), o_offsets = take(4ll * (a->E + 1)), o_err = take(4),
                 o_nmt = take(16), o_cb = take(4ll * max_chunks * a->E), o_sa = take(4 * nmax),
                 o_ro = take(4 * nmax), o_mt = take(16ll * max_mtiles), o_mth = take(16ll * max_mtiles),
-                o_h = take(rows * a->I * es),
-                o_hs = take(a->dtype == kFP8 ? rows * (a->I / 128) * 4 : 0),
-                o_xs = take(a->dtype == kFP8 ? rows * (a->H / 128) * 4 : 0), o_y = take(rows * a->H * ys);
+                o_h = take(rows * a->I * (w8 ? 2 : es)),
+                o_hs = take(a->dtype == kFP8 ? rows * (a->I / 128) * 4 : w8 ? rows * 4 : 0),
+                o_xs = take(a->dtype == kFP8 ? rows * (a->H / 128) * 4 : w8 ? rows * 4 : 0),
+                o_h8 = take(w8 ? rows * a->I : 0), o_pm = take(w8 ? rows * (a->I / 128) * 4 : 0),
+                o_y = take(rows * a->H * ys);
   if (base && w) {
     w->counts = (int32_t*)(base + o_counts);
     w->offsets = (int32_t*)(base + o_offsets);
@@ -238,8 +247,11 @@ int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w
     w->mtiles = (int4*)(base + o_mt);
     w->mtiles_heavy = (int4*)(base + o_mth);
     w->h = base + o_h;
-    w->h_scales = a->dtype == kFP8 ? (float*)(base + o_hs) : nullptr;
-    w->x_scales = a->dtype == kFP8 ? (float*)(base + o_xs) : nullptr;
+    const bool sc = a->dtype == kFP8 || w8;
+    w->h_scales = sc ? (float*)(base + o_hs) : nullptr;
+    w->x_scales = sc ? (float*)(base + o_xs) : nullptr;
+    w->h8 = w8 ? base + o_h8 : nullptr;
+    w->pamax = w8 ? (float*)(base + o_pm) : nullptr;
     w->y = base + o_y;
     w->nmax = nmax;
     w->h_rows = rows;
@@ -301,12 +313,29 @@ afd_status pack_weights(const afd_ffn_config* c, afd_ffn* a) {
     AFD_HIP(launch_pack(dt, false, c->sh_down, nullptr, (int64_t)I * H, 1, I, H, w->dn + w->dn_expert_bytes * E,
                         w->dn_expert_bytes, 0));
   }
+  if (dt == kW8A8) {
+    // per output channel: gate, up [E+S][I], down [E+S][H]
+    const int64_t sgu = (int64_t)I * 4, sdn = (int64_t)H * 4;
+    if ((st = mal((uint8_t**)&w->sg, sgu * ES)) || (st = mal((uint8_t**)&w->su, sgu * ES)) ||
+        (st = mal((uint8_t**)&w->sd, sdn * ES)))
+      return st;
+    w->scale_bytes = sgu * ES;
+    w->dn_scale_bytes = sdn * ES;
+    AFD_HIP(hipMemcpy(w->sg, c->s_gate, sgu * E, hipMemcpyDeviceToDevice));
+    AFD_HIP(hipMemcpy(w->su, c->s_up, sgu * E, hipMemcpyDeviceToDevice));
+    AFD_HIP(hipMemcpy(w->sd, c->s_down, sdn * E, hipMemcpyDeviceToDevice));
+    if (a->S) {
+      AFD_HIP(hipMemcpy((uint8_t*)w->sg + sgu * E, c->sh_s_gate, sgu, hipMemcpyDeviceToDevice));
+      AFD_HIP(hipMemcpy((uint8_t*)w->su + sgu * E, c->sh_s_up, sgu, hipMemcpyDeviceToDevice));
+      AFD_HIP(hipMemcpy((uint8_t*)w->sd + sdn * E, c->sh_s_down, sdn, hipMemcpyDeviceToDevice));
+    }
+  }
   if (dt == kFP8) {
     const int64_t sblk = (int64_t)(H / 128) * (I / 128) * 4;
     if ((st = mal((uint8_t**)&w->sg, sblk * ES)) || (st = mal((uint8_t**)&w->su, sblk * ES)) ||
         (st = mal((uint8_t**)&w->sd, sblk * ES)))
       return st;
-    w->scale_bytes = sblk * ES;
+    w->scale_bytes = w->dn_scale_bytes = sblk * ES;
     AFD_HIP(hipMemcpy(w->sg, c->s_gate, sblk * E, hipMemcpyDeviceToDevice));
     AFD_HIP(hipMemcpy(w->su, c->s_up, sblk * E, hipMemcpyDeviceToDevice));
     AFD_HIP(hipMemcpy(w->sd, c->s_down, sblk * E, hipMemcpyDeviceToDevice));
@@ -350,10 +379,11 @@ afd_status check_forward_args(const afd_ffn* a, int32_t T, int64_t tcap, const v
   if (T < 0 || T > tcap) return fail(AFD_ERR_INVALID_ARG, "num_tokens %d outside [0, %lld]", T, (long long)tcap);
   if (T > 0 && (!hidden || !topk_ids || !topk_weights || !out))
     return fail(AFD_ERR_INVALID_ARG, "hidden, topk_ids, topk_weights and out must be non-NULL");
-  if (a->dtype == kFP8 && T > 0 && !hidden_scales)
-    return fail(AFD_ERR_INVALID_ARG, "block-FP8 input needs hidden_scales");
-  if (a->dtype != kFP8 && hidden_scales)
-    return fail(AFD_ERR_INVALID_ARG, "hidden_scales is only used with AFD_DTYPE_FP8_BLOCK");
+  const bool scaled = a->dtype == kFP8 || a->dtype == kW8A8;
+  if (scaled && T > 0 && !hidden_scales)
+    return fail(AFD_ERR_INVALID_ARG, "block-FP8 and W8A8 input needs hidden_scales");
+  if (!scaled && hidden_scales)
+    return fail(AFD_ERR_INVALID_ARG, "hidden_scales is only used with AFD_DTYPE_FP8_BLOCK and AFD_DTYPE_W8A8");
   auto mis = [](const void* q, uintptr_t al) { return q && (reinterpret_cast<uintptr_t>(q) & (al - 1)); };
   if (mis(hidden, 16) || mis(out, 16)) return fail(AFD_ERR_INVALID_ARG, "hidden and out must be 16-byte aligned");
   if (mis(hidden_scales, 4) || mis(topk_ids, 4) || mis(topk_weights, 4))
@@ -378,12 +408,13 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, int32_t T, c
   // weights through registers (gemm_stream.h), heavy ones take the LDS-tiled
   // GEMM (gemm_tiled.hip), which fetches each weight panel once per tile of
   // tiled_rows() rows; one mixed launch runs both, on disjoint CUs.
-  // Block-FP8: both lists run the weight-ring GEMM (gemm_ring.hip), light
-  // tiles (<= 64 rows) and heavy tiles of ring_rows(true) rows.  fp32 uses
-  // light tiles of 32 rows only.
+  // Block-FP8 and W8A8: both lists run the weight-ring GEMM (gemm_ring.hip),
+  // light tiles (<= 64 rows) and heavy tiles of ring_rows(true) rows.  fp32
+  // uses light tiles of 32 rows only.
   const int mr = dt == kF32 ? 1 : (n_flat <= 32ll * E ? 1 : 2);
   const int bm = 32 * mr;
-  const bool fp8 = dt == kFP8;
+  const bool w8 = dt == kW8A8;
+  const bool fp8 = dt == kFP8 || w8;  // 8-bit codes: the ring GEMM
   const int bm_heavy = dt == kF32 ? bm : fp8 ? ring_rows(true) : tiled_rows(dt);
   // fp32 runs the light list only.  bf16 batches (no shared expert) of at
   // most 32 rows per expert on average usually need no heavy list either:
@@ -452,10 +483,12 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, int32_t T, c
     return AFD_OK;
   }
   AFD_HIP(launch_dispatch_scatter(d, s));
-  if (dt == kFP8) {
+  if (fp8) {
+    // the hidden rows' scales in sorted-row order: block-FP8 one per 128
+    // columns (step-major), W8A8 one per token
     ScaleGatherParams sg{};
     sg.src = hidden_scales;
-    sg.ks = H / 128;
+    sg.ks = w8 ? 1 : H / 128;
     sg.tokens = T;
     sg.top_k = K;
     sg.sorted_assign = w.sorted_assign;
@@ -472,7 +505,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, int32_t T, c
   // upper bounds of the routed + shared m-tiles of this call, per list
   const int64_t mt_bound = n_flat / bm + std::min<int64_t>(E, n_flat) + (a->S ? (T + bm - 1) / bm : 0) + 1;
   const int64_t mth_bound = light_only ? 0 : n_flat / heavy_min + (a->S ? (T + bm_heavy - 1) / bm_heavy : 0) + 1;
-  const int64_t rows_ld_h = (int64_t)I * esize_of(dt);
+  const int64_t rows_ld_h = (int64_t)I * (w8 ? 2 : esize_of(dt));  // W8A8: bf16 h before re-quantisation
   const int64_t h_rows = w.h_rows;
   const int occupancy_wgs = 4;  // resident workgroups per CU the persistent grids aim for
 
@@ -517,7 +550,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, int32_t T, c
     g.a_bytes = (int64_t)T * H * es;
     g.a_row_bytes = (int64_t)H * es;
     g.a_scales = w.x_scales;  // gathered by gather_scales_kernel
-    g.a_scale_bytes = fp8 ? (int64_t)(H / 128) * w.h_rows * 4 : 0;
+    g.a_scale_bytes = fp8 ? (int64_t)(w8 ? 1 : H / 128) * w.h_rows * 4 : 0;
     g.a_scale_ld = (int32_t)w.h_rows;
     g.b = a->w->gu;
     g.b_expert_bytes = a->w->gu_expert_bytes;
@@ -526,34 +559,35 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, int32_t T, c
     g.b_scale_bytes = a->w->scale_bytes;
     g.b_scales1 = a->w->su;
     g.b_scale_rows = H / 128;
-    g.b_scale_cols = I / 128;
+    g.b_scale_cols = w8 ? I : I / 128;  // W8A8: per output channel
     g.k_steps = (int32_t)((int64_t)H * es / kStepBytes);
     g.n_panels = I / 32;
     g.n_groups = I / 128;
     g.c = w.h;
     g.c_row_bytes = rows_ld_h;
-    g.c_scales = w.h_scales;
+    g.c_scales = w8 ? w.pamax : w.h_scales;  // W8A8: each row's amax per task, for quant.hip
     g.c_scale_ld = (int32_t)w.h_rows;
     GemmParams gu_light = g;
     GemmParams gu_heavy = g;
     gu_heavy.mtiles = w.mtiles_heavy;
     gu_heavy.num_mtiles = w.num_mtiles + 1;
     gu_heavy.n_groups = (2 * I / 32 + tiled_panels() - 1) / tiled_panels();  // bf16 only
-    // down: A = h rows in sorted order
+    // down: A = h rows in sorted order (W8A8: their int8 codes)
     g.gather = 0;
-    g.a = w.h;
-    g.a_bytes = h_rows * rows_ld_h;
-    g.a_row_bytes = rows_ld_h;
+    g.a = w8 ? w.h8 : w.h;
+    g.a_bytes = h_rows * (w8 ? I : rows_ld_h);
+    g.a_row_bytes = w8 ? I : rows_ld_h;
     g.a_scales = w.h_scales;
-    g.a_scale_bytes = fp8 ? h_rows * (I / 128) * 4 : 0;
+    g.a_scale_bytes = fp8 ? h_rows * (w8 ? 1 : I / 128) * 4 : 0;
     g.a_scale_ld = (int32_t)w.h_rows;
     g.b = a->w->dn;
     g.b_expert_bytes = a->w->dn_expert_bytes;
     g.b_panel_bytes = a->w->dn_panel_bytes;
     g.b_scales0 = a->w->sd;
     g.b_scales1 = a->w->sd;
+    g.b_scale_bytes = a->w->dn_scale_bytes;
     g.b_scale_rows = I / 128;
-    g.b_scale_cols = H / 128;
+    g.b_scale_cols = w8 ? H : H / 128;
     g.k_steps = (int32_t)((int64_t)I * es / kStepBytes);
     g.n_panels = H / 32;
     // light tasks of the down GEMM: down_panels_per_task(mr) H panels (bf16
@@ -583,7 +617,8 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, int32_t T, c
         GemmParams both = light;
         both.mtiles2 = heavy.mtiles;
         both.num_mtiles2 = heavy.num_mtiles;
-        return launch_gemm_ring(gate_up, a->concurrency == 1, both, (mt_bound + mth_bound) * light.n_groups, cus, s);
+        return launch_gemm_ring(gate_up, a->concurrency == 1, w8, both, (mt_bound + mth_bound) * light.n_groups,
+                                cus, s);
       }
       if (auto_launch) {
         GemmParams lo = light, mx = light;
@@ -597,6 +632,22 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, int32_t T, c
       return launch_gemm_mixed(gate_up, mr, heavy, light, cus, s);
     };
     AFD_HIP(stage(true, gu_light, gu_heavy));
+    if (w8) {
+      // h -> int8 codes with one scale per row, for the down GEMM
+      QuantParams qp{};
+      qp.h = w.h;
+      qp.pamax = w.pamax;
+      qp.ld = (int32_t)w.h_rows;
+      qp.inter = I;
+      qp.offsets = w.offsets;
+      qp.num_experts = E;
+      qp.routed_max = (int32_t)n_flat;
+      qp.shared_row0 = a->S ? (int32_t)nmax : -1;
+      qp.shared_rows = a->S ? T : 0;
+      qp.h8 = (int8_t*)w.h8;
+      qp.hsc = w.h_scales;
+      AFD_HIP(launch_quant_rows(qp, s));
+    }
     if ((st = mark(3))) return st;
     AFD_HIP(stage(false, dn_light, dn_heavy));
     if ((st = mark(4))) return st;

@@ -46,7 +46,17 @@
 // into the accumulator times (token scale x block scale).  Eight waves, two per
 // SIMD, as WM x WN = (BM / 16) x (8 / (BM / 16)): each wave owns 16 rows and
 // 8 / WN panels (8 x 1 for 128-row tiles, 4 x 2 for 64-row tiles).
+//
+// W8A8 layers (I8) run the same ring on int8 codes: each lane's 32 bytes of a
+// step feed two int8 MFMAs 16x16x64 (its first and its second 16 bytes, in
+// both operands, so every product pairs the same k), accumulated exactly in
+// int32 over the whole reduction.  The scales are per token and per output
+// channel, so they are applied once, in the epilogue: the task's last step
+// carries them in its slot (the tile's row scales, the task's column scales).
+// The gate/up epilogue stores h in bf16 with its per-row amax over the task's
+// 128 columns; quant.hip turns that into int8 h with one scale per row.
 #include <algorithm>
+#include <type_traits>
 
 #include "afd_device.h"
 
@@ -122,7 +132,7 @@ struct RingDesc {
 // Every task rank + k * stride (k = 0, 1, ...) below n_tiles x n_groups of one
 // m-tile list, in one continuous pipeline.  Every wave of the workgroup calls
 // it with the same arguments.
-template <bool GATEUP, int BM, bool WNT>
+template <bool GATEUP, int BM, bool WNT, bool I8>
 __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles, const int n_tiles,
                                           const int first, const int stride) {
   // declared here, not passed in: the copies need pointers known to be in LDS
@@ -200,19 +210,25 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
     }
     if (scopy == 0)  // lane i: rows 4i .. 4i+3 of the tile's run in a step
       d.svoff = (valid && 4 * lane < BM) ? (d.row0 + 4 * lane) * 4 : soob;
-    else             // lane 0: one block scale of the step (row c of the expert's block grid)
+    else if (!I8)    // lane 0: one block scale of the step (row c of the expert's block grid)
       d.svoff = (valid && scopy > 0 && lane == 0) ? (d.expert * wsb + (GATEUP ? q : 2 * q + (scopy - 1))) * 4 : soob;
+    else if (GATEUP) // I8 gate/up: lane i < 32: gate (wave 1) or up (wave 2) scales of columns 128q + 4i ..
+      d.svoff = (valid && scopy > 0 && lane < 32) ? (d.expert * p.b_scale_cols + 128 * q + 4 * lane) * 4 : soob;
+    else             // I8 down: wave 1, lane i: scales of columns 256q + 4i .. (wave 2 copies nothing)
+      d.svoff = (valid && scopy == 1) ? (d.expert * p.b_scale_cols + 256 * q + 4 * lane) * 4 : soob;
     return d;
   };
 
   i32x4 areg[NS][RT][2];
-  f32x4 acc[RT][2 * NPW];
+  // fp32 accumulators (block-FP8, scaled per step) or int32 (W8A8, exact)
+  typedef typename std::conditional<I8, i32x4, f32x4>::type acc_t;
+  acc_t acc[RT][2 * NPW];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int b = 0; b < 2 * NPW; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[rt][b][r] = 0.0f;
+      for (int r = 0; r < 4; ++r) acc[rt][b][r] = 0;
 
   // step s of the current task into ring slot `slot` and register stage
   // `slot`; s >= nsr: step s - nsr of the next task
@@ -237,11 +253,19 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
       areg[slot][rt][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff, in ? c * kStepBytes : oobA, 0);
       areg[slot][rt][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff, in ? c * kStepBytes + 16 : oobA, 0);
     }
-    dma16(rs, scopy >= 0 ? st + S_OFF + scopy * 1024 : ring + kRingSinkOff, nx ? nxt.svoff : cur.svoff,
-          in ? c * sstep : soob);
+    // block-FP8: every step's scales; W8A8: the task's scales, with its last
+    // step run (slot NS - 1, still intact when the epilogue reads it).  (The
+    // block-FP8 offset stays inside the call: computed ahead as a variable, it
+    // made the compiler spill that kernel's registers.)
+    if constexpr (I8)
+      dma16(rs, scopy >= 0 ? st + S_OFF + scopy * 1024 : ring + kRingSinkOff, nx ? nxt.svoff : cur.svoff,
+            (!nx && c == nsr - 1) ? 0 : soob);
+    else
+      dma16(rs, scopy >= 0 ? st + S_OFF + scopy * 1024 : ring + kRingSinkOff, nx ? nxt.svoff : cur.svoff,
+            in ? c * sstep : soob);
   };
 
-  auto compute = [&](int slot) {
+  auto compute_fp8 = [&](int slot) {
     const uint8_t* Bs = ring + slot * SLOT;
     const float* S = reinterpret_cast<const float*>(Bs + S_OFF);
     float sa[RT];
@@ -288,9 +312,42 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
     }
   };
 
+  auto compute_i8 = [&](int slot) {
+    const uint8_t* Bs = ring + slot * SLOT;
+      // two int8 MFMAs per 32 bytes of k: the first and the second 16 bytes of
+      // both operands
+      const int g = kg >> 1, j0 = (kg & 1) * 2;
+#pragma unroll
+      for (int pp = 0; pp < NPW; ++pp) {
+        i32x4 wlo[2], whi[2];
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          const uint8_t* lo = Bs + (wn * NPW + pp) * kStepPanelBytes + j0 * 1024 + (16 * sh + tok + 32 * g) * 16;
+          wlo[sh] = *reinterpret_cast<const i32x4*>(lo);
+          whi[sh] = *reinterpret_cast<const i32x4*>(lo + 1024);
+        }
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            acc[rt][pp * 2 + sh] =
+                __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo[sh], areg[slot][rt][0], acc[rt][pp * 2 + sh], 0, 0, 0);
+            acc[rt][pp * 2 + sh] =
+                __builtin_amdgcn_mfma_i32_16x16x64_i8(whi[sh], areg[slot][rt][1], acc[rt][pp * 2 + sh], 0, 0, 0);
+          }
+      }
+  };
+
+  auto compute = [&](int slot) {
+    if constexpr (I8)
+      compute_i8(slot);
+    else
+      compute_fp8(slot);
+  };
+
   // The task's outputs.  Its barriers are the ring's kind (LDS only): the
   // next task's copies stay in flight.
-  auto epilogue = [&](const RingDesc& d) {
+  auto epilogue_fp8 = [&](const RingDesc& d) {
     const int row0 = d.row0, rows = d.rows, q = d.q;
     if constexpr (GATEUP) {
       // h of unit u = 4q + (wn NPW + pp) / 2 (pp even: gate, pp + 1: up), per
@@ -385,6 +442,111 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
         for (int r = 0; r < 4; ++r) acc[rt][b][r] = 0.0f;
   };
 
+  // W8A8: the task's outputs from exact int32 sums.  Its scales came with its
+  // last step (slot NS - 1): row m at Sx[m]; gate/up: the gate and up scales
+  // of the task's h column c at Sc0[c], Sc1[c]; down: output column c of the
+  // task at Sc0[c].  Gate/up stores h in bf16 and each row's amax over the
+  // task's 128 columns (quant.hip re-quantises h per row from those).
+  auto epilogue_i8 = [&](const RingDesc& d) {
+    const int row0 = d.row0, rows = d.rows, q = d.q;
+    const float* Sx = reinterpret_cast<const float*>(ring + (NS - 1) * SLOT + S_OFF);
+    const float* Sc0 = reinterpret_cast<const float*>(ring + (NS - 1) * SLOT + S_OFF + 1024);
+    const float* Sc1 = reinterpret_cast<const float*>(ring + (NS - 1) * SLOT + S_OFF + 2048);
+    const bool odd = (kg & 1) != 0;
+    // lane pairs (kg, kg ^ 1) of a token swap one half each, so every lane
+    // stores 8 consecutive bf16 columns (16 bytes) from column 32 * unit
+    auto store_pair = [&](uint8_t* orow, const int unit, const float (&v)[2][4], const bool nt) {
+      uint2 o0, o1;
+      o0.x = pack_bf16x2(v[0][0], v[0][1]);
+      o0.y = pack_bf16x2(v[0][2], v[0][3]);
+      o1.x = pack_bf16x2(v[1][0], v[1][1]);
+      o1.y = pack_bf16x2(v[1][2], v[1][3]);
+      const uint2 snd = odd ? o0 : o1;
+      uint2 rcv;
+      rcv.x = __shfl_xor(snd.x, 16, 64);
+      rcv.y = __shfl_xor(snd.y, 16, 64);
+      const uint4 w = odd ? make_uint4(rcv.x, rcv.y, o1.x, o1.y) : make_uint4(o0.x, o0.y, rcv.x, rcv.y);
+      uint8_t* dst = orow + (int64_t)(odd ? 32 * unit + 16 + 4 * (kg - 1) : 32 * unit + 4 * kg) * 2;
+      if (nt)
+        store16<true>(dst, w);
+      else
+        store16(dst, w);
+    };
+    if constexpr (GATEUP) {
+      float h[RT][NPW / 2][2][4];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float sx = Sx[wm * WR + rt * 16 + tok];
+        float a = 0.0f;
+#pragma unroll
+        for (int u = 0; u < NPW / 2; ++u)
+#pragma unroll
+          for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const int c = 32 * ((wn * NPW) / 2 + u) + 16 * sh + 4 * kg + r4;
+              const float v = silu_mul((float)acc[rt][4 * u + sh][r4] * sx * Sc0[c],
+                                       (float)acc[rt][4 * u + 2 + sh][r4] * sx * Sc1[c]);
+              h[rt][u][sh][r4] = v;
+              a = fmaxf(a, fabsf(v));
+            }
+        a = fmaxf(a, __shfl_xor(a, 16, 64));
+        a = fmaxf(a, __shfl_xor(a, 32, 64));
+        if (kg == 0) red[(wm * WN + wn) * 32 + rt * 16 + tok] = a;
+      }
+      lds_reads_done();
+      raw_barrier();
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int mi = rt * 16 + tok;
+        const int m = wm * WR + mi;
+        float amax = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, red[(wm * WN + w2) * 32 + mi]);
+        if (m >= rows) continue;
+        uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes;
+#pragma unroll
+        for (int u = 0; u < NPW / 2; ++u) store_pair(orow, 4 * q + (wn * NPW) / 2 + u, h[rt][u], false);
+        if (wn == 0 && kg == 0) p.c_scales[(int64_t)q * p.c_scale_ld + row0 + m] = amax;
+      }
+      lds_reads_done();
+      raw_barrier();  // red[] is rewritten by the next task
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int m = wm * WR + rt * 16 + tok;
+        if (m >= rows) continue;
+        uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes;
+        const float sx = Sx[m];
+#pragma unroll
+        for (int pp = 0; pp < NPW; ++pp) {
+          const int P = q * kRingPanels + wn * NPW + pp;
+          if (P >= p.n_panels) continue;
+          float v[2][4];
+#pragma unroll
+          for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+              v[sh][r4] = (float)acc[rt][pp * 2 + sh][r4] * sx * Sc0[32 * (wn * NPW + pp) + 16 * sh + 4 * kg + r4];
+          store_pair(orow, P, v, true);
+        }
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int b = 0; b < 2 * NPW; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[rt][b][r] = 0;
+  };
+
+  auto epilogue = [&](const RingDesc& d) {
+    if constexpr (I8)
+      epilogue_i8(d);
+    else
+      epilogue_fp8(d);
+  };
+
   // The row sources of a task are copied two tasks ahead into alternating
   // buffers, so the descriptor of the next task can be built when the current
   // one starts, from data that landed behind the previous task's waits.  The
@@ -460,7 +622,7 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
 // has one tail instead of two.  A workgroup runs tasks rank, rank + G, ... of
 // the two lists in a row; ranks are renumbered so that each XCD owns a
 // contiguous run of tasks (shared rows stay in its L2).
-template <bool GATEUP, bool WNT>
+template <bool GATEUP, bool WNT, bool I8>
 __global__ __launch_bounds__(kRingWaves * 64, 1) void gemm_ring_kernel(GemmParams p) {
   const int nq = p.n_groups;
   const int nh = uniform(p.num_mtiles2 ? p.num_mtiles2[0] : 0);
@@ -469,42 +631,49 @@ __global__ __launch_bounds__(kRingWaves * 64, 1) void gemm_ring_kernel(GemmParam
   const int G = gridDim.x;
   const int rank = (AFD_RING_XCD_REMAP && G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds
                                                           : blockIdx.x;
-  if (nh > 0) ring_list<GATEUP, 128, WNT>(p, p.mtiles2, nh, rank, G);
+  if (nh > 0) ring_list<GATEUP, 128, WNT, I8>(p, p.mtiles2, nh, rank, G);
   // this workgroup's first task past the heavy list, as an index into the light list
   const int first_l = rank >= th ? rank - th : rank + (th - rank + G - 1) / G * G - th;
-  ring_list<GATEUP, 64, WNT>(p, p.mtiles, nl, first_l, G);
+  ring_list<GATEUP, 64, WNT, I8>(p, p.mtiles, nl, first_l, G);
 }
 
-template <bool GATEUP, bool WNT>
+template <bool GATEUP, bool WNT, bool I8>
 static hipError_t launch_ring_one(const GemmParams& p, int64_t max_tasks, int num_cus, hipStream_t s) {
   constexpr int lds = kRingLdsBytes;
   static int per_cu = 0;
   if (per_cu == 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_ring_kernel<GATEUP, WNT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_ring_kernel<GATEUP, WNT, I8>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_ring_kernel<GATEUP, WNT>, kRingWaves * 64, lds) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_ring_kernel<GATEUP, WNT, I8>, kRingWaves * 64,
+                                                     lds) != hipSuccess ||
         occ <= 0)
       occ = 1;
     per_cu = occ;
   }
   const int64_t grid = std::min<int64_t>(max_tasks, (int64_t)num_cus * per_cu);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_ring_kernel<GATEUP, WNT>), dim3((unsigned)grid), dim3(kRingWaves * 64), lds, s, p);
+  hipLaunchKernelGGL((gemm_ring_kernel<GATEUP, WNT, I8>), dim3((unsigned)grid), dim3(kRingWaves * 64), lds, s, p);
   return hipGetLastError();
 }
 
 int ring_rows(bool heavy) { return heavy ? 128 : 64; }
 
-hipError_t launch_gemm_ring(bool gate_up, bool stream_weights, const GemmParams& p, int64_t max_tasks, int num_cus,
-                            hipStream_t s) {
+template <bool I8>
+static hipError_t launch_ring_fmt(bool gate_up, bool stream_weights, const GemmParams& p, int64_t max_tasks,
+                                  int num_cus, hipStream_t s) {
   if (stream_weights)
-    return gate_up ? launch_ring_one<true, true>(p, max_tasks, num_cus, s)
-                   : launch_ring_one<false, true>(p, max_tasks, num_cus, s);
-  return gate_up ? launch_ring_one<true, false>(p, max_tasks, num_cus, s)
-                 : launch_ring_one<false, false>(p, max_tasks, num_cus, s);
+    return gate_up ? launch_ring_one<true, true, I8>(p, max_tasks, num_cus, s)
+                   : launch_ring_one<false, true, I8>(p, max_tasks, num_cus, s);
+  return gate_up ? launch_ring_one<true, false, I8>(p, max_tasks, num_cus, s)
+                 : launch_ring_one<false, false, I8>(p, max_tasks, num_cus, s);
+}
+
+hipError_t launch_gemm_ring(bool gate_up, bool stream_weights, bool int8, const GemmParams& p, int64_t max_tasks,
+                            int num_cus, hipStream_t s) {
+  return int8 ? launch_ring_fmt<true>(gate_up, stream_weights, p, max_tasks, num_cus, s)
+              : launch_ring_fmt<false>(gate_up, stream_weights, p, max_tasks, num_cus, s);
 }
 
 }  // namespace afd

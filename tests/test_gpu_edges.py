@@ -13,7 +13,7 @@ def cfg(dtype="bf16", T=64, H=256, I=256, E=8, K=2, shared=0):
     return dict(dtype=dtype, T=T, H=H, I=I, E=E, K=K, routing="uniform", shared_inter=shared)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8", "w8a8"])
 def test_adversarial_routing(dtype):
     """All tokens on one expert (many m-tiles), duplicate ids, -1 slots, nothing local."""
     T, E, K = 130, 6, 3
@@ -37,9 +37,9 @@ def test_adversarial_routing(dtype):
         layer.close()
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "w8a8"])
 def test_empty_and_tiny_batches(dtype):
-    p = problem(cfg(dtype, T=40, shared=256 if dtype == "fp8" else 0), seed=2)
+    p = problem(cfg(dtype, T=40, shared=256 if dtype != "bf16" else 0), seed=2)
     layer = afd.Layer(p, max_tokens=40)
     for T in (0, 1, 2, 40):
         say("case", dtype, "T =", T)
@@ -191,7 +191,7 @@ def test_unused_experts_poisoned_with_nan():
     layer.close()
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "w8a8"])
 def test_deterministic_and_permutation_equivariant(dtype):
     p = problem(cfg(dtype, T=96, E=8, K=2, shared=256 if dtype == "fp8" else 0), seed=6)
     layer, a = run_layer(p)

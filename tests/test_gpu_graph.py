@@ -20,6 +20,7 @@ CASES = {
     "bf16_light_only": (cfg("bf16", 64, 512, 256, 16, 2), 21),
     "bf16_zipf_mixed": (cfg("bf16", 700, 512, 256, 8, 4, routing="zipf"), 22),
     "fp8_shared_ring": (cfg("fp8", 150, 512, 384, 6, 3, shared=384), 23),
+    "w8a8_shared_ring": (cfg("w8a8", 150, 512, 384, 6, 3, shared=384), 25),
     "f32_tiny": (cfg("f32", 40, 256, 384, 5, 3), 24),
 }
 

@@ -41,6 +41,12 @@ SMALL_CASES = {
     # block-FP8: 128-row tiles)
     "bf16_heavy_ragged": (small("bf16", 600, 256, 256, 4, 2), 10),
     "fp8_heavy_ragged": (small("fp8", 300, 256, 256, 4, 2), 11),
+    # W8A8 (int8 MFMA, per-token and per-channel scales, h re-quantised per row)
+    "w8a8_mr1": (small("w8a8", 33, 512, 256, 16, 2), 12),
+    "w8a8_shared_multi_tile": (small("w8a8", 70, 512, 384, 5, 3, shared=384), 13),
+    "w8a8_heavy_ragged": (small("w8a8", 300, 256, 256, 4, 2), 14),
+    "w8a8_k32_shared_h384": (small("w8a8", 40, 384, 256, 64, 32, shared=256), 15),
+    "w8a8_local_shard": (small("w8a8", 200, 256, 384, 4, 8, routing="local_shard", global_experts=32), 16),
 }
 
 
@@ -56,7 +62,7 @@ def test_small_full_batch(name):
     layer.close()
 
 
-FULL = ["tiny", "decode", "aggregated", "fp8_shared"]
+FULL = ["tiny", "decode", "aggregated", "fp8_shared", "w8a8_shared"]
 EVERY_TOKEN = {"tiny", "decode"}
 
 

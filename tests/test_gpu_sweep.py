@@ -19,7 +19,7 @@ N_CASES = int(os.environ.get("AFD_SWEEP_CASES", "8"))  # more for a wider one-of
 
 
 def draw_case(dtype: str, i: int) -> dict:
-    rng = np.random.default_rng(1000 * (1 + ["f32", "bf16", "fp8"].index(dtype)) + i)
+    rng = np.random.default_rng(1000 * (1 + ["f32", "bf16", "fp8", "w8a8"].index(dtype)) + i)
     H = 128 * int(rng.integers(1, 5))
     I = 128 * int(rng.integers(1, 5))
     E = int(rng.integers(2, 40))
@@ -30,7 +30,7 @@ def draw_case(dtype: str, i: int) -> dict:
     return dict(dtype=dtype, T=T, H=H, I=I, E=E, K=K, routing=routing, shared_inter=shared)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8", "w8a8"])
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_shapes(dtype, i):
     cfg = draw_case(dtype, i)

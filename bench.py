@@ -40,8 +40,8 @@ METRIC = "routed tokens/s per MoE layer on 1 MI355X; % of MFMA/HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GATE_UP_STAGE = 2  # stage index of the grouped GEMM gate/up + SwiGLU in the library's timing
 STAGE_STEPS = 20   # steps with every stage timed, after the timed steps, for the per-stage breakdown
-KERNEL_SOURCES = ("gemm.hip", "gemm_stream.h", "gemm_tiled.hip", "gemm_ring.hip", "quant.hip", "afd_device.h",
-                  "afd_internal.h")
+KERNEL_SOURCES = ("gemm.hip", "gemm_stream.h", "gemm_tiled.hip", "gemm_ring.hip", "gemm_ring.h", "quant.hip",
+                  "quant.h", "fused.hip", "combine.h", "afd_device.h", "afd_internal.h")
 
 
 def kernel_source_hash() -> str:
@@ -197,6 +197,8 @@ def main():
                     help="also time the step captured in a HIP graph and replayed (graph_ms_per_step)")
     ap.add_argument("--sweep", action="store_true",
                     help="time the layer at the workload's shape for T = 64 ... 16384 (one JSON line per T)")
+    ap.add_argument("--fused", action="store_true",
+                    help="block-FP8 / W8A8 workloads: each forward as one persistent launch (afd_ffn_set_fused)")
     ap.add_argument("--serial", action="store_true",
                     help="microbatch workloads: run the microbatches one after the other on one stream, "
                          "each on every CU (the baseline the two-stream ping-pong is compared with)")
@@ -241,6 +243,8 @@ def main():
     serial = args.serial and mbs > 1
     for layer in layers:  # the microbatches run side by side, each on its share of the CUs
         layer.set_concurrency(1 if serial else mbs)
+        if args.fused:
+            layer.set_fused(True)
     if mbs == 1:
         parts = [p]
         streams = [torch.cuda.current_stream()]
@@ -337,8 +341,9 @@ def main():
     # dominant kernel: grouped GEMM gate/up + SwiGLU (two thirds of the weight bytes and flops)
     gu_launch_s = gu_launch_ms * 1e-3
     launches_per_step = mbs
-    gu_bytes = units["gu_bytes"] / launches_per_step
-    gu_flops = units["gu_flops"] / launches_per_step
+    # the timed kernel: the gate/up stage, or with --fused the one launch of the whole layer
+    gu_bytes = units["layer_bytes" if args.fused else "gu_bytes"] / launches_per_step
+    gu_flops = units["layer_flops" if args.fused else "gu_flops"] / launches_per_step
     hbm_ach = gu_bytes / gu_launch_s / 1e9
     mfma_ach = gu_flops / gu_launch_s / 1e12
     # the bound follows the layer's arithmetic intensity against the ridge
@@ -353,20 +358,21 @@ def main():
     # both fractions of the same launch, whichever bound the layer sits at
     roof["hbm_frac"] = round(hbm_ach / PEAK_HBM_GBS, 4)
     roof["mfma_frac"] = round(mfma_ach / PEAK_TFLOPS[dt], 4)
-    roof["kernel"] = gate_up_kernels(cfg, T // mbs)
+    roof["kernel"] = ("the whole layer: fused_kernel (one persistent launch per forward)" if args.fused
+                      else gate_up_kernels(cfg, T // mbs))
     roof["launch_ms"] = round(gu_launch_ms, 4)
     # launches of this kernel running at once, each on its share of the CUs
     roof["concurrent_launches"] = 1 if serial else mbs
     if not serial and mbs > 1:
         # the concurrent launches start together on disjoint CU shares: their
         # bytes together over their mean duration (the window they share)
-        agg = units["gu_bytes"] / gu_launch_s / 1e9
+        agg = units["layer_bytes" if args.fused else "gu_bytes"] / gu_launch_s / 1e9
         roof["aggregate_hbm_gbs"] = round(agg, 1)
         roof["aggregate_hbm_frac"] = round(agg / PEAK_HBM_GBS, 4)
     traffic = None
     try:
         with open(TRAFFIC_FILE) as f:
-            tr = json.load(f).get(args.workload)
+            tr = json.load(f).get(args.workload + ("_fused" if args.fused else ""))
         if tr and tr.get("kernel_hash") == kernel_source_hash():
             traffic = tr.get("bytes_per_launch")
     except (OSError, ValueError):
@@ -386,7 +392,8 @@ def main():
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3_block128", "f32": "f32", "w8a8": "int8_w8a8"}[dt],
         "data": "synthetic (seeded; random-init expert weights N(0,0.02), hidden N(0,1))",
-        "config": {"workload": inputs.WORKLOAD_TITLES[args.workload], "T": T, "H": cfg["H"], "I": cfg["I"],
+        "config": {"workload": inputs.WORKLOAD_TITLES[args.workload] + ("_fused" if args.fused else ""),
+                   "T": T, "H": cfg["H"], "I": cfg["I"],
                    "E": cfg["E"], "top_k": cfg["K"], "shared_inter": cfg.get("shared_inter", 0),
                    "routing": cfg["routing"], "microbatches": mbs, "microbatch_streams": 1 if serial else mbs,
                    "routed_rows": units["N"],

@@ -142,6 +142,31 @@ afd_status afd_ffn_clone(const afd_ffn_t *src, afd_ffn_t **out_handle);
 afd_status afd_ffn_set_concurrency(afd_ffn_t *handle, int32_t streams);
 
 /*
+ * Run each later forward of this handle as ONE persistent launch instead of
+ * five to eight (enable = 1), or as separate launches (0, the default).
+ * FastAFD's expert GPUs run the MoE layer as one persistent kernel (System
+ * Design item 3; the "Ablation Results" credit that fusion with about half the
+ * step latency of separate kernels).  Here the launch runs the dispatch (every
+ * workgroup counting and placing a chunk of the slots), gate/up + SwiGLU, the
+ * W8A8 re-quantisation of h, down and the combine, separated by grid barriers;
+ * results are bit-identical to the separate launches.  One workgroup per CU of
+ * the call's share (afd_ffn_set_concurrency), all resident at once: the
+ * caller must not keep other kernels occupying those CUs for long (a barrier
+ * wait gives up after about a second, counts a timeout and goes on, so the
+ * GPU never hangs, but that call's results are wrong; see
+ * afd_ffn_fused_errors).  Block-FP8 and W8A8 handles only
+ * (AFD_ERR_UNSUPPORTED otherwise); a clone starts with its source's setting;
+ * afd_ffn_forward_noalloc always uses separate launches.  With timing on, the
+ * whole launch is reported as stage 2 and the other stages as about 0.
+ */
+afd_status afd_ffn_set_fused(afd_ffn_t *handle, int32_t enable);
+
+/* Timed-out grid-barrier waits of the handle's fused forwards since the last
+ * query (synchronises the stream; *count is host memory; resets the count).
+ * Returns AFD_ERR_HIP if > 0. */
+afd_status afd_ffn_fused_errors(afd_ffn_t *handle, int32_t *count, void *stream);
+
+/*
  * One layer forward for T = num_tokens tokens (0 <= T <= max_tokens):
  *   hidden         device [T, H]: fp32 | bf16 | e4m3 codes | int8 codes (per dtype)
  *   hidden_scales  device fp32: [T, H/128] for AFD_DTYPE_FP8_BLOCK, [T] (one per

@@ -29,7 +29,7 @@ EXPORTS = ("afd_ffn_validate_config", "afd_ffn_create", "afd_ffn_clone", "afd_ff
            "afd_ffn_forward_noalloc",
            "afd_ffn_destroy", "afd_ffn_status_string", "afd_ffn_last_error", "afd_ffn_debug_dispatch",
            "afd_ffn_routing_errors", "afd_ffn_set_timing", "afd_ffn_set_timing_stages", "afd_ffn_get_timing",
-           "afd_ffn_set_concurrency")
+           "afd_ffn_set_concurrency", "afd_ffn_set_fused", "afd_ffn_fused_errors")
 
 
 class afd_ffn_config(ctypes.Structure):
@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH):
     lib.afd_ffn_set_timing.argtypes = [vp, i32]
     lib.afd_ffn_set_timing_stages.argtypes = [vp, ctypes.c_uint32]
     lib.afd_ffn_set_concurrency.argtypes = [vp, i32]
+    lib.afd_ffn_set_fused.argtypes = [vp, i32]
+    lib.afd_ffn_fused_errors.argtypes = [vp, ctypes.POINTER(i32), vp]
     lib.afd_ffn_get_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
     for name in EXPORTS:
         if name not in ("afd_ffn_status_string", "afd_ffn_last_error"):
@@ -176,6 +178,19 @@ def afd_ffn_set_concurrency(handle, streams: int) -> None:
     _check(load().afd_ffn_set_concurrency(handle, int(streams)))
 
 
+def afd_ffn_set_fused(handle, enable: bool) -> None:
+    _check(load().afd_ffn_set_fused(handle, 1 if enable else 0))
+
+
+def afd_ffn_fused_errors(handle, stream=None) -> int:
+    """Timed-out grid-barrier waits of fused forwards since the last query."""
+    n = ctypes.c_int32(0)
+    st = load().afd_ffn_fused_errors(handle, ctypes.byref(n), _stream(stream))
+    if st not in (AFD_OK, AFD_ERR_HIP):
+        _check(st)
+    return int(n.value)
+
+
 def afd_ffn_set_timing(handle, enable: bool) -> None:
     _check(load().afd_ffn_set_timing(handle, 1 if enable else 0))
 
@@ -239,6 +254,10 @@ class Layer:
     def set_concurrency(self, streams: int) -> None:
         """Forwards run at once on other streams (this handle and its clones)."""
         afd_ffn_set_concurrency(self.handle, streams)
+
+    def set_fused(self, enable: bool) -> None:
+        """Later forwards as one persistent launch (block-FP8 and W8A8 layers)."""
+        afd_ffn_set_fused(self.handle, enable)
 
     def out_like(self, T: int, device="cuda"):
         dt = torch.float32 if self.dtype == "f32" else torch.bfloat16

@@ -207,6 +207,29 @@ struct F32Params {
   float* c;                 // [rows, N]
 };
 
+// The whole layer in one persistent launch (fused.hip; block-FP8 and W8A8):
+// the dispatch's, the GEMM stages' and the combine's parameters plus the
+// grid-barrier state, all in the handle's workspace.
+constexpr int kFusedMaxGrid = 512;  // workgroups of one fused launch (one chunk count per thread)
+struct FusedParams {
+  DispatchParams d;       // ids, sizes, outputs and tile-list parameters of the dispatch
+  const float* x_src;     // the caller's hidden scales [T][ks]
+  int32_t ks;             // block-FP8: H / 128; W8A8: 1
+  float* x_dst;           // [ks][ld] in sorted-row order
+  int32_t ld;             // rows of the activation buffers
+  int32_t tokens;         // T
+  int32_t top_k;
+  GemmParams gu, dn;      // the two GEMM stages (light list in mtiles, heavy in mtiles2)
+  QuantParams qp;         // W8A8: h to int8
+  CombineParams cp;
+  int32_t* bar;           // [4]: arrivals, departures, timed-out spins, spare (zero between calls)
+  int32_t* chunk_counts;  // [grid][E] per-chunk expert counts
+  int32_t* chunk_bad;     // [grid] ids outside [-1, E) per chunk
+  int32_t* local_base;    // [grid][E] exclusive prefix of the chunk counts per expert
+  int32_t* totals;        // [E]
+  int32_t spin_limit;     // rounds a barrier spin waits before it counts a timeout and goes on
+};
+
 // launchers (return hipError_t of the launch)
 hipError_t launch_dispatch_count_scan(const DispatchParams& p, hipStream_t s);
 hipError_t launch_dispatch_scatter(const DispatchParams& p, hipStream_t s);
@@ -234,6 +257,9 @@ hipError_t launch_gemm_ring(bool gate_up, bool stream_weights, bool int8, const 
 int ring_rows(bool heavy);
 hipError_t launch_gemm_f32(bool gate_up, const F32Params& p, int grid, hipStream_t s);
 hipError_t launch_quant_rows(const QuantParams& p, hipStream_t s);
+// one workgroup per CU of num_cus (all resident at once); stream_weights and
+// int8 as for launch_gemm_ring
+hipError_t launch_fused(bool stream_weights, bool int8, const FusedParams& f, int num_cus, hipStream_t s);
 hipError_t launch_combine(int dtype, const CombineParams& p, int tokens, hipStream_t s);
 hipError_t launch_pack(int dtype, bool gate_up, const void* w_first, const void* w_second,
                        int64_t expert_in_stride_elems, int experts, int kdim, int ndim,

@@ -133,6 +133,9 @@ struct Workspace {
   uint8_t* h8 = nullptr;      // W8A8: [h_rows, I] int8 codes of h
   float* pamax = nullptr;     // W8A8: [I/128][h_rows] per-row amax of each gate/up task's columns
   uint8_t* y = nullptr;
+  // the fused launch (8-bit layers): grid-barrier state and the dispatch's chunk sums
+  int32_t *bar = nullptr, *chunk_counts = nullptr, *chunk_bad = nullptr, *local_base = nullptr, *totals = nullptr;
+  int fused_grid = 0;  // workgroups the chunk arrays are sized for
   int64_t nmax = 0;    // routed-row capacity tcap * K; the shared expert's rows start here
   int64_t h_rows = 0;  // rows of h and y: nmax (+ tcap with a shared expert)
   int tcap = 0;
@@ -144,6 +147,7 @@ struct afd_ffn {
   int H = 0, I = 0, E = 0, K = 0, Tmax = 0, S = 0, dtype = 0, device = 0;
   int num_cus = 256;
   int concurrency = 1;  // forwards the caller runs at once on other streams (afd_ffn_set_concurrency)
+  int fused = 0;        // 1: the whole layer in one persistent launch (afd_ffn_set_fused)
   WeightStore* w = nullptr;
   uint8_t* ws_mem = nullptr;  // the handle's workspace allocation (sized for Tmax)
   Workspace ws;
@@ -236,6 +240,10 @@ int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w
                 o_xs = take(a->dtype == kFP8 ? rows * (a->H / 128) * 4 : w8 ? rows * 4 : 0),
                 o_h8 = take(w8 ? rows * a->I : 0), o_pm = take(w8 ? rows * (a->I / 128) * 4 : 0),
                 o_y = take(rows * a->H * ys);
+  const bool fz = a->dtype == kFP8 || w8;  // the fused launch's state
+  const int64_t fg = fz ? std::min(a->num_cus, kFusedMaxGrid) : 0;
+  const int64_t o_bar = take(fz ? 16 : 0), o_fcc = take(4 * fg * a->E), o_fcb = take(4 * fg),
+                o_flb = take(4 * fg * a->E), o_ftot = take(fz ? 4ll * a->E : 0);
   if (base && w) {
     w->counts = (int32_t*)(base + o_counts);
     w->offsets = (int32_t*)(base + o_offsets);
@@ -252,6 +260,12 @@ int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w
     w->x_scales = sc ? (float*)(base + o_xs) : nullptr;
     w->h8 = w8 ? base + o_h8 : nullptr;
     w->pamax = w8 ? (float*)(base + o_pm) : nullptr;
+    w->bar = fz ? (int32_t*)(base + o_bar) : nullptr;
+    w->chunk_counts = fz ? (int32_t*)(base + o_fcc) : nullptr;
+    w->chunk_bad = fz ? (int32_t*)(base + o_fcb) : nullptr;
+    w->local_base = fz ? (int32_t*)(base + o_flb) : nullptr;
+    w->totals = fz ? (int32_t*)(base + o_ftot) : nullptr;
+    w->fused_grid = (int)fg;
     w->y = base + o_y;
     w->nmax = nmax;
     w->h_rows = rows;
@@ -393,7 +407,9 @@ afd_status check_forward_args(const afd_ffn* a, int32_t T, int64_t tcap, const v
 
 // Enqueue one forward on `stream` with the buffers of `w` (capacity w.tcap >= T).
 // `timed`: record the handle's timing events (the handle's own workspace only).
-afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, int32_t T, const void* hidden,
+// `own_ws`: w is the handle's workspace (the fused launch keeps its barrier
+// state there, zero between calls).
+afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws, int32_t T, const void* hidden,
                         const float* hidden_scales, const int32_t* topk_ids, const float* topk_weights, void* out,
                         void* stream) {
   DeviceGuard dg(a->device);
@@ -474,16 +490,18 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, int32_t T, c
   d.mtiles_heavy = w.mtiles_heavy;
   d.num_mtiles = w.num_mtiles;
 
+  // the whole layer in one persistent launch (afd_ffn_set_fused; 8-bit layers)
+  const bool use_fused = own_ws && a->fused && fp8 && T > 0;
   if ((st = mark(0))) return st;
-  AFD_HIP(launch_dispatch_count_scan(d, s));
+  if (!use_fused) AFD_HIP(launch_dispatch_count_scan(d, s));
   if ((st = mark(1))) return st;
   if (T == 0) {
     // nothing else to do (the later stages count as not timed)
     if (tmask) a->ev_pending.push_back(ev);
     return AFD_OK;
   }
-  AFD_HIP(launch_dispatch_scatter(d, s));
-  if (fp8) {
+  if (!use_fused) AFD_HIP(launch_dispatch_scatter(d, s));
+  if (fp8 && !use_fused) {
     // the hidden rows' scales in sorted-row order: block-FP8 one per 128
     // columns (step-major), W8A8 one per token
     ScaleGatherParams sg{};
@@ -500,7 +518,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, int32_t T, c
     sg.ld = (int32_t)w.h_rows;
     AFD_HIP(launch_gather_scales(sg, s));
   }
-  if ((st = mark(2))) return st;
+  if ((st = mark(2))) return st;  // (fused: the boundary before its one launch)
 
   // upper bounds of the routed + shared m-tiles of this call, per list
   const int64_t mt_bound = n_flat / bm + std::min<int64_t>(E, n_flat) + (a->S ? (T + bm - 1) / bm : 0) + 1;
@@ -508,6 +526,28 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, int32_t T, c
   const int64_t rows_ld_h = (int64_t)I * (w8 ? 2 : esize_of(dt));  // W8A8: bf16 h before re-quantisation
   const int64_t h_rows = w.h_rows;
   const int occupancy_wgs = 4;  // resident workgroups per CU the persistent grids aim for
+
+  CombineParams cp{};
+  cp.y = w.y;
+  cp.y_bytes = w.h_rows * (int64_t)H * (dt == kF32 ? 4 : 2);
+  cp.row_of = w.row_of;
+  cp.weights = topk_weights;
+  cp.top_k = K;
+  cp.hidden = H;
+  cp.shared_row0 = a->S ? (int32_t)nmax : -1;
+  cp.out = (uint8_t*)out;
+  QuantParams qp{};  // W8A8: h -> int8 codes with one scale per row, for the down GEMM
+  qp.h = w.h;
+  qp.pamax = w.pamax;
+  qp.ld = (int32_t)w.h_rows;
+  qp.inter = I;
+  qp.offsets = w.offsets;
+  qp.num_experts = E;
+  qp.routed_max = (int32_t)n_flat;
+  qp.shared_row0 = a->S ? (int32_t)nmax : -1;
+  qp.shared_rows = a->S ? T : 0;
+  qp.h8 = (int8_t*)w.h8;
+  qp.hsc = w.h_scales;
 
   if (dt == kF32) {
     F32Params g{};
@@ -631,37 +671,44 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, int32_t T, c
       }
       return launch_gemm_mixed(gate_up, mr, heavy, light, cus, s);
     };
-    AFD_HIP(stage(true, gu_light, gu_heavy));
-    if (w8) {
-      // h -> int8 codes with one scale per row, for the down GEMM
-      QuantParams qp{};
-      qp.h = w.h;
-      qp.pamax = w.pamax;
-      qp.ld = (int32_t)w.h_rows;
-      qp.inter = I;
-      qp.offsets = w.offsets;
-      qp.num_experts = E;
-      qp.routed_max = (int32_t)n_flat;
-      qp.shared_row0 = a->S ? (int32_t)nmax : -1;
-      qp.shared_rows = a->S ? T : 0;
-      qp.h8 = (int8_t*)w.h8;
-      qp.hsc = w.h_scales;
-      AFD_HIP(launch_quant_rows(qp, s));
+    if (use_fused) {
+      // one launch: dispatch, both GEMM stages (and the W8A8 re-quantisation)
+      // and the combine, timed as the gate/up stage
+      FusedParams fp{};
+      fp.d = d;
+      fp.x_src = hidden_scales;
+      fp.ks = w8 ? 1 : H / 128;
+      fp.x_dst = w.x_scales;
+      fp.ld = (int32_t)w.h_rows;
+      fp.tokens = T;
+      fp.top_k = K;
+      fp.gu = gu_light;
+      fp.gu.mtiles2 = gu_heavy.mtiles;
+      fp.gu.num_mtiles2 = gu_heavy.num_mtiles;
+      fp.dn = dn_light;
+      fp.dn.mtiles2 = dn_heavy.mtiles;
+      fp.dn.num_mtiles2 = dn_heavy.num_mtiles;
+      fp.qp = qp;
+      fp.cp = cp;
+      fp.bar = w.bar;
+      fp.chunk_counts = w.chunk_counts;
+      fp.chunk_bad = w.chunk_bad;
+      fp.local_base = w.local_base;
+      fp.totals = w.totals;
+      fp.spin_limit = 1 << 20;
+      AFD_HIP(launch_fused(a->concurrency == 1, w8, fp, std::min(cus, w.fused_grid), s));
+      for (int b = 3; b <= AFD_NUM_STAGES; ++b)
+        if ((st = mark(b))) return st;
+      if (tmask) a->ev_pending.push_back(ev);
+      return AFD_OK;
     }
+    AFD_HIP(stage(true, gu_light, gu_heavy));
+    if (w8) AFD_HIP(launch_quant_rows(qp, s));
     if ((st = mark(3))) return st;
     AFD_HIP(stage(false, dn_light, dn_heavy));
     if ((st = mark(4))) return st;
   }
 
-  CombineParams cp{};
-  cp.y = w.y;
-  cp.y_bytes = w.h_rows * (int64_t)H * (dt == kF32 ? 4 : 2);
-  cp.row_of = w.row_of;
-  cp.weights = topk_weights;
-  cp.top_k = K;
-  cp.hidden = H;
-  cp.shared_row0 = a->S ? (int32_t)nmax : -1;
-  cp.out = (uint8_t*)out;
   AFD_HIP(launch_combine(dt == kF32 ? kF32 : kBF16, cp, T, s));
   if ((st = mark(5))) return st;
   if (tmask) a->ev_pending.push_back(ev);
@@ -740,6 +787,7 @@ afd_status afd_ffn_clone(const afd_ffn_t* src, afd_ffn_t** out_handle) {
   a->device = src->device;
   a->num_cus = src->num_cus;
   a->concurrency = src->concurrency;
+  a->fused = src->fused;
   a->w = src->w;
   a->w->refs.fetch_add(1);
   afd_status st = alloc_workspace(a);
@@ -766,7 +814,7 @@ afd_status afd_ffn_forward(afd_ffn_t* a, int32_t T, const void* hidden, const fl
   g_last_error.clear();
   afd_status st = check_forward_args(a, T, a ? a->Tmax : 0, hidden, hidden_scales, topk_ids, topk_weights, out);
   if (st) return st;
-  st = forward_impl(a, a->ws, true, T, hidden, hidden_scales, topk_ids, topk_weights, out, stream);
+  st = forward_impl(a, a->ws, true, true, T, hidden, hidden_scales, topk_ids, topk_weights, out, stream);
   if (st == AFD_OK) a->last_T = T;
   return st;
 }
@@ -786,7 +834,7 @@ afd_status afd_ffn_forward_noalloc(afd_ffn_t* a, int32_t T, const void* hidden, 
   if ((st = scratch_address(a->device, &base))) return st;
   Workspace w;
   layout_workspace(a, T, base, &w);
-  return forward_impl(a, w, false, T, hidden, hidden_scales, topk_ids, topk_weights, out, stream);
+  return forward_impl(a, w, false, false, T, hidden, hidden_scales, topk_ids, topk_weights, out, stream);
 }
 
 afd_status afd_ffn_debug_dispatch(afd_ffn_t* a, int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
@@ -821,6 +869,29 @@ afd_status afd_ffn_set_concurrency(afd_ffn_t* a, int32_t streams) {
     return fail(AFD_ERR_INVALID_ARG, "concurrency %d outside [1, %d]", streams, a->num_cus);
   a->concurrency = streams;
   return AFD_OK;
+}
+
+afd_status afd_ffn_set_fused(afd_ffn_t* a, int32_t enable) {
+  g_last_error.clear();
+  if (!a) return fail(AFD_ERR_INVALID_ARG, "handle is NULL");
+  if (enable != 0 && enable != 1) return fail(AFD_ERR_INVALID_ARG, "enable must be 0 or 1, not %d", enable);
+  if (enable && a->dtype != kFP8 && a->dtype != kW8A8)
+    return fail(AFD_ERR_UNSUPPORTED, "the fused launch serves block-FP8 and W8A8 layers");
+  a->fused = enable;
+  return AFD_OK;
+}
+
+afd_status afd_ffn_fused_errors(afd_ffn_t* a, int32_t* count, void* stream) {
+  g_last_error.clear();
+  if (!a || !count) return fail(AFD_ERR_INVALID_ARG, "NULL argument");
+  *count = 0;
+  if (!a->ws.bar) return AFD_OK;
+  DeviceGuard dg(a->device);
+  hipStream_t s = (hipStream_t)stream;
+  AFD_HIP(hipMemcpyAsync(count, a->ws.bar + 2, 4, hipMemcpyDeviceToHost, s));
+  AFD_HIP(hipStreamSynchronize(s));
+  if (*count) AFD_HIP(hipMemsetAsync(a->ws.bar + 2, 0, 4, s));
+  return *count > 0 ? fail(AFD_ERR_HIP, "%d grid-barrier waits of fused forwards timed out", *count) : AFD_OK;
 }
 
 afd_status afd_ffn_set_timing(afd_ffn_t* a, int32_t enable) {

@@ -16,18 +16,18 @@
 
 namespace afd {
 
-// Token t of the combine; every thread of the workgroup calls it (any
-// workgroup size that is a multiple of 64).  Ends with the workgroup's
-// threads past every read of its LDS lists.
+// Token t of the combine by a group of `nthr` threads (a multiple of 64; this
+// thread is number `tid` of it) with its own LDS lists rows[kMaxTopK + 1],
+// ws[kMaxTopK + 1] and nrows[1].  Every thread of the workgroup calls it the
+// same number of times (it holds two workgroup barriers); a thread whose group
+// has no token this round passes active = false.  Ends with every thread past
+// the reads of its group's lists.
 template <int DT>
-__device__ __forceinline__ void combine_token(const CombineParams& p, const int t) {
+__device__ __forceinline__ void combine_rows(const CombineParams& p, const int t, const bool active, const int tid,
+                                             const int nthr, int* rows, float* ws, int* nrows) {
   // the token's rows to add, in order: routed slots with a row (k order), then
   // the shared expert's row; compacted so dropped slots cost nothing
-  __shared__ int rows[kMaxTopK + 1];
-  __shared__ float ws[kMaxTopK + 1];
-  __shared__ int nrows;
-  const int tid = threadIdx.x;
-  if (tid < 64) {
+  if (active && tid < 64) {
     const int r = tid < p.top_k ? p.row_of[(int64_t)t * p.top_k + tid] : -1;
     const bool valid = r >= 0;
     const uint64_t mask = __ballot(valid);
@@ -42,7 +42,7 @@ __device__ __forceinline__ void combine_token(const CombineParams& p, const int 
         rows[n] = p.shared_row0 + t;
         ws[n] = 1.0f;
       }
-      nrows = n + (p.shared_row0 >= 0 ? 1 : 0);
+      *nrows = n + (p.shared_row0 >= 0 ? 1 : 0);
     }
   }
   __syncthreads();
@@ -52,8 +52,8 @@ __device__ __forceinline__ void combine_token(const CombineParams& p, const int 
   const int nvec = p.hidden / kVec;
   const int row_bytes = p.hidden * kEsz;
   const auto ry = dev::make_rsrc(p.y, p.y_bytes);
-  const int nr = dev::uniform(nrows);
-  for (int v = tid; v < nvec; v += blockDim.x) {
+  const int nr = active ? dev::uniform(*nrows) : 0;
+  for (int v = tid; active && v < nvec; v += nthr) {
     float acc[kVec];
 #pragma unroll
     for (int i = 0; i < kVec; ++i) acc[i] = 0.0f;

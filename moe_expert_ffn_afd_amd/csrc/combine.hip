@@ -6,7 +6,10 @@ namespace afd {
 
 template <int DT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  combine_token<DT>(p, blockIdx.x);
+  __shared__ int rows[kMaxTopK + 1];
+  __shared__ float ws[kMaxTopK + 1];
+  __shared__ int nrows;
+  combine_rows<DT>(p, blockIdx.x, true, threadIdx.x, blockDim.x, rows, ws, &nrows);
 }
 
 hipError_t launch_combine(int dtype, const CombineParams& p, int tokens, hipStream_t s) {

@@ -15,14 +15,16 @@
 //   D1  every workgroup counts its chunk of the flat slots per expert;
 //   D2  per expert, the exclusive scan of the chunk counts (experts spread
 //       over the workgroups) and the expert's total;
-//   D3  every workgroup scans the totals into the offsets, places its chunk's
-//       slots at their stable rows (ballot ranks, as in dispatch.hip) and
-//       gathers their activation scales; workgroup 0 also writes the counts,
-//       offsets and both m-tile lists;
+//   D3  every workgroup scans the totals into the offsets and places its
+//       chunk's slots at their stable rows (ballot ranks, as in dispatch.hip);
+//       workgroup 0 also writes the counts, offsets and both m-tile lists;
+//   D4  the activation scales gathered into sorted-row order (coalesced
+//       stores; inside D3 they were 56 scattered stores per slot, which made
+//       D3 the slowest phase after the GEMMs);
 //   G1  gate/up + SwiGLU over both tile lists (gemm_ring.h);
 //   Q   W8A8 only: h re-quantised to int8 per row (quant.h);
 //   G2  down;
-//   C   the combine, tokens spread over the workgroups (combine.h).
+//   C   the combine, two tokens at a time per workgroup (combine.h).
 // The results equal the separate launches' bit for bit: the same per-element
 // arithmetic in the same order, only scheduled differently.
 //
@@ -221,9 +223,6 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(FusedParams f) 
         const int pos = cursor[e] + prefix + rank;
         d.sorted_assign[pos] = fi;
         d.row_of[fi] = pos;
-        // the row's activation scales, in sorted-row order (step-major)
-        const int t = fi / K;
-        for (int c = 0; c < f.ks; ++c) f.x_dst[(int64_t)c * f.ld + pos] = f.x_src[(int64_t)t * f.ks + c];
       } else if (fi < f1) {
         d.row_of[fi] = -1;
       }
@@ -237,10 +236,40 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(FusedParams f) 
       if (valid && rank == 0) wcnt[wave * E + e] = 0;
       __syncthreads();
     }
-    // the shared expert's rows (token order): their scales
-    for (int i = b * kFusedThreads + tid; i < d.shared_rows; i += G * kFusedThreads)
-      for (int c = 0; c < f.ks; ++c)
-        f.x_dst[(int64_t)c * f.ld + d.shared_row0 + i] = f.x_src[(int64_t)i * f.ks + c];
+  }
+  grid_sync(f.bar, target, G, f.spin_limit);
+
+  // ---- D4: the activation scales in sorted-row order (step-major), for the
+  // routed rows and the shared expert's; consecutive threads write
+  // consecutive rows of a step, 8 items per thread in flight
+  {
+    const int N = d.offsets[E];
+    const int R = N + d.shared_rows;
+    const int64_t total = (int64_t)f.ks * R, stride = (int64_t)G * kFusedThreads;
+    constexpr int kU = 8;
+    for (int64_t i0 = (int64_t)b * kFusedThreads + tid; i0 < total; i0 += kU * stride) {
+      int tok[kU];
+      int64_t dst[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t i = i0 + u * stride;
+        dst[u] = -1;
+        tok[u] = 0;
+        if (i < total) {
+          const int c = (int)(i / R), rr = (int)(i - (int64_t)c * R);
+          const int row = rr < N ? rr : d.shared_row0 + (rr - N);
+          tok[u] = rr < N ? d.sorted_assign[rr] / K : rr - N;
+          tok[u] = tok[u] * f.ks + c;  // source index
+          dst[u] = (int64_t)c * f.ld + row;
+        }
+      }
+      float v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[u] = dst[u] >= 0 ? f.x_src[tok[u]] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (dst[u] >= 0) f.x_dst[dst[u]] = v[u];
+    }
   }
   grid_sync(f.bar, target, G, f.spin_limit);
 
@@ -261,8 +290,15 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(FusedParams f) 
   ring_stage<false, WNT, I8>(f.dn, b, G);
   grid_sync(f.bar, target, G, f.spin_limit);
 
-  // ---- C: combine
-  for (int t = b; t < f.tokens; t += G) combine_token<kBF16>(f.cp, t);
+  // ---- C: combine, two tokens at a time per workgroup (4 waves each)
+  {
+    __shared__ int c_rows[2][kMaxTopK + 1];
+    __shared__ float c_ws[2][kMaxTopK + 1];
+    __shared__ int c_n[2];
+    const int grp = tid >> 8;
+    for (int t0 = 2 * b; t0 < f.tokens; t0 += 2 * G)
+      combine_rows<kBF16>(f.cp, t0 + grp, t0 + grp < f.tokens, tid & 255, 256, c_rows[grp], c_ws[grp], &c_n[grp]);
+  }
 
   // the last workgroup out resets the barrier counters for the next call
   __syncthreads();

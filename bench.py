@@ -15,6 +15,8 @@ steps with every stage timed.
 
 Other modes: --copy-calibration runs a plain device copy of known size (the
 reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters);
+--mfma-ceiling measures the MFMA rate sustained with no memory traffic and
+the shader clock meanwhile (the ceiling of the MFMA fractions);
 --no-cpu-baseline skips the oracle timing; --graph also times the step
 captured in a HIP graph and replayed; --sweep times the layer at the
 workload's shape over a range of batch sizes T (the FFN-side time T_e as a
@@ -79,12 +81,17 @@ def algorithmic_units(cfg: dict, ids) -> dict:
     dt = cfg["dtype"]
     bw = {"f32": 4, "bf16": 2, "fp8": 1, "w8a8": 1}[dt]
     by = 4 if dt == "f32" else 2
-    S = 1 if cfg.get("shared_inter") else 0
+    Is = cfg.get("shared_inter") or 0  # the shared expert's width (0: none)
     ids = np.asarray(ids)
     counts = np.bincount(ids[ids >= 0].reshape(-1), minlength=E)
     N = int(counts.sum())
+    S = 1 if Is else 0
     Ns = N + S * T
     ne = int((counts > 0).sum()) + S
+    # routed experts' and the shared expert's intermediate widths summed over
+    # rows (h elements) and over non-empty experts (weight columns)
+    h_elems = N * I + T * Is
+    w_cols = (ne - S) * I + Is
     # scales per weight and per activation element: block-FP8 one per 128 x 128
     # weights and per 1 x 128 activations; W8A8 one per output channel (gate/up:
     # per column of H weights, down: per column of I) and per token row
@@ -92,12 +99,11 @@ def algorithmic_units(cfg: dict, ids) -> dict:
     xs = hs = 4.0 / 128 if dt == "fp8" else 0.0
     if dt == "w8a8":
         sc_gu, sc_dn, xs, hs = 4.0 / H, 4.0 / I, 4.0 / H, 4.0 / I
-    gu_bytes = ne * 2 * H * I * (bw + sc_gu) + T * H * (bw + xs) + Ns * I * (bw + hs)
-    dn_bytes = ne * I * H * (bw + sc_dn) + Ns * I * (bw + hs) + Ns * H * by
-    layer_bytes = (ne * H * I * (2 * (bw + sc_gu) + bw + sc_dn) + T * H * (bw + xs) + T * H * by +
-                   T * K * 8)
+    gu_bytes = w_cols * 2 * H * (bw + sc_gu) + T * H * (bw + xs) + h_elems * (bw + hs)
+    dn_bytes = w_cols * H * (bw + sc_dn) + h_elems * (bw + hs) + Ns * H * by
+    layer_bytes = (w_cols * H * (2 * (bw + sc_gu) + bw + sc_dn) + T * H * (bw + xs) + T * H * by + T * K * 8)
     return dict(N=N, Ns=Ns, nonempty=ne, gu_bytes=gu_bytes, dn_bytes=dn_bytes, layer_bytes=layer_bytes,
-                gu_flops=4.0 * H * I * Ns, dn_flops=2.0 * H * I * Ns, layer_flops=6.0 * H * I * Ns)
+                gu_flops=4.0 * H * h_elems, dn_flops=2.0 * H * h_elems, layer_flops=6.0 * H * h_elems)
 
 
 def cpu_baseline(p: dict, cfg: dict, budget_s: float = 12.0) -> dict:
@@ -193,6 +199,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="the MFMA rate sustained with no memory traffic (bf16, fp8, int8) and its shader clock")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph and replayed (graph_ms_per_step)")
     ap.add_argument("--sweep", action="store_true",
@@ -213,6 +221,15 @@ def main():
 
     if args.sweep:
         sweep(args)
+        return
+    if args.mfma_ceiling:
+        from moe_expert_ffn_afd_amd import afd
+
+        res = {}
+        for dt, spec in (("bf16", PEAK_TFLOPS["bf16"]), ("fp8", PEAK_TFLOPS["fp8"]), ("w8a8", PEAK_TFLOPS["w8a8"])):
+            tf, ghz = afd.afd_ffn_mfma_peak(dt)
+            res[dt] = {"tflops": round(tf, 1), "clock_ghz": round(ghz, 3), "frac_of_spec": round(tf / spec, 4)}
+        print(json.dumps({"mfma_ceiling": res, "note": "8 waves per CU, register operands, no memory traffic"}))
         return
     if args.copy_calibration:
         n = 1 << 30

@@ -81,8 +81,11 @@ typedef enum {
  *                 [E, I] fp32 per-column scales (AFD_DTYPE_W8A8), else NULL
  *   s_down        [E, I/128, H/128] (AFD_DTYPE_FP8_BLOCK), [E, H] (AFD_DTYPE_W8A8),
  *                 else NULL
- * Optional shared expert (shared_inter > 0; applied to every token with
- * weight 1 after the routed sum; shared_inter must equal inter):
+ * Optional shared expert (shared_inter > 0, a multiple of 128 of at most
+ * 16 x inter; applied to every token with weight 1 after the routed sum; one of
+ * another width than the routed experts runs as ceil(shared_inter / inter)
+ * parts of width inter, the last zero-padded, whose outputs the combine adds
+ * in order):
  *   sh_gate, sh_up [H, shared_inter], sh_down [shared_inter, H], and for FP8
  *   sh_s_gate, sh_s_up [H/128, shared_inter/128], sh_s_down [shared_inter/128, H/128]
  *   (W8A8: sh_s_gate, sh_s_up [shared_inter], sh_s_down [H]).
@@ -262,6 +265,19 @@ afd_status afd_ffn_routing_errors(afd_ffn_t *handle, int32_t *count, void *strea
  * only the stages it needs.  AFD_ERR_INVALID_ARG for a NULL handle or a bit
  * at AFD_NUM_STAGES or above.  The setting applies to later forwards.
  */
+/*
+ * Measurement helper (not part of a forward): the MFMA rate this device
+ * sustains with no memory traffic, the ceiling the grouped GEMMs' MFMA
+ * fractions are read against.  8 waves per CU each keep independent MFMA
+ * chains of the dtype's kind busy for `iters` rounds (AFD_DTYPE_BF16: 32x32x16
+ * bf16; AFD_DTYPE_FP8_BLOCK: 16x16x128 e4m3, the block-scaled kind;
+ * AFD_DTYPE_W8A8: 16x16x64 int8).  *tflops: flops (int8: operations) per
+ * second over the launch; *clock_ghz: the shader clock the loop ran at (shader
+ * clock counter against the constant 100 MHz counter).  Allocates a few bytes,
+ * synchronises the device; AFD_ERR_UNSUPPORTED for fp32.
+ */
+afd_status afd_ffn_mfma_peak(int32_t dtype, int32_t device, int32_t iters, double *tflops, double *clock_ghz);
+
 #define AFD_NUM_STAGES 5
 afd_status afd_ffn_set_timing(afd_ffn_t *handle, int32_t enable);
 afd_status afd_ffn_set_timing_stages(afd_ffn_t *handle, uint32_t stage_mask);

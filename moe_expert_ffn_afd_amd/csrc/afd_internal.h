@@ -22,7 +22,10 @@
 //  panel p at index 2p and up panel p at 2p + 1 (a wave streams both with one
 //  base pointer and finds gate and up of the same h column in the same
 //  accumulator register).  Down weights of one expert are H / 32 panels.
-//  The shared expert, if any, is stored as expert index E.
+//  The shared expert, if any, is stored as experts E .. E + S - 1: its
+//  intermediate dimension cut into S parts of width I (the last zero-padded;
+//  SwiGLU separates along it, and zero columns and rows add exactly nothing),
+//  each run as an expert of its own over all T tokens.
 //
 //  Block-FP8 scales: gate [E+S][H/128][I/128], up likewise, down
 //  [E+S][I/128][H/128] (fp32, copies of the caller's); one super-step is one
@@ -34,9 +37,9 @@
 //    chunk_base[n_chunks][E]          first sorted row of each (chunk, expert)
 //    sorted_assign[N_max], row_of[N_max]
 //    mtiles[max_mtiles] (int4) x 2    light and heavy lists {expert, first row, rows, 0}
-//    h   [N_max + T_max, I]           routed rows in sorted order, then the
-//                                     shared expert's rows (token order) at
-//                                     row N_max; bf16 | e4m3 | fp32
+//    h   [N_max + S T_max, I]         routed rows in sorted order, then the
+//                                     shared expert's parts' rows (part-major,
+//                                     token order) from row N_max; bf16 | e4m3 | fp32
 //    FP8 activation scales, step-major over the same rows (one 128-deep
 //    block per "step", so a tile's scales of one step are contiguous):
 //    xs  [H/128][N_max + T_max]       the caller's 1x128 hidden scales,
@@ -69,6 +72,8 @@ constexpr int kDispatchLdsInts = 12288;  // chunk x expert counters held in LDS 
 constexpr int kMaxExperts = 512;
 constexpr int kDispatchFuseSlots = 4096;  // up to this many flat slots: one dispatch launch
 constexpr int kMaxTopK = 32;
+constexpr int kMaxSharedParts = 16;  // a shared expert of up to 16 times the routed experts' width
+constexpr int kMaxRowsPerToken = kMaxTopK + kMaxSharedParts;  // rows the combine adds per token
 
 struct DispatchParams {
   const int32_t* ids;      // [n_flat]
@@ -87,6 +92,8 @@ struct DispatchParams {
   int32_t heavy_min_rows;  // experts with at least this many rows are heavy
   int32_t shared_rows;     // T when a shared expert exists, else 0
   int32_t shared_row0;     // first shared row (N_max)
+  int32_t shared_parts;    // the shared expert's parts of width I (experts E .. E + parts - 1), rows
+                           // shared_row0 + v T + t for part v and token t
   int4* mtiles;            // light tile list
   int4* mtiles_heavy;      // heavy tile list
   int32_t* num_mtiles;     // [4]: light tiles, heavy tiles, light workgroups of the mixed
@@ -126,7 +133,8 @@ struct GemmParams {
   const int32_t* num_mtiles2;
   const int32_t* sorted_assign;  // row -> flat slot (gate/up gather)
   int32_t top_k;
-  int32_t shared_row0;           // rows >= this are shared-expert rows (token = row - shared_row0)
+  int32_t shared_row0;           // rows >= this are shared-expert rows: token (row - shared_row0) % shared_tokens
+  int32_t shared_tokens;         // T (the shared expert's parts lie one after another)
   int32_t gather;                // 1: A row = hidden[token of row]; 0: A row = a[row]
   const uint8_t* a;              // activation rows
   int64_t a_bytes;               // size of the activation buffer (< 2^31)
@@ -178,6 +186,7 @@ struct ScaleGatherParams {
   int32_t num_experts;
   int32_t routed_max;            // T * K of this call (upper bound of the routed rows)
   int32_t shared_row0;           // N_max with a shared expert, else -1
+  int32_t shared_parts;          // the shared expert's parts (rows shared_row0 + v T + t)
   float* dst;                    // [ks][ld]
   int32_t ld;
 };
@@ -190,6 +199,8 @@ struct CombineParams {
   int32_t top_k;
   int32_t hidden;
   int32_t shared_row0;     // -1 when no shared expert
+  int32_t shared_parts;    // the shared expert's parts: rows shared_row0 + v shared_stride + t, v in order
+  int32_t shared_stride;   // T
   uint8_t* out;            // [T, H]
 };
 
@@ -199,6 +210,7 @@ struct F32Params {
   const int32_t* sorted_assign;
   int32_t top_k;
   int32_t shared_row0;
+  int32_t shared_tokens;    // T: shared rows map to tokens (row - shared_row0) % T
   int32_t gather;
   const float* a;           // [*, K] rows
   const float* w0;          // gate (gate/up) or down: [E+S][K][N]
@@ -257,6 +269,9 @@ hipError_t launch_gemm_ring(bool gate_up, bool stream_weights, bool int8, const 
 int ring_rows(bool heavy);
 hipError_t launch_gemm_f32(bool gate_up, const F32Params& p, int grid, hipStream_t s);
 hipError_t launch_quant_rows(const QuantParams& p, hipStream_t s);
+// calib.hip: the MFMA rate sustained with no memory traffic (kind 0 bf16,
+// 1 e4m3, 2 int8) on num_cus CUs, and the shader clock meanwhile; synchronous
+hipError_t mfma_peak(int kind, int num_cus, int iters, double* tflops, double* clock_ghz);
 // one workgroup per CU of num_cus (all resident at once); stream_weights and
 // int8 as for launch_gemm_ring
 hipError_t launch_fused(bool stream_weights, bool int8, const FusedParams& f, int num_cus, hipStream_t s);

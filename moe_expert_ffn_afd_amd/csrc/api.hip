@@ -181,12 +181,15 @@ afd_status check_config(const afd_ffn_config* c) {
   if (c->top_k > kMaxTopK) return fail(AFD_ERR_UNSUPPORTED, "top_k %d > %d", c->top_k, kMaxTopK);
   if ((int64_t)c->max_tokens * c->top_k >= (1ll << 26))
     return fail(AFD_ERR_UNSUPPORTED, "max_tokens * top_k must stay below 2^26");
-  if (c->shared_inter < 0 || (c->shared_inter > 0 && c->shared_inter != c->inter))
-    return fail(AFD_ERR_UNSUPPORTED, "shared_inter must be 0 or equal to inter");
+  if (c->shared_inter < 0 || c->shared_inter % 128 ||
+      (int64_t)c->shared_inter > (int64_t)kMaxSharedParts * c->inter)
+    return fail(AFD_ERR_UNSUPPORTED, "shared_inter (%d) must be 0 or a multiple of 128 of at most %d x inter",
+                c->shared_inter, kMaxSharedParts);
   {
     // the GEMMs and the combine address rows (hidden, h, y) with 32-bit buffer offsets
     const int64_t es = c->dtype == kF32 ? 4 : c->dtype == kBF16 ? 2 : 1;
-    const int64_t rows = (int64_t)c->max_tokens * c->top_k + (c->shared_inter > 0 ? c->max_tokens : 0);
+    const int64_t parts = (c->shared_inter + c->inter - 1) / c->inter;  // the shared expert's parts of width I
+    const int64_t rows = (int64_t)c->max_tokens * c->top_k + parts * c->max_tokens;
     const int64_t lim = (1ll << 31) - (1ll << 24);
     const int64_t ys = c->dtype == kF32 ? 4 : 2;  // expert outputs y are bf16 | fp32
     const int64_t hs = c->dtype == kW8A8 ? 2 : es;  // W8A8 keeps h in bf16 before re-quantising it
@@ -224,9 +227,9 @@ afd_status check_config(const afd_ffn_config* c) {
 // null: sizes only) and return its size in bytes.
 int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w) {
   const int64_t nmax = (int64_t)tcap * a->K;
-  const int64_t rows = nmax + (a->S ? tcap : 0);
+  const int64_t rows = nmax + (int64_t)a->S * tcap;  // routed rows, then the shared expert's parts
   const int64_t max_chunks = (nmax + 1023) / 1024;
-  const int64_t max_mtiles = nmax / 32 + a->E + (a->S ? (tcap + 31) / 32 : 0) + 1;
+  const int64_t max_mtiles = nmax / 32 + a->E + (int64_t)a->S * ((tcap + 31) / 32) + 1;
   const int es = esize_of(a->dtype);
   const int ys = a->dtype == kF32 ? 4 : 2;
   const bool w8 = a->dtype == kW8A8;
@@ -286,6 +289,27 @@ afd_status alloc_workspace(afd_ffn* a) {
   return AFD_OK;
 }
 
+// Part v of the shared expert (its intermediate columns [v I, v I + I), the
+// last part zero-padded to width I) as one expert's matrices: gate and up
+// [H, I] from sh_gate, sh_up [H, shared_inter], down [I, H] from the rows of
+// sh_down [shared_inter, H]; es bytes per element.  SwiGLU separates along the
+// intermediate dimension, and zero columns and rows add exactly nothing.
+afd_status copy_shared_part(const afd_ffn_config* c, const afd_ffn* a, int v, int es, uint8_t* g, uint8_t* u,
+                            uint8_t* d) {
+  const int H = a->H, I = a->I, Is = c->shared_inter;
+  const int wv = std::min(I, Is - v * I);
+  const int64_t mat = (int64_t)H * I * es;
+  if (wv < I)
+    for (uint8_t* q : {g, u, d}) AFD_HIP(hipMemset(q, 0, mat));
+  AFD_HIP(hipMemcpy2D(g, (size_t)I * es, (const uint8_t*)c->sh_gate + (int64_t)v * I * es, (size_t)Is * es,
+                      (size_t)wv * es, H, hipMemcpyDeviceToDevice));
+  AFD_HIP(hipMemcpy2D(u, (size_t)I * es, (const uint8_t*)c->sh_up + (int64_t)v * I * es, (size_t)Is * es,
+                      (size_t)wv * es, H, hipMemcpyDeviceToDevice));
+  AFD_HIP(hipMemcpy(d, (const uint8_t*)c->sh_down + (int64_t)v * I * H * es, (int64_t)wv * H * es,
+                    hipMemcpyDeviceToDevice));
+  return AFD_OK;
+}
+
 afd_status pack_weights(const afd_ffn_config* c, afd_ffn* a) {
   WeightStore* w = a->w;
   const int E = a->E, ES = a->E + a->S, H = a->H, I = a->I, dt = a->dtype;
@@ -306,11 +330,9 @@ afd_status pack_weights(const afd_ffn_config* c, afd_ffn* a) {
     AFD_HIP(hipMemcpy(w->gu, c->w_gate, mat * E, hipMemcpyDeviceToDevice));
     AFD_HIP(hipMemcpy(w->up, c->w_up, mat * E, hipMemcpyDeviceToDevice));
     AFD_HIP(hipMemcpy(w->dn, c->w_down, mat * E, hipMemcpyDeviceToDevice));
-    if (a->S) {
-      AFD_HIP(hipMemcpy(w->gu + mat * E, c->sh_gate, mat, hipMemcpyDeviceToDevice));
-      AFD_HIP(hipMemcpy(w->up + mat * E, c->sh_up, mat, hipMemcpyDeviceToDevice));
-      AFD_HIP(hipMemcpy(w->dn + mat * E, c->sh_down, mat, hipMemcpyDeviceToDevice));
-    }
+    for (int v = 0; v < a->S; ++v)
+      if ((st = copy_shared_part(c, a, v, 4, w->gu + mat * (E + v), w->up + mat * (E + v), w->dn + mat * (E + v))))
+        return st;
     w->gu_expert_bytes = w->dn_expert_bytes = mat;
     return AFD_OK;
   }
@@ -322,10 +344,23 @@ afd_status pack_weights(const afd_ffn_config* c, afd_ffn* a) {
   AFD_HIP(launch_pack(dt, true, c->w_gate, c->w_up, (int64_t)H * I, E, H, I, w->gu, w->gu_expert_bytes, 0));
   AFD_HIP(launch_pack(dt, false, c->w_down, nullptr, (int64_t)I * H, E, I, H, w->dn, w->dn_expert_bytes, 0));
   if (a->S) {
-    AFD_HIP(launch_pack(dt, true, c->sh_gate, c->sh_up, (int64_t)H * I, 1, H, I, w->gu + w->gu_expert_bytes * E,
-                        w->gu_expert_bytes, 0));
-    AFD_HIP(launch_pack(dt, false, c->sh_down, nullptr, (int64_t)I * H, 1, I, H, w->dn + w->dn_expert_bytes * E,
-                        w->dn_expert_bytes, 0));
+    // each part of the shared expert, zero-padded to width I in a staging
+    // buffer, then packed as expert E + v
+    const int64_t mat = (int64_t)H * I * es;
+    uint8_t* stg = nullptr;
+    if ((st = mal(&stg, 3 * mat))) return st;
+    for (int v = 0; v < a->S && st == AFD_OK; ++v) {
+      st = copy_shared_part(c, a, v, es, stg, stg + mat, stg + 2 * mat);
+      if (st == AFD_OK &&
+          (launch_pack(dt, true, stg, stg + mat, (int64_t)H * I, 1, H, I, w->gu + w->gu_expert_bytes * (E + v),
+                       w->gu_expert_bytes, 0) != hipSuccess ||
+           launch_pack(dt, false, stg + 2 * mat, nullptr, (int64_t)I * H, 1, I, H,
+                       w->dn + w->dn_expert_bytes * (E + v), w->dn_expert_bytes, 0) != hipSuccess ||
+           hipDeviceSynchronize() != hipSuccess))
+        st = fail(AFD_ERR_HIP, "packing part %d of the shared expert failed", v);
+    }
+    (void)hipFree(stg);
+    if (st) return st;
   }
   if (dt == kW8A8) {
     // per output channel: gate, up [E+S][I], down [E+S][H]
@@ -338,10 +373,17 @@ afd_status pack_weights(const afd_ffn_config* c, afd_ffn* a) {
     AFD_HIP(hipMemcpy(w->sg, c->s_gate, sgu * E, hipMemcpyDeviceToDevice));
     AFD_HIP(hipMemcpy(w->su, c->s_up, sgu * E, hipMemcpyDeviceToDevice));
     AFD_HIP(hipMemcpy(w->sd, c->s_down, sdn * E, hipMemcpyDeviceToDevice));
-    if (a->S) {
-      AFD_HIP(hipMemcpy((uint8_t*)w->sg + sgu * E, c->sh_s_gate, sgu, hipMemcpyDeviceToDevice));
-      AFD_HIP(hipMemcpy((uint8_t*)w->su + sgu * E, c->sh_s_up, sgu, hipMemcpyDeviceToDevice));
-      AFD_HIP(hipMemcpy((uint8_t*)w->sd + sdn * E, c->sh_s_down, sdn, hipMemcpyDeviceToDevice));
+    for (int v = 0; v < a->S; ++v) {
+      // part v: the gate and up scales of its columns (1 for the padding, whose
+      // codes are 0), the down scales (per output column) unchanged
+      const int wv = std::min(I, c->shared_inter - v * I);
+      float* g = (float*)((uint8_t*)w->sg + sgu * (E + v));
+      float* u = (float*)((uint8_t*)w->su + sgu * (E + v));
+      AFD_HIP(hipMemsetD32((hipDeviceptr_t)g, 0x3f800000, I));
+      AFD_HIP(hipMemsetD32((hipDeviceptr_t)u, 0x3f800000, I));
+      AFD_HIP(hipMemcpy(g, c->sh_s_gate + (int64_t)v * I, 4ll * wv, hipMemcpyDeviceToDevice));
+      AFD_HIP(hipMemcpy(u, c->sh_s_up + (int64_t)v * I, 4ll * wv, hipMemcpyDeviceToDevice));
+      AFD_HIP(hipMemcpy((uint8_t*)w->sd + sdn * (E + v), c->sh_s_down, sdn, hipMemcpyDeviceToDevice));
     }
   }
   if (dt == kFP8) {
@@ -353,10 +395,21 @@ afd_status pack_weights(const afd_ffn_config* c, afd_ffn* a) {
     AFD_HIP(hipMemcpy(w->sg, c->s_gate, sblk * E, hipMemcpyDeviceToDevice));
     AFD_HIP(hipMemcpy(w->su, c->s_up, sblk * E, hipMemcpyDeviceToDevice));
     AFD_HIP(hipMemcpy(w->sd, c->s_down, sblk * E, hipMemcpyDeviceToDevice));
-    if (a->S) {
-      AFD_HIP(hipMemcpy((uint8_t*)w->sg + sblk * E, c->sh_s_gate, sblk, hipMemcpyDeviceToDevice));
-      AFD_HIP(hipMemcpy((uint8_t*)w->su + sblk * E, c->sh_s_up, sblk, hipMemcpyDeviceToDevice));
-      AFD_HIP(hipMemcpy((uint8_t*)w->sd + sblk * E, c->sh_s_down, sblk, hipMemcpyDeviceToDevice));
+    for (int v = 0; v < a->S; ++v) {
+      // part v: its columns' blocks of the gate and up grids [H/128][Is/128]
+      // and its rows' blocks of the down grid [Is/128][H/128] (1 for the
+      // padding blocks, whose codes are 0)
+      const int wb = std::min(I, c->shared_inter - v * I) / 128, ib = I / 128, isb = c->shared_inter / 128;
+      float* g = (float*)((uint8_t*)w->sg + sblk * (E + v));
+      float* u = (float*)((uint8_t*)w->su + sblk * (E + v));
+      float* dd = (float*)((uint8_t*)w->sd + sblk * (E + v));
+      for (float* q : {g, u, dd}) AFD_HIP(hipMemsetD32((hipDeviceptr_t)q, 0x3f800000, (H / 128) * ib));
+      AFD_HIP(hipMemcpy2D(g, 4ll * ib, c->sh_s_gate + (int64_t)v * ib, 4ll * isb, 4ll * wb, H / 128,
+                          hipMemcpyDeviceToDevice));
+      AFD_HIP(hipMemcpy2D(u, 4ll * ib, c->sh_s_up + (int64_t)v * ib, 4ll * isb, 4ll * wb, H / 128,
+                          hipMemcpyDeviceToDevice));
+      AFD_HIP(hipMemcpy(dd, c->sh_s_down + (int64_t)v * ib * (H / 128), 4ll * wb * (H / 128),
+                        hipMemcpyDeviceToDevice));
     }
   }
   AFD_HIP(hipDeviceSynchronize());
@@ -485,6 +538,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
   d.bm_heavy = bm_heavy;
   d.heavy_min_rows = heavy_min;
   d.shared_rows = a->S ? T : 0;
+  d.shared_parts = a->S;
   d.shared_row0 = (int32_t)nmax;
   d.mtiles = w.mtiles;
   d.mtiles_heavy = w.mtiles_heavy;
@@ -514,6 +568,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
     sg.num_experts = E;
     sg.routed_max = (int32_t)n_flat;
     sg.shared_row0 = a->S ? (int32_t)nmax : -1;
+    sg.shared_parts = a->S;
     sg.dst = w.x_scales;
     sg.ld = (int32_t)w.h_rows;
     AFD_HIP(launch_gather_scales(sg, s));
@@ -521,8 +576,9 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
   if ((st = mark(2))) return st;  // (fused: the boundary before its one launch)
 
   // upper bounds of the routed + shared m-tiles of this call, per list
-  const int64_t mt_bound = n_flat / bm + std::min<int64_t>(E, n_flat) + (a->S ? (T + bm - 1) / bm : 0) + 1;
-  const int64_t mth_bound = light_only ? 0 : n_flat / heavy_min + (a->S ? (T + bm_heavy - 1) / bm_heavy : 0) + 1;
+  const int64_t mt_bound = n_flat / bm + std::min<int64_t>(E, n_flat) + (int64_t)a->S * ((T + bm - 1) / bm) + 1;
+  const int64_t mth_bound =
+      light_only ? 0 : n_flat / heavy_min + (int64_t)a->S * ((T + bm_heavy - 1) / bm_heavy) + 1;
   const int64_t rows_ld_h = (int64_t)I * (w8 ? 2 : esize_of(dt));  // W8A8: bf16 h before re-quantisation
   const int64_t h_rows = w.h_rows;
   const int occupancy_wgs = 4;  // resident workgroups per CU the persistent grids aim for
@@ -535,6 +591,8 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
   cp.top_k = K;
   cp.hidden = H;
   cp.shared_row0 = a->S ? (int32_t)nmax : -1;
+  cp.shared_parts = a->S;
+  cp.shared_stride = T;
   cp.out = (uint8_t*)out;
   QuantParams qp{};  // W8A8: h -> int8 codes with one scale per row, for the down GEMM
   qp.h = w.h;
@@ -545,7 +603,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
   qp.num_experts = E;
   qp.routed_max = (int32_t)n_flat;
   qp.shared_row0 = a->S ? (int32_t)nmax : -1;
-  qp.shared_rows = a->S ? T : 0;
+  qp.shared_rows = a->S * T;  // every part's rows, one after another
   qp.h8 = (int8_t*)w.h8;
   qp.hsc = w.h_scales;
 
@@ -556,6 +614,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
     g.sorted_assign = w.sorted_assign;
     g.top_k = K;
     g.shared_row0 = (int32_t)nmax;
+    g.shared_tokens = T;
     g.gather = 1;
     g.a = (const float*)hidden;
     g.w0 = (const float*)a->w->gu;
@@ -584,6 +643,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
     g.sorted_assign = w.sorted_assign;
     g.top_k = K;
     g.shared_row0 = (int32_t)nmax;
+    g.shared_tokens = T;
     // gate/up: A = hidden rows gathered by token
     g.gather = 1;
     g.a = (const uint8_t*)hidden;
@@ -752,7 +812,7 @@ afd_status afd_ffn_create(const afd_ffn_config* cfg, afd_ffn_t** out_handle) {
   a->E = cfg->num_experts;
   a->K = cfg->top_k;
   a->Tmax = cfg->max_tokens;
-  a->S = cfg->shared_inter > 0 ? 1 : 0;
+  a->S = (cfg->shared_inter + cfg->inter - 1) / cfg->inter;  // the shared expert's parts of width I
   a->dtype = cfg->dtype;
   a->device = cfg->device;
   int cus = 0;
@@ -868,6 +928,19 @@ afd_status afd_ffn_set_concurrency(afd_ffn_t* a, int32_t streams) {
   if (streams < 1 || streams > a->num_cus)
     return fail(AFD_ERR_INVALID_ARG, "concurrency %d outside [1, %d]", streams, a->num_cus);
   a->concurrency = streams;
+  return AFD_OK;
+}
+
+afd_status afd_ffn_mfma_peak(int32_t dtype, int32_t device, int32_t iters, double* tflops, double* clock_ghz) {
+  g_last_error.clear();
+  if (!tflops || !clock_ghz || iters <= 0) return fail(AFD_ERR_INVALID_ARG, "NULL output or iters <= 0");
+  const int kind = dtype == kBF16 ? 0 : dtype == kFP8 ? 1 : dtype == kW8A8 ? 2 : -1;
+  if (kind < 0) return fail(AFD_ERR_UNSUPPORTED, "dtype %d has no MFMA peak measurement", dtype);
+  DeviceGuard dg(device);
+  if (!dg.ok) return fail(AFD_ERR_HIP, "cannot select device %d", device);
+  int cus = 0;
+  AFD_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device));
+  AFD_HIP(mfma_peak(kind, cus, iters, tflops, clock_ghz));
   return AFD_OK;
 }
 

@@ -5,7 +5,8 @@
 // outputs ("FastAFD" structured summary, System Design item 3: push-back of
 // the MoE result; vLLM AFD blog, FFN service returns the computed output):
 //   out[t] = sum_k w[t,k] * y[row_of[t,k]]   (k in order, slots with row -1
-//            skipped)  + y[shared_row0 + t]  (shared expert, weight 1)
+//            skipped)  + sum_v y[shared_row0 + v T + t]  (the shared expert's
+//            parts, weight 1)
 // accumulated in fp32 in a fixed order, so the result does not depend on
 // scheduling.  The token's rows are compacted first (dropped slots cost
 // nothing), then read with 16-byte coalesced loads, up to 8 rows in flight per
@@ -17,8 +18,8 @@
 namespace afd {
 
 // Token t of the combine by a group of `nthr` threads (a multiple of 64; this
-// thread is number `tid` of it) with its own LDS lists rows[kMaxTopK + 1],
-// ws[kMaxTopK + 1] and nrows[1].  Every thread of the workgroup calls it the
+// thread is number `tid` of it) with its own LDS lists rows[kMaxRowsPerToken],
+// ws[kMaxRowsPerToken] and nrows[1].  Every thread of the workgroup calls it the
 // same number of times (it holds two workgroup barriers); a thread whose group
 // has no token this round passes active = false.  Ends with every thread past
 // the reads of its group's lists.
@@ -38,11 +39,12 @@ __device__ __forceinline__ void combine_rows(const CombineParams& p, const int t
     }
     const int n = __popcll(mask);
     if (tid == 0) {
-      if (p.shared_row0 >= 0) {
-        rows[n] = p.shared_row0 + t;
-        ws[n] = 1.0f;
+      const int parts = p.shared_row0 >= 0 ? p.shared_parts : 0;
+      for (int v = 0; v < parts; ++v) {  // the shared expert's parts, in order
+        rows[n + v] = p.shared_row0 + v * p.shared_stride + t;
+        ws[n + v] = 1.0f;
       }
-      *nrows = n + (p.shared_row0 >= 0 ? 1 : 0);
+      *nrows = n + parts;
     }
   }
   __syncthreads();

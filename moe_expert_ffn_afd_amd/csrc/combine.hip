@@ -6,8 +6,8 @@ namespace afd {
 
 template <int DT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  __shared__ int rows[kMaxTopK + 1];
-  __shared__ float ws[kMaxTopK + 1];
+  __shared__ int rows[kMaxRowsPerToken];
+  __shared__ float ws[kMaxRowsPerToken];
   __shared__ int nrows;
   combine_rows<DT>(p, blockIdx.x, true, threadIdx.x, blockDim.x, rows, ws, &nrows);
 }

@@ -228,12 +228,13 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
     }
     const bool sh_heavy = p.shared_rows >= heavy_min;
     const int bms = sh_heavy ? p.bm_heavy : bm_light;
-    const int n_shared = (p.shared_rows + bms - 1) / bms;
+    const int per_part = (p.shared_rows + bms - 1) / bms;
+    const int n_shared = per_part * p.shared_parts;
     int4* list = sh_heavy ? p.mtiles_heavy : p.mtiles;
     const int base = sh_heavy ? n_heavy : n_light;
     for (int j = tid; j < n_shared; j += kDispatchThreads) {
-      const int r0 = j * bms;
-      list[base + j] = make_int4(E, p.shared_row0 + r0, min(bms, p.shared_rows - r0), 0);
+      const int v = j / per_part, r0 = (j - v * per_part) * bms;
+      list[base + j] = make_int4(E + v, p.shared_row0 + v * p.shared_rows + r0, min(bms, p.shared_rows - r0), 0);
     }
     if (tid == 0) {
       const int nl = n_light + (sh_heavy ? 0 : n_shared), nh = n_heavy + (sh_heavy ? n_shared : 0);
@@ -277,7 +278,8 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_scatter_kernel(Disp
 // (dst[c][row]), so that one GEMM step reads a tile's scales as one contiguous
 // run.  One thread per (row, step c = blockIdx.y): coalesced stores, reads
 // from the small, cache-resident source.  blockIdx.z = 0: routed rows (token
-// of row r = sorted_assign[r] / K); 1: the shared expert's rows (token order).
+// of row r = sorted_assign[r] / K); 1 + v: part v of the shared expert's rows
+// (token order).
 __global__ __launch_bounds__(256) void gather_scales_kernel(ScaleGatherParams p) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   const int c = blockIdx.y;
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(256) void gather_scales_kernel(ScaleGatherParams p)
     token = p.sorted_assign[i] / p.top_k;
   } else {
     if (i >= p.tokens) return;
-    row = p.shared_row0 + i;
+    row = p.shared_row0 + (int)(blockIdx.z - 1) * p.tokens + i;
     token = i;
   }
   p.dst[(int64_t)c * p.ld + row] = p.src[(int64_t)token * p.ks + c];
@@ -297,7 +299,8 @@ __global__ __launch_bounds__(256) void gather_scales_kernel(ScaleGatherParams p)
 hipError_t launch_gather_scales(const ScaleGatherParams& p, hipStream_t s) {
   const int n = std::max(p.routed_max, p.shared_row0 >= 0 ? p.tokens : 0);
   if (n <= 0 || p.ks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_scales_kernel, dim3((n + 255) / 256, p.ks, p.shared_row0 >= 0 ? 2 : 1), dim3(256), 0, s,
+  hipLaunchKernelGGL(gather_scales_kernel, dim3((n + 255) / 256, p.ks, p.shared_row0 >= 0 ? 1 + p.shared_parts : 1),
+                     dim3(256), 0, s,
                      p);
   return hipGetLastError();
 }

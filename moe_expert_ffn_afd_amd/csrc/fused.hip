@@ -184,11 +184,14 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(FusedParams f) 
       }
       const bool sh_heavy = d.shared_rows >= d.heavy_min_rows;
       const int bms = sh_heavy ? d.bm_heavy : d.bm_light;
-      const int n_shared = (d.shared_rows + bms - 1) / bms;
+      const int per_part = (d.shared_rows + bms - 1) / bms;
+      const int n_shared = per_part * d.shared_parts;
       int4* list = sh_heavy ? d.mtiles_heavy : d.mtiles;
       const int base = sh_heavy ? n_heavy : n_light;
-      for (int j = tid; j < n_shared; j += kFusedThreads)
-        list[base + j] = make_int4(E, d.shared_row0 + j * bms, min(bms, d.shared_rows - j * bms), 0);
+      for (int j = tid; j < n_shared; j += kFusedThreads) {
+        const int v = j / per_part, r0 = (j - v * per_part) * bms;
+        list[base + j] = make_int4(E + v, d.shared_row0 + v * d.shared_rows + r0, min(bms, d.shared_rows - r0), 0);
+      }
       if (tid == 0) {
         d.num_mtiles[0] = n_light + (sh_heavy ? 0 : n_shared);
         d.num_mtiles[1] = n_heavy + (sh_heavy ? n_shared : 0);
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(FusedParams f) 
   // consecutive rows of a step, 8 items per thread in flight
   {
     const int N = d.offsets[E];
-    const int R = N + d.shared_rows;
+    const int R = N + d.shared_parts * d.shared_rows;
     const int64_t total = (int64_t)f.ks * R, stride = (int64_t)G * kFusedThreads;
     constexpr int kU = 8;
     for (int64_t i0 = (int64_t)b * kFusedThreads + tid; i0 < total; i0 += kU * stride) {
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(FusedParams f) 
         if (i < total) {
           const int c = (int)(i / R), rr = (int)(i - (int64_t)c * R);
           const int row = rr < N ? rr : d.shared_row0 + (rr - N);
-          tok[u] = rr < N ? d.sorted_assign[rr] / K : rr - N;
+          tok[u] = rr < N ? d.sorted_assign[rr] / K : (rr - N) % d.shared_rows;
           tok[u] = tok[u] * f.ks + c;  // source index
           dst[u] = (int64_t)c * f.ld + row;
         }
@@ -292,8 +295,8 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(FusedParams f) 
 
   // ---- C: combine, two tokens at a time per workgroup (4 waves each)
   {
-    __shared__ int c_rows[2][kMaxTopK + 1];
-    __shared__ float c_ws[2][kMaxTopK + 1];
+    __shared__ int c_rows[2][kMaxRowsPerToken];
+    __shared__ float c_ws[2][kMaxRowsPerToken];
     __shared__ int c_n[2];
     const int grp = tid >> 8;
     for (int t0 = 2 * b; t0 < f.tokens; t0 += 2 * G)

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
         if (r < rows && k0 + kk < p.kdim) {
           const int row = row0 + r;
           int64_t src = row;
-          if (p.gather) src = row >= p.shared_row0 ? (row - p.shared_row0) : (p.sorted_assign[row] / p.top_k);
+          if (p.gather) src = row >= p.shared_row0 ? (row - p.shared_row0) % p.shared_tokens : (p.sorted_assign[row] / p.top_k);
           v = p.a[src * p.kdim + k0 + kk];
         }
         as[r][kk] = v;

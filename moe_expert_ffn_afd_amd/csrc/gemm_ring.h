@@ -99,7 +99,10 @@ constexpr int kRingSinkOff = kRingNS * kRingSlotBytes;      // the other waves' 
 constexpr int kRingMetaOff = kRingSinkOff + 1024;           // per wave: source rows of two tasks ahead
 constexpr int kRingMetaBytes = 256;                         // 64 lanes x 4 bytes
 constexpr int kRingLdsBytes = kRingMetaOff + kRingWaves * 2 * kRingMetaBytes;
-constexpr int kRingMB = 4;         // m-tiles per rasterisation block
+#ifndef AFD_RING_MB
+#define AFD_RING_MB 4
+#endif
+constexpr int kRingMB = AFD_RING_MB;  // m-tiles per rasterisation block
 constexpr int kRingMinRounds = 1;  // unrolled rounds per task
 static_assert(kRingLdsBytes <= 160 * 1024 - 4096, "ring exceeds LDS");
 
@@ -208,7 +211,7 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
       const int r = d.row0 + (m < d.rows ? m : 0);
       int src = r;
       if (GATEUP && r < p.shared_row0) src = (m < d.rows ? mi[rt * 16 + tok] : mi[32]) / p.top_k;
-      if (GATEUP && r >= p.shared_row0) src = r - p.shared_row0;
+      if (GATEUP && r >= p.shared_row0) src = (r - p.shared_row0) % p.shared_tokens;
       d.aoff[rt] = valid ? (int)((int64_t)src * p.a_row_bytes) + 32 * kg : 0;
     }
     if (scopy == 0)  // lane i: rows 4i .. 4i+3 of the tile's run in a step

@@ -165,7 +165,7 @@ __device__ __forceinline__ void stream_body(const GemmParams& p, const int rank,
         const int m = mr * 32 + 8 * wave + r8;
         const int r = row0 + (m < rows ? m : 0);
         int src = r;
-        if (p.gather) src = r >= p.shared_row0 ? (r - p.shared_row0) : (p.sorted_assign[r] / p.top_k);
+        if (p.gather) src = r >= p.shared_row0 ? (r - p.shared_row0) % p.shared_tokens : (p.sorted_assign[r] / p.top_k);
         doff[mr] = (int)(src * p.a_row_bytes) + (((lane & 7) + r8) & 7) * 16;
       }
       // fragment read of lane (col, g), chunk 4g + j of row col

@@ -153,7 +153,7 @@ __device__ __forceinline__ void tiled_body(const GemmParams& p, const int b, con
     auto src_row = [&](int r) -> int {  // activation row of tile row r (valid r)
       const int rr = row0 + r;
       if (!p.gather) return rr;
-      return rr >= p.shared_row0 ? rr - p.shared_row0 : p.sorted_assign[rr] / p.top_k;
+      return rr >= p.shared_row0 ? (rr - p.shared_row0) % p.shared_tokens : p.sorted_assign[rr] / p.top_k;
     };
     // Activation copy k of a wave covers rows (wave*A_DMA + k)*ROWS_PER_COPY
     // + [0, ROWS_PER_COPY); lane i -> row +i/SLOTS, LDS part i%SLOTS holding

@@ -59,6 +59,9 @@ def test_validate_config_accepts_good(lib):
     afd.afd_ffn_validate_config(_cfg(max_tokens=(1 << 17) - 4096, top_k=8, hidden=1024, inter=1024))
     afd.afd_ffn_validate_config(_cfg(dtype=afd.AFD_DTYPE_FP8_BLOCK, s_gate=8, s_up=8, s_down=8))
     afd.afd_ffn_validate_config(_cfg(shared_inter=512, sh_gate=0x4000, sh_up=0x5000, sh_down=0x6000))
+    # a shared expert of another width than the routed ones: parts of width inter
+    for si in (128, 768, 2048, 16 * 512):
+        afd.afd_ffn_validate_config(_cfg(shared_inter=si, sh_gate=0x4000, sh_up=0x5000, sh_down=0x6000))
 
 
 @pytest.mark.parametrize("bad, status", [
@@ -75,7 +78,8 @@ def test_validate_config_accepts_good(lib):
     (dict(w_up=0), afd.AFD_ERR_INVALID_ARG),
     (dict(dtype=afd.AFD_DTYPE_FP8_BLOCK), afd.AFD_ERR_INVALID_ARG),          # scales missing
     (dict(s_gate=8, s_up=8, s_down=8), afd.AFD_ERR_INVALID_ARG),              # scales with bf16
-    (dict(shared_inter=256), afd.AFD_ERR_UNSUPPORTED),                        # != inter
+    (dict(shared_inter=200, sh_gate=0x4000, sh_up=0x5000, sh_down=0x6000), afd.AFD_ERR_UNSUPPORTED),  # not x128
+    (dict(shared_inter=17 * 512, sh_gate=0x4000, sh_up=0x5000, sh_down=0x6000), afd.AFD_ERR_UNSUPPORTED),  # > 16 I
     (dict(shared_inter=512), afd.AFD_ERR_INVALID_ARG),                        # shared weights missing
     (dict(device=-1), afd.AFD_ERR_INVALID_ARG),
     (dict(w_gate=0x1008), afd.AFD_ERR_INVALID_ARG),                          # bf16 weights need 16 bytes

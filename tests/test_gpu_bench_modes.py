@@ -60,3 +60,14 @@ def test_sweep_path_matches_oracle():
         compare(out, oracle_out(to_host_problem(q)), cfg["dtype"], what="sweep T=%d" % T)
         assert np.isfinite(out.cpu().numpy()).all()
     layer.close()
+
+
+def test_mfma_ceiling_line():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--mfma-ceiling"], capture_output=True,
+                       text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])["mfma_ceiling"]
+    for dt in ("bf16", "fp8", "w8a8"):
+        say("  mfma ceiling", dt, d[dt])
+        # a real, sustained rate: above a tenth of the spec peak, below the spec peak at 2.4 GHz
+        assert 0.1 < d[dt]["frac_of_spec"] <= 1.02 and 0.5 < d[dt]["clock_ghz"] < 2.6

@@ -47,6 +47,7 @@ CASES = {
     "fp8_one_token": (cfg("fp8", 1, 256, 256, 8, 2, shared=256), 46),
     "w8a8_shared_multi_tile": (cfg("w8a8", 150, 512, 384, 6, 3, shared=384), 47),
     "w8a8_zipf": (cfg("w8a8", 700, 512, 256, 8, 4, routing="zipf"), 48),
+    "fp8_shared_2p5x": (cfg("fp8", 150, 512, 256, 6, 3, shared=640), 53),
 }
 
 

@@ -47,6 +47,15 @@ SMALL_CASES = {
     "w8a8_heavy_ragged": (small("w8a8", 300, 256, 256, 4, 2), 14),
     "w8a8_k32_shared_h384": (small("w8a8", 40, 384, 256, 64, 32, shared=256), 15),
     "w8a8_local_shard": (small("w8a8", 200, 256, 384, 4, 8, routing="local_shard", global_experts=32), 16),
+    # a shared expert of another width than the routed experts: ceil(Is / I)
+    # parts of width I, the last zero-padded (twice, half, one and a half, three
+    # times the routed width; light and heavy shared tiles)
+    "bf16_shared_2x": (small("bf16", 60, 256, 256, 8, 2, shared=512), 17),
+    "bf16_shared_2x_heavy": (small("bf16", 600, 256, 256, 4, 2, shared=512), 18),
+    "fp8_shared_half": (small("fp8", 70, 512, 256, 5, 3, shared=128), 19),
+    "fp8_shared_1p5x_heavy": (small("fp8", 300, 256, 256, 6, 2, shared=384), 20),
+    "w8a8_shared_3x": (small("w8a8", 50, 256, 128, 6, 2, shared=384), 21),
+    "f32_shared_1p5x": (small("f32", 45, 256, 256, 5, 3, shared=384), 22),
 }
 
 

@@ -127,6 +127,7 @@ struct Workspace {
   int32_t *chunk_base = nullptr, *sorted_assign = nullptr, *row_of = nullptr;
   int4* mtiles = nullptr;
   int4* mtiles_heavy = nullptr;
+  int32_t* pool = nullptr;    // [2] the ring GEMMs' tail-pool counters
   uint8_t* h = nullptr;       // bf16 | e4m3 | fp32 (W8A8: bf16, before re-quantisation)
   float* h_scales = nullptr;  // FP8: [I/128][h_rows] step-major; W8A8: [h_rows]
   float* x_scales = nullptr;  // FP8: [H/128][h_rows] hidden scales in sorted-row order; W8A8: [h_rows]
@@ -238,6 +239,7 @@ int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w
   const int64_t o_counts = take(4ll * a->E), o_offsets = take(4ll * (a->E + 1)), o_err = take(4),
                 o_nmt = take(16), o_cb = take(4ll * max_chunks * a->E), o_sa = take(4 * nmax),
                 o_ro = take(4 * nmax), o_mt = take(16ll * max_mtiles), o_mth = take(16ll * max_mtiles),
+                o_pool = take(16),
                 o_h = take(rows * a->I * (w8 ? 2 : es)),
                 o_hs = take(a->dtype == kFP8 ? rows * (a->I / 128) * 4 : w8 ? rows * 4 : 0),
                 o_xs = take(a->dtype == kFP8 ? rows * (a->H / 128) * 4 : w8 ? rows * 4 : 0),
@@ -257,6 +259,7 @@ int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w
     w->row_of = (int32_t*)(base + o_ro);
     w->mtiles = (int4*)(base + o_mt);
     w->mtiles_heavy = (int4*)(base + o_mth);
+    w->pool = (int32_t*)(base + o_pool);
     w->h = base + o_h;
     const bool sc = a->dtype == kFP8 || w8;
     w->h_scales = sc ? (float*)(base + o_hs) : nullptr;
@@ -543,6 +546,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
   d.mtiles = w.mtiles;
   d.mtiles_heavy = w.mtiles_heavy;
   d.num_mtiles = w.num_mtiles;
+  d.pool = fp8 ? w.pool : nullptr;
 
   // the whole layer in one persistent launch (afd_ffn_set_fused; 8-bit layers)
   const bool use_fused = own_ws && a->fused && fp8 && T > 0;
@@ -667,6 +671,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
     g.c_row_bytes = rows_ld_h;
     g.c_scales = w8 ? w.pamax : w.h_scales;  // W8A8: each row's amax per task, for quant.hip
     g.c_scale_ld = (int32_t)w.h_rows;
+    g.pool = fp8 ? w.pool : nullptr;  // the ring GEMMs' tail pool
     GemmParams gu_light = g;
     GemmParams gu_heavy = g;
     gu_heavy.mtiles = w.mtiles_heavy;

@@ -192,6 +192,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
     if (tid == 0) {
       p.offsets[E] = n_routed;
       p.err[0] = bad;
+      if (p.pool) p.pool[0] = p.pool[1] = 0;
     }
   }
   __syncthreads();

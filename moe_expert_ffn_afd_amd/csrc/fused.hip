@@ -165,7 +165,10 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(FusedParams f) 
         d.counts[tid] = cnt_e;
         d.offsets[tid] = off_e;
       }
-      if (tid == 0) d.offsets[E] = N;
+      if (tid == 0) {
+        d.offsets[E] = N;
+        if (d.pool) d.pool[0] = d.pool[1] = 0;
+      }
       // m-tile lists: experts with at least heavy_min_rows rows in heavy tiles
       // of bm_heavy rows, the others in light tiles of bm_light; routed experts
       // in expert order, then the shared expert

@@ -86,6 +86,9 @@ namespace {
 #ifndef AFD_RING_XCD_REMAP
 #define AFD_RING_XCD_REMAP 1
 #endif
+#ifndef AFD_RING_POOL
+#define AFD_RING_POOL 1  // the light list's tail as a pool claimed by the workgroups done first
+#endif
 
 constexpr int kRingWaves = 8;
 constexpr int kRingPanels = 8;
@@ -135,12 +138,12 @@ struct RingDesc {
 
 }  // namespace
 
-// Every task rank + k * stride (k = 0, 1, ...) below n_tiles x n_groups of one
-// m-tile list, in one continuous pipeline.  Every wave of the workgroup calls
-// it with the same arguments.
+// Every task rank + k * stride (k = 0, 1, ...) below min(limit, n_tiles x
+// n_groups) of one m-tile list, in one continuous pipeline.  Every wave of the
+// workgroup calls it with the same arguments.
 template <bool GATEUP, int BM, bool WNT, bool I8>
 __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles, const int n_tiles,
-                                          const int first, const int stride) {
+                                          const int first, const int stride, const int limit) {
   // declared here, not passed in: the copies need pointers known to be in LDS
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   __shared__ float red[kRingWaves * 32];  // gate/up: per-wave token amax
@@ -157,7 +160,7 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
   static_assert(NS >= 2 && (NS - 2) * PER_STAGE < 64, "wait count");
 
   const int nq = p.n_groups;
-  const int count = n_tiles * nq;
+  const int count = min(n_tiles * nq, limit);
   if (first >= count) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -628,17 +631,39 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
 // so a GEMM stage has one tail instead of two.  A workgroup runs tasks rank,
 // rank + G, ... of the two lists in a row; ranks are renumbered so that each
 // XCD owns a contiguous run of tasks (shared rows stay in its L2).
+//
+// The light list's last tasks (up to one per workgroup) form a pool instead:
+// a workgroup done with its own tasks claims them one at a time from a
+// counter (p.pool[stage], zeroed by the dispatch), each in a pipeline of its
+// own.  The static shares end within a task of each other, but CUs do not run
+// equally fast (measured: the last workgroup of a gate/up launch ends about
+// 5 % after the first), so the fast ones take the tail.
 template <bool GATEUP, bool WNT, bool I8>
 __device__ __forceinline__ void ring_stage(const GemmParams& p, const int b, const int G) {
   const int nq = p.n_groups;
   const int nh = uniform(p.num_mtiles2 ? p.num_mtiles2[0] : 0);
   const int nl = uniform(p.num_mtiles[0]);
-  const int th = nh * nq;
+  const int th = nh * nq, tl = nl * nq;
   const int rank = (AFD_RING_XCD_REMAP && G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
-  if (nh > 0) ring_list<GATEUP, 128, WNT, I8>(p, p.mtiles2, nh, rank, G);
+  if (nh > 0) ring_list<GATEUP, 128, WNT, I8>(p, p.mtiles2, nh, rank, G, th);
   // this workgroup's first task past the heavy list, as an index into the light list
   const int first_l = rank >= th ? rank - th : rank + (th - rank + G - 1) / G * G - th;
-  ring_list<GATEUP, 64, WNT, I8>(p, p.mtiles, nl, first_l, G);
+  const int pool = (AFD_RING_POOL && p.pool) ? min(tl, G) : 0;
+  int first = first_l, stride = G, limit = tl - pool;
+  for (;;) {
+    ring_list<GATEUP, 64, WNT, I8>(p, p.mtiles, nl, first, stride, limit);
+    if (pool == 0) break;
+    __shared__ int claim;
+    if (threadIdx.x == 0)
+      claim = __hip_atomic_fetch_add(p.pool + (GATEUP ? 0 : 1), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int c = uniform(claim);
+    __syncthreads();  // claim is rewritten by the next round
+    if (c >= pool) break;
+    first = tl - pool + c;  // one pool task
+    stride = tl;
+    limit = first + 1;
+  }
 }
 
 }  // namespace afd

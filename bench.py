@@ -42,8 +42,9 @@ METRIC = "routed tokens/s per MoE layer on 1 MI355X; % of MFMA/HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GATE_UP_STAGE = 2  # stage index of the grouped GEMM gate/up + SwiGLU in the library's timing
 STAGE_STEPS = 20   # steps with every stage timed, after the timed steps, for the per-stage breakdown
-KERNEL_SOURCES = ("gemm.hip", "gemm_stream.h", "gemm_tiled.hip", "gemm_ring.hip", "gemm_ring.h", "quant.hip",
-                  "quant.h", "fused.hip", "combine.h", "afd_device.h", "afd_internal.h")
+KERNEL_SOURCES = ("gemm.hip", "gemm_stream.h", "gemm_tiled.hip", "gemm_tiled.h", "gemm_ring.hip", "gemm_ring.h",
+                  "quant.hip", "quant.h", "fused.h", "fused.hip", "fused_bf16.hip", "combine.h", "afd_device.h",
+                  "afd_internal.h")
 
 
 def kernel_source_hash() -> str:
@@ -206,7 +207,7 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="time the layer at the workload's shape for T = 64 ... 16384 (one JSON line per T)")
     ap.add_argument("--fused", action="store_true",
-                    help="block-FP8 / W8A8 workloads: each forward as one persistent launch (afd_ffn_set_fused)")
+                    help="bf16 / block-FP8 / W8A8 workloads: each forward as one persistent launch (afd_ffn_set_fused)")
     ap.add_argument("--serial", action="store_true",
                     help="microbatch workloads: run the microbatches one after the other on one stream, "
                          "each on every CU (the baseline the two-stream ping-pong is compared with)")
@@ -375,7 +376,8 @@ def main():
     # both fractions of the same launch, whichever bound the layer sits at
     roof["hbm_frac"] = round(hbm_ach / PEAK_HBM_GBS, 4)
     roof["mfma_frac"] = round(mfma_ach / PEAK_TFLOPS[dt], 4)
-    roof["kernel"] = ("the whole layer: fused_kernel (one persistent launch per forward)" if args.fused
+    roof["kernel"] = (("the whole layer: %s (one persistent launch per forward)"
+                       % ("fused_bf16_kernel" if dt == "bf16" else "fused_kernel")) if args.fused
                       else gate_up_kernels(cfg, T // mbs))
     roof["launch_ms"] = round(gu_launch_ms, 4)
     # launches of this kernel running at once, each on its share of the CUs

@@ -151,14 +151,16 @@ afd_status afd_ffn_set_concurrency(afd_ffn_t *handle, int32_t streams);
  * Design item 3; the "Ablation Results" credit that fusion with about half the
  * step latency of separate kernels).  Here the launch runs the dispatch (every
  * workgroup counting and placing a chunk of the slots), gate/up + SwiGLU, the
- * W8A8 re-quantisation of h, down and the combine, separated by grid barriers;
- * results are bit-identical to the separate launches.  One workgroup per CU of
+ * W8A8 re-quantisation of h, down and the combine, separated by grid barriers
+ * (bf16: each GEMM stage as the light-only or the mixed light + heavy split
+ * the dispatch chooses, as the separate launches do); results are
+ * bit-identical to the separate launches.  One workgroup per CU of
  * the call's share (afd_ffn_set_concurrency), all resident at once: the
  * caller must not keep other kernels occupying those CUs for long (a barrier
  * wait gives up after about a second, counts a timeout and goes on, so the
  * GPU never hangs, but that call's results are wrong; see
- * afd_ffn_fused_errors).  Block-FP8 and W8A8 handles only
- * (AFD_ERR_UNSUPPORTED otherwise); a clone starts with its source's setting;
+ * afd_ffn_fused_errors).  bf16, block-FP8 and W8A8 handles (fp32:
+ * AFD_ERR_UNSUPPORTED); a clone starts with its source's setting;
  * afd_ffn_forward_noalloc always uses separate launches.  With timing on, the
  * whole launch is reported as stage 2 and the other stages as about 0.
  */

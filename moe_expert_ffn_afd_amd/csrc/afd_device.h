@@ -147,6 +147,22 @@ __device__ inline void raw_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Workgroups of the mixed bf16 GEMM launch (cus of them) that take the light
+// list: in proportion to the light list's share of the cost, a multiple of 8
+// where cus is (the same number on every XCD), at least one for a nonempty
+// list of either kind when cus allows two.
+__device__ inline int mixed_light_workgroups(int cus, int nl, int nh) {
+  if (cus <= 0 || nl == 0) return 0;
+  if (nh == 0) return cus;
+  if (cus < 2) return 0;  // one workgroup runs both lists, heavy first
+  const float share = (float)nl / ((float)nl + kHeavyTileCost * (float)nh);
+  int l = (int)(share * (float)cus + 0.5f);
+  if (cus % kXcds == 0 && cus >= 2 * kXcds) {
+    l = (l + kXcds / 2) / kXcds * kXcds;
+    return min(max(l, kXcds), cus - kXcds);
+  }
+  return min(max(l, 1), cus - 1);
+}
 
 }  // namespace dev
 }  // namespace afd

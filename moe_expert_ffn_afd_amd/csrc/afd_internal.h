@@ -222,9 +222,9 @@ struct F32Params {
   float* c;                 // [rows, N]
 };
 
-// The whole layer in one persistent launch (fused.hip; block-FP8 and W8A8):
-// the dispatch's, the GEMM stages' and the combine's parameters plus the
-// grid-barrier state, all in the handle's workspace.
+// The whole layer in one persistent launch (fused.hip: block-FP8 and W8A8;
+// fused_bf16.hip: bf16): the dispatch's, the GEMM stages' and the combine's
+// parameters plus the grid-barrier state, all in the handle's workspace.
 constexpr int kFusedMaxGrid = 512;  // workgroups of one fused launch (one chunk count per thread)
 struct FusedParams {
   DispatchParams d;       // ids, sizes, outputs and tile-list parameters of the dispatch
@@ -234,7 +234,10 @@ struct FusedParams {
   int32_t ld;             // rows of the activation buffers
   int32_t tokens;         // T
   int32_t top_k;
-  GemmParams gu, dn;      // the two GEMM stages (light list in mtiles, heavy in mtiles2)
+  GemmParams gu, dn;      // the two GEMM stages (light list in mtiles; 8-bit: heavy in mtiles2)
+  GemmParams gu_heavy, dn_heavy;  // bf16: the heavy list (LDS-tiled body)
+  GemmParams gu_lo, dn_lo;        // bf16: the light list when the dispatch keeps every expert light
+  int32_t auto_launch;            // bf16: the dispatch chooses light-only or mixed (num_mtiles[3])
   QuantParams qp;         // W8A8: h to int8
   CombineParams cp;
   int32_t* bar;           // [4]: arrivals, departures, timed-out spins, spare (zero between calls)
@@ -278,6 +281,8 @@ hipError_t mfma_peak(int kind, int num_cus, int iters, double* tflops, double* c
 // one workgroup per CU of num_cus (all resident at once); stream_weights and
 // int8 as for launch_gemm_ring
 hipError_t launch_fused(bool stream_weights, bool int8, const FusedParams& f, int num_cus, hipStream_t s);
+// bf16: mr_lo / mr the row fragments of the light-only / mixed launches' light tiles
+hipError_t launch_fused_bf16(int mr_lo, int mr, const FusedParams& f, int num_cus, hipStream_t s);
 hipError_t launch_combine(int dtype, const CombineParams& p, int tokens, hipStream_t s);
 hipError_t launch_pack(int dtype, bool gate_up, const void* w_first, const void* w_second,
                        int64_t expert_in_stride_elems, int experts, int kdim, int ndim,

@@ -245,7 +245,7 @@ int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w
                 o_xs = take(a->dtype == kFP8 ? rows * (a->H / 128) * 4 : w8 ? rows * 4 : 0),
                 o_h8 = take(w8 ? rows * a->I : 0), o_pm = take(w8 ? rows * (a->I / 128) * 4 : 0),
                 o_y = take(rows * a->H * ys);
-  const bool fz = a->dtype == kFP8 || w8;  // the fused launch's state
+  const bool fz = a->dtype != kF32;  // the fused launch's state
   const int64_t fg = fz ? std::min(a->num_cus, kFusedMaxGrid) : 0;
   const int64_t o_bar = take(fz ? 16 : 0), o_fcc = take(4 * fg * a->E), o_fcb = take(4 * fg),
                 o_flb = take(4 * fg * a->E), o_ftot = take(fz ? 4ll * a->E : 0);
@@ -548,8 +548,8 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
   d.num_mtiles = w.num_mtiles;
   d.pool = fp8 ? w.pool : nullptr;
 
-  // the whole layer in one persistent launch (afd_ffn_set_fused; 8-bit layers)
-  const bool use_fused = own_ws && a->fused && fp8 && T > 0;
+  // the whole layer in one persistent launch (afd_ffn_set_fused; not fp32)
+  const bool use_fused = own_ws && a->fused && dt != kF32 && T > 0;
   if ((st = mark(0))) return st;
   if (!use_fused) AFD_HIP(launch_dispatch_count_scan(d, s));
   if ((st = mark(1))) return st;
@@ -761,7 +761,21 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
       fp.local_base = w.local_base;
       fp.totals = w.totals;
       fp.spin_limit = 1 << 20;
-      AFD_HIP(launch_fused(a->concurrency == 1, w8, fp, std::min(cus, w.fused_grid), s));
+      if (fp8) {
+        AFD_HIP(launch_fused(a->concurrency == 1, w8, fp, std::min(cus, w.fused_grid), s));
+      } else {
+        // bf16: the mixed GEMM's parameters (the light list in gu / dn) and,
+        // where the dispatch chooses, the light-only ones
+        fp.gu = gu_light;
+        fp.dn = dn_light;
+        fp.gu_heavy = gu_heavy;
+        fp.dn_heavy = dn_heavy;
+        fp.gu_lo = gu_light;
+        fp.dn_lo = dn_light;
+        fp.dn_lo.n_groups = (H / 32 + down_panels_per_task(mr_lo) - 1) / down_panels_per_task(mr_lo);
+        fp.auto_launch = auto_launch ? 1 : 0;
+        AFD_HIP(launch_fused_bf16(auto_launch ? mr_lo : mr, mr, fp, std::min(cus, w.fused_grid), s));
+      }
       for (int b = 3; b <= AFD_NUM_STAGES; ++b)
         if ((st = mark(b))) return st;
       if (tmask) a->ev_pending.push_back(ev);
@@ -953,8 +967,8 @@ afd_status afd_ffn_set_fused(afd_ffn_t* a, int32_t enable) {
   g_last_error.clear();
   if (!a) return fail(AFD_ERR_INVALID_ARG, "handle is NULL");
   if (enable != 0 && enable != 1) return fail(AFD_ERR_INVALID_ARG, "enable must be 0 or 1, not %d", enable);
-  if (enable && a->dtype != kFP8 && a->dtype != kW8A8)
-    return fail(AFD_ERR_UNSUPPORTED, "the fused launch serves block-FP8 and W8A8 layers");
+  if (enable && a->dtype == kF32)
+    return fail(AFD_ERR_UNSUPPORTED, "the fused launch serves bf16, block-FP8 and W8A8 layers");
   a->fused = enable;
   return AFD_OK;
 }

@@ -25,7 +25,7 @@
 // stable position with no order-dependent atomics.
 #include <algorithm>
 
-#include "afd_internal.h"
+#include "afd_device.h"
 
 namespace afd {
 
@@ -57,23 +57,6 @@ __device__ inline int block_exclusive_scan_1024(int v, int* lds_waves, int* tota
   int r = base + x - v;
   __syncthreads();  // lds_waves may be reused by the caller
   return r;
-}
-
-// Workgroups of the mixed bf16 GEMM launch (cus of them) that take the light
-// list: in proportion to the light list's share of the cost, a multiple of 8
-// where cus is (the same number on every XCD), at least one for a nonempty
-// list of either kind when cus allows two.
-__device__ inline int mixed_light_workgroups(int cus, int nl, int nh) {
-  if (cus <= 0 || nl == 0) return 0;
-  if (nh == 0) return cus;
-  if (cus < 2) return 0;  // one workgroup runs both lists, heavy first
-  const float share = (float)nl / ((float)nl + kHeavyTileCost * (float)nh);
-  int l = (int)(share * (float)cus + 0.5f);
-  if (cus % kXcds == 0 && cus >= 2 * kXcds) {
-    l = (l + kXcds / 2) / kXcds * kXcds;
-    return min(max(l, kXcds), cus - kXcds);
-  }
-  return min(max(l, 1), cus - 1);
 }
 
 }  // namespace
@@ -241,7 +224,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
       const int nl = n_light + (sh_heavy ? 0 : n_shared), nh = n_heavy + (sh_heavy ? n_shared : 0);
       p.num_mtiles[0] = nl;
       p.num_mtiles[1] = nh;
-      p.num_mtiles[2] = mixed_light_workgroups(p.mix_cus, nl, nh);
+      p.num_mtiles[2] = dev::mixed_light_workgroups(p.mix_cus, nl, nh);
       p.num_mtiles[3] = mixed ? kLaunchMixed : kLaunchLight;
     }
   }

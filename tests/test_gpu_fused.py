@@ -48,6 +48,15 @@ CASES = {
     "w8a8_shared_multi_tile": (cfg("w8a8", 150, 512, 384, 6, 3, shared=384), 47),
     "w8a8_zipf": (cfg("w8a8", 700, 512, 256, 8, 4, routing="zipf"), 48),
     "fp8_shared_2p5x": (cfg("fp8", 150, 512, 256, 6, 3, shared=640), 53),
+    # bf16: the dispatch keeps every expert light (light-only streaming, 32-
+    # and 64-row tiles), chooses the mixed split for a skewed batch, or always
+    # takes it (shared expert, many rows per expert)
+    "bf16_light_only_mr1": (cfg("bf16", 64, 512, 256, 32, 4), 54),
+    "bf16_light_only_mr2": (cfg("bf16", 200, 256, 384, 32, 4), 55),
+    "bf16_auto_zipf": (cfg("bf16", 256, 256, 256, 32, 4, routing="zipf"), 56),
+    "bf16_heavy_ragged": (cfg("bf16", 600, 256, 256, 4, 2), 57),
+    "bf16_shared_mixed": (cfg("bf16", 150, 512, 384, 6, 3, shared=384), 58),
+    "bf16_shared_2x_heavy": (cfg("bf16", 600, 256, 256, 4, 2, shared=512), 59),
 }
 
 
@@ -70,9 +79,10 @@ def test_fused_equals_separate_launches(name):
     layer.close()
 
 
-def test_fused_on_shares_of_the_cus():
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+def test_fused_on_shares_of_the_cus(dtype):
     """Grids of a third of the CUs (not a multiple of the 8 XCDs) and of two."""
-    c = cfg("fp8", 260, 512, 256, 16, 4, shared=256)
+    c = cfg(dtype, 260, 512, 256, 16, 4, shared=256)
     p = problem(c, 49)
     layer = afd.Layer(p)
     base, _ = run(layer, p, False)
@@ -86,17 +96,16 @@ def test_fused_on_shares_of_the_cus():
     layer.close()
 
 
-def test_fused_refused_for_bf16_and_f32():
-    for dt in ("bf16", "f32"):
-        p = problem(cfg(dt, 8, 256, 256, 4, 2), 50)
-        layer = afd.Layer(p)
-        with pytest.raises(afd.AfdError) as e:
-            layer.set_fused(True)
-        assert e.value.status == afd.AFD_ERR_UNSUPPORTED
-        layer.close()
+def test_fused_refused_for_f32():
+    p = problem(cfg("f32", 8, 256, 256, 4, 2), 50)
+    layer = afd.Layer(p)
+    with pytest.raises(afd.AfdError) as e:
+        layer.set_fused(True)
+    assert e.value.status == afd.AFD_ERR_UNSUPPORTED
+    layer.close()
 
 
-@pytest.mark.parametrize("name", ["fp8_shared", "w8a8_shared"])
+@pytest.mark.parametrize("name", ["fp8_shared", "w8a8_shared", "decode", "aggregated"])
 def test_fused_full_size(name):
     c = inputs.workload(name)
     say("fused full size", name)
@@ -106,18 +115,27 @@ def test_fused_full_size(name):
     check_dispatch(layer, p)
     # bit-equal to the separate launches, which the parity tests compare over
     # every m-tile; here a tile-covering sample of 40 tiles per list
-    tokens, cov = tile_covering_tokens(c["dtype"], c["T"], c["E"], c["K"], p["ids"].cpu().numpy(), True,
-                                       max_tiles=40)
+    tokens, cov = tile_covering_tokens(c["dtype"], c["T"], c["E"], c["K"], p["ids"].cpu().numpy(),
+                                       bool(c.get("shared_inter")), max_tiles=40)
     say("  compared tiles", cov, len(tokens), "tokens")
     compare(got, oracle_out(to_host_problem(p), tokens), c["dtype"], tokens=tokens, what=name + " fused")
     layer.close()
 
 
-def test_fused_two_stream_ping_pong():
-    """The verify shard's two microbatches, each one fused launch on half the
-    CUs, running at once on two streams: equal to the single separate-launch
-    call over all tokens."""
-    c = inputs.workload("verify_shard")
+PING_PONG = {
+    "verify_shard": inputs.workload("verify_shard"),
+    # bf16 with Zipf routing: each microbatch has heavy and light experts
+    "bf16_zipf_mixed": cfg("bf16", 2048, 1024, 512, 32, 8, routing="zipf"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PING_PONG))
+def test_fused_two_stream_ping_pong(name):
+    """Two microbatches, each one fused launch on half the CUs, running at once
+    on two streams: equal to the single separate-launch call over all
+    tokens."""
+    c = PING_PONG[name]
+    say("fused ping-pong", name)
     p = problem(c, 0)
     T = c["T"]
     half = T // 2
@@ -140,15 +158,16 @@ def test_fused_two_stream_ping_pong():
     check_dispatch(l0, mbs[0])
     check_dispatch(l1, mbs[1])
     tokens = np.sort(np.random.default_rng(8).choice(T, 16, replace=False))
-    compare(single, oracle_out(to_host_problem(p), tokens), "fp8", tokens=tokens, what="verify shard fused")
+    compare(single, oracle_out(to_host_problem(p), tokens), c["dtype"], tokens=tokens, what=name + " fused")
     l1.close()
     l0.close()
 
 
-def test_fused_graph_replay():
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+def test_fused_graph_replay(dtype):
     """The fused forward captured in a HIP graph replays bit-exactly, with
     eager fused forwards of another batch on the same handle in between."""
-    c = cfg("fp8", 150, 512, 384, 6, 3, shared=384)
+    c = cfg(dtype, 150, 512, 384, 6, 3, shared=384)
     p = problem(c, 51)
     other = problem(c, 52)
     layer = afd.Layer(p)
@@ -174,6 +193,6 @@ def test_fused_graph_replay():
         layer.forward(other["hidden"], other["hidden_scales"], other["ids"], other["weights"], out=scratch)
         torch.cuda.synchronize()
     assert afd.afd_ffn_fused_errors(layer.handle) == 0
-    compare(eager, oracle_out(to_host_problem(p)), "fp8", what="graph fused")
+    compare(eager, oracle_out(to_host_problem(p)), dtype, what="graph fused")
     del graph
     layer.close()

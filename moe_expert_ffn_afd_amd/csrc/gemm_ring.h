@@ -361,7 +361,9 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
     if constexpr (GATEUP) {
       // h of unit u = 4q + (wn NPW + pp) / 2 (pp even: gate, pp + 1: up), per
       // token amax over the task's 128 h columns: this wave's, then over WN
+      // (a wave of a WN = 1 grid holds all of them: no exchange, no barriers)
       float h[RT][NPW / 2][2][4];
+      float am[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         float a = 0.0f;
@@ -377,17 +379,23 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
             }
         a = fmaxf(a, __shfl_xor(a, 16, 64));
         a = fmaxf(a, __shfl_xor(a, 32, 64));
-        if (kg == 0) red[(wm * WN + wn) * 32 + rt * 16 + tok] = a;
+        am[rt] = a;
+        if (WN > 1 && kg == 0) red[(wm * WN + wn) * 32 + rt * 16 + tok] = a;
       }
-      lds_reads_done();
-      raw_barrier();
+      if constexpr (WN > 1) {
+        lds_reads_done();
+        raw_barrier();
+      }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int mi = rt * 16 + tok;
         const int m = wm * WR + mi;
-        float amax = 0.0f;
+        float amax = am[rt];
+        if constexpr (WN > 1) {
+          amax = 0.0f;
 #pragma unroll
-        for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, red[(wm * WN + w2) * 32 + mi]);
+          for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, red[(wm * WN + w2) * 32 + mi]);
+        }
         const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
         const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
         if (m < rows) {
@@ -412,8 +420,10 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
           if (wn == 0 && kg == 0) p.c_scales[(int64_t)q * p.c_scale_ld + row0 + m] = scale;
         }
       }
-      lds_reads_done();
-      raw_barrier();  // red[] is rewritten by the next task
+      if constexpr (WN > 1) {
+        lds_reads_done();
+        raw_barrier();  // red[] is rewritten by the next task
+      }
     } else {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -483,6 +493,7 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
     };
     if constexpr (GATEUP) {
       float h[RT][NPW / 2][2][4];
+      float am[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const float sx = Sx[wm * WR + rt * 16 + tok];
@@ -501,25 +512,33 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
             }
         a = fmaxf(a, __shfl_xor(a, 16, 64));
         a = fmaxf(a, __shfl_xor(a, 32, 64));
-        if (kg == 0) red[(wm * WN + wn) * 32 + rt * 16 + tok] = a;
+        am[rt] = a;
+        if (WN > 1 && kg == 0) red[(wm * WN + wn) * 32 + rt * 16 + tok] = a;
       }
-      lds_reads_done();
-      raw_barrier();
+      if constexpr (WN > 1) {
+        lds_reads_done();
+        raw_barrier();
+      }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int mi = rt * 16 + tok;
         const int m = wm * WR + mi;
-        float amax = 0.0f;
+        float amax = am[rt];
+        if constexpr (WN > 1) {
+          amax = 0.0f;
 #pragma unroll
-        for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, red[(wm * WN + w2) * 32 + mi]);
+          for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, red[(wm * WN + w2) * 32 + mi]);
+        }
         if (m >= rows) continue;
         uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes;
 #pragma unroll
         for (int u = 0; u < NPW / 2; ++u) store_pair(orow, 4 * q + (wn * NPW) / 2 + u, h[rt][u], false);
         if (wn == 0 && kg == 0) p.c_scales[(int64_t)q * p.c_scale_ld + row0 + m] = amax;
       }
-      lds_reads_done();
-      raw_barrier();  // red[] is rewritten by the next task
+      if constexpr (WN > 1) {
+        lds_reads_done();
+        raw_barrier();  // red[] is rewritten by the next task
+      }
     } else {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {

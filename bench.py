@@ -43,6 +43,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GATE_UP_STAGE = 2  # stage index of the grouped GEMM gate/up + SwiGLU in the library's timing
 STAGE_STEPS = 20   # steps with every stage timed, after the timed steps, for the per-stage breakdown
 KERNEL_SOURCES = ("gemm.hip", "gemm_stream.h", "gemm_tiled.hip", "gemm_tiled.h", "gemm_ring.hip", "gemm_ring.h",
+                  "gemm_tiled8.h",
                   "quant.hip", "quant.h", "fused.h", "fused.hip", "fused_bf16.hip", "combine.h", "afd_device.h",
                   "afd_internal.h")
 

@@ -127,6 +127,7 @@ struct Workspace {
   int32_t *chunk_base = nullptr, *sorted_assign = nullptr, *row_of = nullptr;
   int4* mtiles = nullptr;
   int4* mtiles_heavy = nullptr;
+  int4* mtiles_tiled = nullptr;  // block-FP8: experts with many rows (gemm_tiled8.h)
   int32_t* pool = nullptr;    // [2] the ring GEMMs' tail-pool counters
   uint8_t* h = nullptr;       // bf16 | e4m3 | fp32 (W8A8: bf16, before re-quantisation)
   float* h_scales = nullptr;  // FP8: [I/128][h_rows] step-major; W8A8: [h_rows]
@@ -237,8 +238,9 @@ int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w
   int64_t off = 0;
   auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + bytes, 256); return o; };
   const int64_t o_counts = take(4ll * a->E), o_offsets = take(4ll * (a->E + 1)), o_err = take(4),
-                o_nmt = take(16), o_cb = take(4ll * max_chunks * a->E), o_sa = take(4 * nmax),
+                o_nmt = take(32), o_cb = take(4ll * max_chunks * a->E), o_sa = take(4 * nmax),
                 o_ro = take(4 * nmax), o_mt = take(16ll * max_mtiles), o_mth = take(16ll * max_mtiles),
+                o_mtt = take(a->dtype == kFP8 ? 16ll * max_mtiles : 0),
                 o_pool = take(16),
                 o_h = take(rows * a->I * (w8 ? 2 : es)),
                 o_hs = take(a->dtype == kFP8 ? rows * (a->I / 128) * 4 : w8 ? rows * 4 : 0),
@@ -259,6 +261,7 @@ int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w
     w->row_of = (int32_t*)(base + o_ro);
     w->mtiles = (int4*)(base + o_mt);
     w->mtiles_heavy = (int4*)(base + o_mth);
+    w->mtiles_tiled = a->dtype == kFP8 ? (int4*)(base + o_mtt) : nullptr;
     w->pool = (int32_t*)(base + o_pool);
     w->h = base + o_h;
     const bool sc = a->dtype == kFP8 || w8;
@@ -545,6 +548,13 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
   d.shared_row0 = (int32_t)nmax;
   d.mtiles = w.mtiles;
   d.mtiles_heavy = w.mtiles_heavy;
+  // Block-FP8 batches of at least 256 routed rows per expert on average: the
+  // experts with at least 256 rows take the LDS-tiled FP8 body (256-row tiles,
+  // gemm_tiled8.h) instead of the ring's 128-row ones
+  const bool tiled8 = dt == kFP8 && n_flat >= (int64_t)kTiled8Rows * E;
+  d.mtiles_tiled = w.mtiles_tiled;
+  d.bm_tiled = kTiled8Rows;
+  d.tiled_min_rows = tiled8 ? kTiled8Rows : 0x7fffffff;
   d.num_mtiles = w.num_mtiles;
   d.pool = fp8 ? w.pool : nullptr;
 
@@ -581,6 +591,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
 
   // upper bounds of the routed + shared m-tiles of this call, per list
   const int64_t mt_bound = n_flat / bm + std::min<int64_t>(E, n_flat) + (int64_t)a->S * ((T + bm - 1) / bm) + 1;
+  const int64_t mtt_bound = tiled8 ? n_flat / kTiled8Rows + (int64_t)a->S * ((T + kTiled8Rows - 1) / kTiled8Rows) + 1 : 0;
   const int64_t mth_bound =
       light_only ? 0 : n_flat / heavy_min + (int64_t)a->S * ((T + bm_heavy - 1) / bm_heavy) + 1;
   const int64_t rows_ld_h = (int64_t)I * (w8 ? 2 : esize_of(dt));  // W8A8: bf16 h before re-quantisation
@@ -672,6 +683,8 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
     g.c_scales = w8 ? w.pamax : w.h_scales;  // W8A8: each row's amax per task, for quant.hip
     g.c_scale_ld = (int32_t)w.h_rows;
     g.pool = fp8 ? w.pool : nullptr;  // the ring GEMMs' tail pool
+    g.mtiles3 = tiled8 ? w.mtiles_tiled : nullptr;  // block-FP8: the tiled list, run first
+    g.num_mtiles3 = w.num_mtiles + 4;
     GemmParams gu_light = g;
     GemmParams gu_heavy = g;
     gu_heavy.mtiles = w.mtiles_heavy;
@@ -722,6 +735,10 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
         GemmParams both = light;
         both.mtiles2 = heavy.mtiles;
         both.num_mtiles2 = heavy.num_mtiles;
+        if (tiled8) {
+          const hipError_t e = launch_gemm_tiled8(gate_up, both, mtt_bound * light.n_groups, cus, s);
+          if (e != hipSuccess) return e;
+        }
         return launch_gemm_ring(gate_up, a->concurrency == 1, w8, both, (mt_bound + mth_bound) * light.n_groups,
                                 cus, s);
       }

@@ -185,7 +185,8 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
 
   // m-tile lists: experts with at least heavy_min_rows rows go to the heavy
   // list (tiles of bm_heavy rows), the others to the light list (bm_light);
-  // routed experts in expert order, then the shared expert.  With
+  // block-FP8 experts with at least tiled_min_rows rows to the tiled list
+  // (bm_tiled); routed experts in expert order, then the shared expert.  With
   // auto_heavy_rows, a batch whose largest expert stays below it keeps every
   // expert light, in tiles of bm_light_only rows (one launch of the streaming
   // GEMM); a larger one takes the mixed launch.
@@ -194,13 +195,21 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
     const int heavy_min = mixed ? p.heavy_min_rows : 0x7fffffff;
     const int bm_light = mixed ? p.bm_light : p.bm_light_only;
     const int n = tid < E ? total[tid] : 0;
-    const bool heavy = n >= heavy_min;
-    const int vl = heavy ? 0 : (n + bm_light - 1) / bm_light;
+    const bool has_tiled = p.tiled_min_rows < 0x7fffffff;  // uniform
+    const bool tiled = has_tiled && n >= p.tiled_min_rows;
+    const bool heavy = !tiled && n >= heavy_min;
+    const int vl = (heavy || tiled) ? 0 : (n + bm_light - 1) / bm_light;
     const int vh = heavy ? (n + p.bm_heavy - 1) / p.bm_heavy : 0;
-    int n_light = 0, n_heavy = 0;
+    const int vt = tiled ? (n + p.bm_tiled - 1) / p.bm_tiled : 0;
+    int n_light = 0, n_heavy = 0, n_tiled = 0;
     const int offl = block_exclusive_scan_1024(vl, scan_tmp, &n_light);
     const int offh = block_exclusive_scan_1024(vh, scan_tmp, &n_heavy);
+    const int offt = has_tiled ? block_exclusive_scan_1024(vt, scan_tmp, &n_tiled) : 0;
     if (tid < E) {
+      for (int j = 0; j < vt; ++j) {
+        const int r0 = j * p.bm_tiled;
+        p.mtiles_tiled[offt + j] = make_int4(tid, excl[tid] + r0, min(p.bm_tiled, n - r0), 0);
+      }
       for (int j = 0; j < vl; ++j) {
         const int r0 = j * bm_light;
         p.mtiles[offl + j] = make_int4(tid, excl[tid] + r0, min(bm_light, n - r0), 0);
@@ -210,22 +219,24 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_scan_kernel(D
         p.mtiles_heavy[offh + j] = make_int4(tid, excl[tid] + r0, min(p.bm_heavy, n - r0), 0);
       }
     }
-    const bool sh_heavy = p.shared_rows >= heavy_min;
-    const int bms = sh_heavy ? p.bm_heavy : bm_light;
+    const bool sh_tiled = has_tiled && p.shared_rows >= p.tiled_min_rows;
+    const bool sh_heavy = !sh_tiled && p.shared_rows >= heavy_min;
+    const int bms = sh_tiled ? p.bm_tiled : sh_heavy ? p.bm_heavy : bm_light;
     const int per_part = (p.shared_rows + bms - 1) / bms;
     const int n_shared = per_part * p.shared_parts;
-    int4* list = sh_heavy ? p.mtiles_heavy : p.mtiles;
-    const int base = sh_heavy ? n_heavy : n_light;
+    int4* list = sh_tiled ? p.mtiles_tiled : sh_heavy ? p.mtiles_heavy : p.mtiles;
+    const int base = sh_tiled ? n_tiled : sh_heavy ? n_heavy : n_light;
     for (int j = tid; j < n_shared; j += kDispatchThreads) {
       const int v = j / per_part, r0 = (j - v * per_part) * bms;
       list[base + j] = make_int4(E + v, p.shared_row0 + v * p.shared_rows + r0, min(bms, p.shared_rows - r0), 0);
     }
     if (tid == 0) {
-      const int nl = n_light + (sh_heavy ? 0 : n_shared), nh = n_heavy + (sh_heavy ? n_shared : 0);
+      const int nl = n_light + (sh_heavy || sh_tiled ? 0 : n_shared), nh = n_heavy + (sh_heavy ? n_shared : 0);
       p.num_mtiles[0] = nl;
       p.num_mtiles[1] = nh;
       p.num_mtiles[2] = dev::mixed_light_workgroups(p.mix_cus, nl, nh);
       p.num_mtiles[3] = mixed ? kLaunchMixed : kLaunchLight;
+      p.num_mtiles[4] = n_tiled + (sh_tiled ? n_shared : 0);
     }
   }
 

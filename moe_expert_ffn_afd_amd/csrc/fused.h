@@ -169,8 +169,9 @@ __device__ __forceinline__ void fused_dispatch(const FusedParams& f, const int b
       }
       // m-tile lists, as the dispatch kernel builds them: experts with at
       // least heavy_min rows in heavy tiles of bm_heavy rows, the others in
-      // light tiles of bm_light; routed experts in expert order, then the
-      // shared expert.  With auto_heavy_rows (bf16), a batch whose largest
+      // light tiles of bm_light, block-FP8 experts of at least tiled_min_rows
+      // rows in tiled tiles of bm_tiled; routed experts in expert order, then
+      // the shared expert.  With auto_heavy_rows (bf16), a batch whose largest
       // expert stays below it keeps every expert light, in tiles of
       // bm_light_only rows.
       int* mx = tmp + 16;
@@ -181,37 +182,46 @@ __device__ __forceinline__ void fused_dispatch(const FusedParams& f, const int b
       const bool mixed = d.auto_heavy_rows <= 0 || *mx >= d.auto_heavy_rows;
       const int heavy_min = mixed ? d.heavy_min_rows : 0x7fffffff;
       const int bm_light = mixed ? d.bm_light : d.bm_light_only;
-      const bool heavy = cnt_e >= heavy_min;
-      const int vl = heavy ? 0 : (cnt_e + bm_light - 1) / bm_light;
+      const bool has_tiled = d.tiled_min_rows < 0x7fffffff;  // uniform
+      const bool tiled = has_tiled && cnt_e >= d.tiled_min_rows;
+      const bool heavy = !tiled && cnt_e >= heavy_min;
+      const int vl = (heavy || tiled) ? 0 : (cnt_e + bm_light - 1) / bm_light;
       const int vh = heavy ? (cnt_e + d.bm_heavy - 1) / d.bm_heavy : 0;
-      int n_light = 0, n_heavy = 0;
+      const int vt = tiled ? (cnt_e + d.bm_tiled - 1) / d.bm_tiled : 0;
+      int n_light = 0, n_heavy = 0, n_tiled = 0;
       const int offl = scan512(vl, tmp, &n_light);
       const int offh = scan512(vh, tmp, &n_heavy);
+      const int offt = has_tiled ? scan512(vt, tmp, &n_tiled) : 0;
       if (tid < E) {
+        for (int j = 0; j < vt; ++j)
+          d.mtiles_tiled[offt + j] =
+              make_int4(tid, off_e + j * d.bm_tiled, min(d.bm_tiled, cnt_e - j * d.bm_tiled), 0);
         for (int j = 0; j < vl; ++j)
           d.mtiles[offl + j] = make_int4(tid, off_e + j * bm_light, min(bm_light, cnt_e - j * bm_light), 0);
         for (int j = 0; j < vh; ++j)
           d.mtiles_heavy[offh + j] =
               make_int4(tid, off_e + j * d.bm_heavy, min(d.bm_heavy, cnt_e - j * d.bm_heavy), 0);
       }
-      const bool sh_heavy = d.shared_rows >= heavy_min;
-      const int bms = sh_heavy ? d.bm_heavy : bm_light;
+      const bool sh_tiled = has_tiled && d.shared_rows >= d.tiled_min_rows;
+      const bool sh_heavy = !sh_tiled && d.shared_rows >= heavy_min;
+      const int bms = sh_tiled ? d.bm_tiled : sh_heavy ? d.bm_heavy : bm_light;
       const int per_part = (d.shared_rows + bms - 1) / bms;
       const int n_shared = per_part * d.shared_parts;
-      int4* list = sh_heavy ? d.mtiles_heavy : d.mtiles;
-      const int base = sh_heavy ? n_heavy : n_light;
+      int4* list = sh_tiled ? d.mtiles_tiled : sh_heavy ? d.mtiles_heavy : d.mtiles;
+      const int base = sh_tiled ? n_tiled : sh_heavy ? n_heavy : n_light;
       for (int j = tid; j < n_shared; j += kFusedThreads) {
         const int v = j / per_part, r0 = (j - v * per_part) * bms;
         list[base + j] = make_int4(E + v, d.shared_row0 + v * d.shared_rows + r0, min(bms, d.shared_rows - r0), 0);
       }
       if (tid == 0) {
-        const int nl = n_light + (sh_heavy ? 0 : n_shared), nh = n_heavy + (sh_heavy ? n_shared : 0);
+        const int nl = n_light + (sh_heavy || sh_tiled ? 0 : n_shared), nh = n_heavy + (sh_heavy ? n_shared : 0);
         d.num_mtiles[0] = nl;
         d.num_mtiles[1] = nh;
         // bf16: the grid's workgroups that stream the light list beside the
         // heavy tiles (the ring GEMMs take no split)
         d.num_mtiles[2] = dev::mixed_light_workgroups(d.mix_cus > 0 ? G : 0, nl, nh);
         d.num_mtiles[3] = mixed ? kLaunchMixed : kLaunchLight;
+        d.num_mtiles[4] = n_tiled + (sh_tiled ? n_shared : 0);
       }
     }
     for (int i = tid; i < kFusedWaves * E; i += kFusedThreads) wcnt[i] = 0;

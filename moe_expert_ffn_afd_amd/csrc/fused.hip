@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(FusedParams f) 
   grid_sync(f.bar, target, G, f.spin_limit);
 
   // ---- G1: gate/up + SwiGLU
-  ring_stage<true, WNT, I8>(f.gu, b, G);
+  ring_stage<true, WNT, I8, true>(f.gu, b, G);
   grid_sync(f.bar, target, G, f.spin_limit);
 
   // ---- Q (W8A8): h to int8, one wave per row
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void fused_kernel(FusedParams f) 
   }
 
   // ---- G2: down
-  ring_stage<false, WNT, I8>(f.dn, b, G);
+  ring_stage<false, WNT, I8, true>(f.dn, b, G);
   grid_sync(f.bar, target, G, f.spin_limit);
 
   fused_combine(f, b, G);

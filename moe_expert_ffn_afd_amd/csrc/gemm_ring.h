@@ -62,6 +62,7 @@
 #include <type_traits>
 
 #include "afd_device.h"
+#include "gemm_tiled8.h"
 
 namespace afd {
 
@@ -108,6 +109,7 @@ constexpr int kRingLdsBytes = kRingMetaOff + kRingWaves * 2 * kRingMetaBytes;
 constexpr int kRingMB = AFD_RING_MB;  // m-tiles per rasterisation block
 constexpr int kRingMinRounds = 1;  // unrolled rounds per task
 static_assert(kRingLdsBytes <= 160 * 1024 - 4096, "ring exceeds LDS");
+static_assert(kT8LdsBytes <= kRingLdsBytes, "the tiled FP8 body runs in the ring kernels' LDS");
 
 __device__ inline int clamp31(int64_t v) { return v > 0x7fffffff ? 0x7fffffff : (int)v; }
 
@@ -645,11 +647,14 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
   raw_barrier();    // every wave is done with the ring before another list refills it
 }
 
-// One GEMM stage (both tile lists) as workgroup b of G: the heavy list's
-// tasks (m-tiles of up to 128 rows), then the light list's (up to 64 rows),
-// so a GEMM stage has one tail instead of two.  A workgroup runs tasks rank,
-// rank + G, ... of the two lists in a row; ranks are renumbered so that each
-// XCD owns a contiguous run of tasks (shared rows stay in its L2).
+// One GEMM stage as workgroup b of G: with TILED, block-FP8 layers' tiled list
+// first (m-tiles of up to 256 rows, gemm_tiled8.h; the fused layer kernel),
+// then the heavy list's tasks (up to 128 rows), then the light list's (up to
+// 64 rows), so a GEMM stage has one tail instead of several.  (The separate
+// ring launch leaves the tiled list to a launch of its own before it, which
+// keeps the ring kernel's registers at what the ring alone needs.)  A workgroup runs tasks rank,
+// rank + G, ... of the lists in a row; ranks are renumbered so that each XCD
+// owns a contiguous run of tasks (shared rows stay in its L2).
 //
 // The light list's last tasks (up to one per workgroup) form a pool instead:
 // a workgroup done with its own tasks claims them one at a time from a
@@ -657,16 +662,21 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
 // own.  The static shares end within a task of each other, but CUs do not run
 // equally fast (measured: the last workgroup of a gate/up launch ends about
 // 5 % after the first), so the fast ones take the tail.
-template <bool GATEUP, bool WNT, bool I8>
+template <bool GATEUP, bool WNT, bool I8, bool TILED>
 __device__ __forceinline__ void ring_stage(const GemmParams& p, const int b, const int G) {
   const int nq = p.n_groups;
+  const int nt = (TILED && !I8 && p.num_mtiles3) ? uniform(p.num_mtiles3[0]) : 0;
   const int nh = uniform(p.num_mtiles2 ? p.num_mtiles2[0] : 0);
   const int nl = uniform(p.num_mtiles[0]);
-  const int th = nh * nq, tl = nl * nq;
+  const int tt = nt * nq, th = nh * nq, tl = nl * nq;
   const int rank = (AFD_RING_XCD_REMAP && G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
-  if (nh > 0) ring_list<GATEUP, 128, WNT, I8>(p, p.mtiles2, nh, rank, G, th);
+  // this workgroup's first task at or past index `base` of the lists in a row
+  auto next_from = [&](const int base) { return rank >= base ? rank : rank + (base - rank + G - 1) / G * G; };
+  if constexpr (TILED && !I8)
+    if (nt > 0) tiled8_list<GATEUP>(p, p.mtiles3, nt, rank, G);
+  if (nh > 0) ring_list<GATEUP, 128, WNT, I8>(p, p.mtiles2, nh, next_from(tt) - tt, G, th);
   // this workgroup's first task past the heavy list, as an index into the light list
-  const int first_l = rank >= th ? rank - th : rank + (th - rank + G - 1) / G * G - th;
+  const int first_l = next_from(tt + th) - (tt + th);
   const int pool = (AFD_RING_POOL && p.pool) ? min(tl, G) : 0;
   int first = first_l, stride = G, limit = tl - pool;
   for (;;) {

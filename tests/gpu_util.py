@@ -84,9 +84,13 @@ def tile_lists(dtype: str, T: int, E: int, K: int, counts, shared: bool):
     tile.  bf16
     batches with no shared expert and at most 32 rows per expert on average keep
     every expert light (tiles of 32, or of 64 past 16 rows per expert on
-    average) unless the largest expert exceeds two such tiles.
-    Returns {"light": [...], "heavy": [...]}, each tile (expert, first row in
-    the expert, rows); the shared expert is expert E, its rows are tokens."""
+    average) unless the largest expert exceeds two such tiles.  Block-FP8
+    batches of at least 256 routed rows per expert on average put the experts
+    of at least 256 rows (the shared expert too) in a third, tiled list of
+    256-row tiles.
+    Returns {"light": [...], "heavy": [...], "tiled": [...]}, each tile
+    (expert, first row in the expert, rows); the shared expert is expert E, its
+    rows are tokens."""
     counts = np.asarray(counts)
     n_flat = T * K
     if dtype == "f32":
@@ -100,13 +104,14 @@ def tile_lists(dtype: str, T: int, E: int, K: int, counts, shared: bool):
             mr_lo = 1 if n_flat <= 16 * E else 2
             if counts.max(initial=0) < 2 * 32 * mr_lo + 1:
                 bm, heavy_min = 32 * mr_lo, 1 << 30
-    lists = {"light": [], "heavy": []}
+    tiled_min = 256 if dtype == "fp8" and n_flat >= 256 * E else 1 << 30
+    lists = {"light": [], "heavy": [], "tiled": []}
     sizes = list(enumerate(counts.tolist())) + ([(E, T)] if shared else [])
     for e, n in sizes:
-        heavy = n >= heavy_min
-        b = bm_heavy if heavy else bm
+        kind = "tiled" if n >= tiled_min else "heavy" if n >= heavy_min else "light"
+        b = {"tiled": 256, "heavy": bm_heavy, "light": bm}[kind]
         for r0 in range(0, n, b):
-            lists["heavy" if heavy else "light"].append((e, r0, min(b, n - r0)))
+            lists[kind].append((e, r0, min(b, n - r0)))
     return lists
 
 

@@ -48,6 +48,9 @@ CASES = {
     "w8a8_shared_multi_tile": (cfg("w8a8", 150, 512, 384, 6, 3, shared=384), 47),
     "w8a8_zipf": (cfg("w8a8", 700, 512, 256, 8, 4, routing="zipf"), 48),
     "fp8_shared_2p5x": (cfg("fp8", 150, 512, 256, 6, 3, shared=640), 53),
+    # block-FP8 with the LDS-tiled list (experts of 256 rows or more) beside
+    # the ring's heavy and light lists
+    "fp8_tiled_three_lists": (cfg("fp8", 1100, 256, 256, 16, 4, routing="zipf", shared=256), 60),
     # bf16: the dispatch keeps every expert light (light-only streaming, 32-
     # and 64-row tiles), chooses the mixed split for a skewed batch, or always
     # takes it (shared expert, many rows per expert)

@@ -56,6 +56,13 @@ SMALL_CASES = {
     "fp8_shared_1p5x_heavy": (small("fp8", 300, 256, 256, 6, 2, shared=384), 20),
     "w8a8_shared_3x": (small("w8a8", 50, 256, 128, 6, 2, shared=384), 21),
     "f32_shared_1p5x": (small("f32", 45, 256, 256, 5, 3, shared=384), 22),
+    # block-FP8 batches of at least 256 routed rows per expert on average: the
+    # experts of 256 rows or more (and the shared expert) take the LDS-tiled
+    # FP8 GEMM's 256-row tiles, ragged last tiles included; with Zipf routing
+    # all three lists (tiled, 128-row heavy, 64-row light) in one stage
+    "fp8_tiled_ragged": (small("fp8", 700, 256, 384, 4, 2), 23),
+    "fp8_tiled_shared_parts": (small("fp8", 600, 512, 256, 4, 2, shared=384), 24),
+    "fp8_tiled_three_lists": (small("fp8", 1100, 256, 256, 16, 4, routing="zipf"), 25),
 }
 
 

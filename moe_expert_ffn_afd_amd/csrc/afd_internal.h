@@ -96,7 +96,7 @@ struct DispatchParams {
                            // shared_row0 + v T + t for part v and token t
   int4* mtiles;            // light tile list
   int4* mtiles_heavy;      // heavy tile list
-  int4* mtiles_tiled;      // block-FP8: tiled list (experts of at least tiled_min_rows rows)
+  int4* mtiles_tiled;      // 8-bit layers: tiled list (experts of at least tiled_min_rows rows)
   int32_t bm_tiled;        // rows per m-tile of the tiled list
   int32_t tiled_min_rows;  // experts with at least this many rows take the tiled list (a huge
                            // value: no tiled list)
@@ -117,8 +117,8 @@ struct DispatchParams {
 // mixed GEMM over both lists.  The host launches both kernels with gates; the
 // one not chosen returns at once.
 constexpr int32_t kLaunchLight = 1;
-// rows of the block-FP8 LDS-tiled GEMM's m-tiles, and the fewest routed rows
-// per expert on average (and the fewest of an expert) that use it
+// rows of the 8-bit LDS-tiled GEMM's m-tiles, and the fewest routed rows per
+// expert on average (and the fewest of an expert) that use it
 constexpr int kTiled8Rows = 256;
 constexpr int32_t kLaunchMixed = 2;
 
@@ -140,7 +140,7 @@ struct GemmParams {
   const int32_t* num_mtiles;     // [0] tiles of mtiles; [3] the launch the dispatch chose
   const int4* mtiles2;           // block-FP8 ring GEMM: the heavy list, run before `mtiles`
   const int32_t* num_mtiles2;
-  const int4* mtiles3;           // block-FP8 ring GEMM: the tiled list (gemm_tiled8.h), run first;
+  const int4* mtiles3;           // 8-bit layers: the tiled list (gemm_tiled8.h), run first;
   const int32_t* num_mtiles3;    // nullptr: none
   const int32_t* sorted_assign;  // row -> flat slot (gate/up gather)
   int32_t top_k;
@@ -283,9 +283,10 @@ int tiled_panels();         // weight panels of one LDS-tiled task
 hipError_t launch_gemm_ring(bool gate_up, bool stream_weights, bool int8, const GemmParams& p, int64_t max_tasks,
                             int num_cus, hipStream_t s);
 int ring_rows(bool heavy);
-// Block-FP8 experts of many rows (gemm_tiled8.h): the tiled list (mtiles3) of
-// a stage, launched before that stage's ring kernel (which then skips it)
-hipError_t launch_gemm_tiled8(bool gate_up, const GemmParams& p, int64_t max_tasks, int num_cus, hipStream_t s);
+// 8-bit experts of many rows (gemm_tiled8.h): the tiled list (mtiles3) of a
+// stage, launched before that stage's ring kernel (which then skips it)
+hipError_t launch_gemm_tiled8(bool gate_up, bool int8, const GemmParams& p, int64_t max_tasks, int num_cus,
+                              hipStream_t s);
 hipError_t launch_gemm_f32(bool gate_up, const F32Params& p, int grid, hipStream_t s);
 hipError_t launch_quant_rows(const QuantParams& p, hipStream_t s);
 // calib.hip: the MFMA rate sustained with no memory traffic (kind 0 bf16,

@@ -127,7 +127,7 @@ struct Workspace {
   int32_t *chunk_base = nullptr, *sorted_assign = nullptr, *row_of = nullptr;
   int4* mtiles = nullptr;
   int4* mtiles_heavy = nullptr;
-  int4* mtiles_tiled = nullptr;  // block-FP8: experts with many rows (gemm_tiled8.h)
+  int4* mtiles_tiled = nullptr;  // 8-bit layers: experts with many rows (gemm_tiled8.h)
   int32_t* pool = nullptr;    // [2] the ring GEMMs' tail-pool counters
   uint8_t* h = nullptr;       // bf16 | e4m3 | fp32 (W8A8: bf16, before re-quantisation)
   float* h_scales = nullptr;  // FP8: [I/128][h_rows] step-major; W8A8: [h_rows]
@@ -240,7 +240,7 @@ int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w
   const int64_t o_counts = take(4ll * a->E), o_offsets = take(4ll * (a->E + 1)), o_err = take(4),
                 o_nmt = take(32), o_cb = take(4ll * max_chunks * a->E), o_sa = take(4 * nmax),
                 o_ro = take(4 * nmax), o_mt = take(16ll * max_mtiles), o_mth = take(16ll * max_mtiles),
-                o_mtt = take(a->dtype == kFP8 ? 16ll * max_mtiles : 0),
+                o_mtt = take(a->dtype == kFP8 || w8 ? 16ll * max_mtiles : 0),
                 o_pool = take(16),
                 o_h = take(rows * a->I * (w8 ? 2 : es)),
                 o_hs = take(a->dtype == kFP8 ? rows * (a->I / 128) * 4 : w8 ? rows * 4 : 0),
@@ -261,7 +261,7 @@ int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w
     w->row_of = (int32_t*)(base + o_ro);
     w->mtiles = (int4*)(base + o_mt);
     w->mtiles_heavy = (int4*)(base + o_mth);
-    w->mtiles_tiled = a->dtype == kFP8 ? (int4*)(base + o_mtt) : nullptr;
+    w->mtiles_tiled = a->dtype == kFP8 || w8 ? (int4*)(base + o_mtt) : nullptr;
     w->pool = (int32_t*)(base + o_pool);
     w->h = base + o_h;
     const bool sc = a->dtype == kFP8 || w8;
@@ -548,10 +548,10 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
   d.shared_row0 = (int32_t)nmax;
   d.mtiles = w.mtiles;
   d.mtiles_heavy = w.mtiles_heavy;
-  // Block-FP8 batches of at least 256 routed rows per expert on average: the
-  // experts with at least 256 rows take the LDS-tiled FP8 body (256-row tiles,
-  // gemm_tiled8.h) instead of the ring's 128-row ones
-  const bool tiled8 = dt == kFP8 && n_flat >= (int64_t)kTiled8Rows * E;
+  // 8-bit batches of at least 256 routed rows per expert on average: the
+  // experts with at least 256 rows take the LDS-tiled 8-bit body (256-row
+  // tiles, gemm_tiled8.h) instead of the ring's 128-row ones
+  const bool tiled8 = fp8 && n_flat >= (int64_t)kTiled8Rows * E;
   d.mtiles_tiled = w.mtiles_tiled;
   d.bm_tiled = kTiled8Rows;
   d.tiled_min_rows = tiled8 ? kTiled8Rows : 0x7fffffff;
@@ -736,7 +736,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
         both.mtiles2 = heavy.mtiles;
         both.num_mtiles2 = heavy.num_mtiles;
         if (tiled8) {
-          const hipError_t e = launch_gemm_tiled8(gate_up, both, mtt_bound * light.n_groups, cus, s);
+          const hipError_t e = launch_gemm_tiled8(gate_up, w8, both, mtt_bound * light.n_groups, cus, s);
           if (e != hipSuccess) return e;
         }
         return launch_gemm_ring(gate_up, a->concurrency == 1, w8, both, (mt_bound + mth_bound) * light.n_groups,

@@ -647,7 +647,7 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
   raw_barrier();    // every wave is done with the ring before another list refills it
 }
 
-// One GEMM stage as workgroup b of G: with TILED, block-FP8 layers' tiled list
+// One GEMM stage as workgroup b of G: with TILED, the 8-bit layers' tiled list
 // first (m-tiles of up to 256 rows, gemm_tiled8.h; the fused layer kernel),
 // then the heavy list's tasks (up to 128 rows), then the light list's (up to
 // 64 rows), so a GEMM stage has one tail instead of several.  (The separate
@@ -665,15 +665,15 @@ __device__ __forceinline__ void ring_list(const GemmParams& p, const int4* tiles
 template <bool GATEUP, bool WNT, bool I8, bool TILED>
 __device__ __forceinline__ void ring_stage(const GemmParams& p, const int b, const int G) {
   const int nq = p.n_groups;
-  const int nt = (TILED && !I8 && p.num_mtiles3) ? uniform(p.num_mtiles3[0]) : 0;
+  const int nt = (TILED && p.num_mtiles3) ? uniform(p.num_mtiles3[0]) : 0;
   const int nh = uniform(p.num_mtiles2 ? p.num_mtiles2[0] : 0);
   const int nl = uniform(p.num_mtiles[0]);
   const int tt = nt * nq, th = nh * nq, tl = nl * nq;
   const int rank = (AFD_RING_XCD_REMAP && G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
   // this workgroup's first task at or past index `base` of the lists in a row
   auto next_from = [&](const int base) { return rank >= base ? rank : rank + (base - rank + G - 1) / G * G; };
-  if constexpr (TILED && !I8)
-    if (nt > 0) tiled8_list<GATEUP>(p, p.mtiles3, nt, rank, G);
+  if constexpr (TILED)
+    if (nt > 0) tiled8_list<GATEUP, I8>(p, p.mtiles3, nt, rank, G);
   if (nh > 0) ring_list<GATEUP, 128, WNT, I8>(p, p.mtiles2, nh, next_from(tt) - tt, G, th);
   // this workgroup's first task past the heavy list, as an index into the light list
   const int first_l = next_from(tt + th) - (tt + th);

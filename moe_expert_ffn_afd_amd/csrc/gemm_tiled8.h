@@ -34,7 +34,17 @@
 // re-quantises it to e4m3 per token and 128 columns (amax / 448, the two
 // waves of a row group exchanging their amax through LDS) and writes the
 // scales step-major; down writes the bf16 expert outputs.
+//
+// W8A8 layers (I8) run the same tiles on int8 codes, as the ring does: each
+// lane's 32 bytes of a step feed two int8 MFMAs 16x16x64 (its first and its
+// second 16 bytes in both operands), summed exactly in int32 straight in the
+// accumulators; the per-token and per-channel scales are constant along k, so
+// the task's scales are copied once, at its start, into slot 0's scale area
+// (no step writes it in this mode) and applied in the epilogue, which writes
+// h in bf16 with each row's amax over the task's 128 columns (gate/up) or the
+// bf16 outputs (down).
 #include <algorithm>
+#include <type_traits>
 
 #include "afd_device.h"
 
@@ -63,7 +73,7 @@ __device__ inline int t8_clamp31(int64_t v) { return v > 0x7fffffff ? 0x7fffffff
 // `tiles` (m-tiles of up to 256 rows).  Every wave of the workgroup calls it
 // with the same arguments; it ends with every copy landed and every wave past
 // its last LDS read (the caller may reuse the LDS).
-template <bool GATEUP>
+template <bool GATEUP, bool I8>
 __device__ __forceinline__ void tiled8_list(const GemmParams& p, const int4* tiles, const int n_tiles,
                                             const int first, const int stride) {
   extern __shared__ __attribute__((aligned(16))) uint8_t t8lds[];
@@ -136,13 +146,22 @@ __device__ __forceinline__ void tiled8_list(const GemmParams& p, const int4* til
       }
       avoff[k] = off;
     }
-    // wave 0, lane i: the scales of rows 4i .. 4i+3 of the tile in a step;
-    // waves 1 and 2, lane 0: one block scale of the step
+    // wave 0, lane i: the scales of rows 4i .. 4i+3 of the tile (block-FP8:
+    // in a step); block-FP8 waves 1 and 2, lane 0: one block scale of the
+    // step; W8A8 gate/up waves 1 and 2, lane i < 32: the gate / up scales of
+    // columns 128q + 4i ..; W8A8 down wave 1, lane i: of columns 256q + 4i ..
     int svoff = soob;
     if (scopy == 0)
       svoff = (row0 + 4 * lane) * 4;
-    else if (scopy > 0 && lane == 0)
+    else if (!I8 && scopy > 0 && lane == 0)
       svoff = (expert * wsb + (GATEUP ? q : 2 * q + (scopy - 1))) * 4;
+    else if (I8 && GATEUP && scopy > 0 && lane < 32)
+      svoff = (expert * p.b_scale_cols + 128 * q + 4 * lane) * 4;
+    else if (I8 && !GATEUP && scopy == 1)
+      svoff = (expert * p.b_scale_cols + 256 * q + 4 * lane) * 4;
+    // W8A8: the task's scales, once (landed by the first step's wait)
+    if constexpr (I8)
+      if (scopy >= 0) dma16(rs, t8lds + kT8ScaleOff + scopy * 1024, svoff, 0);
 
     // step c into slot `slot`; `in` false copies zeros (steps past the end)
     auto issue = [&](const int c, const int slot, const bool in) {
@@ -156,16 +175,53 @@ __device__ __forceinline__ void tiled8_list(const GemmParams& p, const int4* til
 #pragma unroll
       for (int k = 0; k < A_DMA; ++k)
         dma16(ra, st + A_OFF + (wave * A_DMA + k) * 1024, avoff[k], in ? c * kStepBytes : oobA);
-      dma16(rs, scopy >= 0 ? st + kT8ScaleOff + scopy * 1024 : t8lds + kT8SinkOff, svoff, in ? c * sstep : soob);
+      if constexpr (!I8)
+        dma16(rs, scopy >= 0 ? st + kT8ScaleOff + scopy * 1024 : t8lds + kT8SinkOff, svoff, in ? c * sstep : soob);
     };
 
-    f32x4 acc[RT][2 * NPW];
+    // fp32 accumulators (block-FP8, scaled per step) or int32 (W8A8, exact)
+    typedef typename std::conditional<I8, i32x4, f32x4>::type acc_t;
+    acc_t acc[RT][2 * NPW];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int b = 0; b < 2 * NPW; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[rt][b][r] = 0.0f;
+        for (int r = 0; r < 4; ++r) acc[rt][b][r] = 0;
+
+    // W8A8: per step, the token fragments as two 16-byte halves (the first
+    // and the second 16 bytes of the lane's 32), then per half panel two
+    // int8 MFMAs into the accumulator
+    auto compute_i8 = [&](const uint8_t* st) {
+      i32x4 xl[RT], xh[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int r = wm * WR + rt * 16 + tok;
+        const uint8_t* rp = st + A_OFF + r * kStepBytes;
+        const int sw = t8_swz(r);
+        xl[rt] = *reinterpret_cast<const i32x4*>(rp + ((2 * kg) ^ sw) * 16);
+        xh[rt] = *reinterpret_cast<const i32x4*>(rp + ((2 * kg + 1) ^ sw) * 16);
+      }
+      const int g = kg >> 1, j0 = (kg & 1) * 2;
+#pragma unroll
+      for (int pp = 0; pp < NPW; ++pp) {
+        const int P = wn * NPW + pp;
+        i32x4 wl[2], wh[2];
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          const uint8_t* lo = st + P * kStepPanelBytes + j0 * 1024 + (16 * sh + tok + 32 * g) * 16;
+          wl[sh] = *reinterpret_cast<const i32x4*>(lo);
+          wh[sh] = *reinterpret_cast<const i32x4*>(lo + 1024);
+        }
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            acc[rt][pp * 2 + sh] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wl[sh], xl[rt], acc[rt][pp * 2 + sh], 0, 0, 0);
+            acc[rt][pp * 2 + sh] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wh[sh], xh[rt], acc[rt][pp * 2 + sh], 0, 0, 0);
+          }
+      }
+    };
 
     auto compute = [&](const uint8_t* st) {
       const float* S = reinterpret_cast<const float*>(st + kT8ScaleOff);
@@ -240,7 +296,10 @@ __device__ __forceinline__ void tiled8_list(const GemmParams& p, const int4* til
       raw_barrier();
       issue(c + 1, (c + 1) & 1, c + 1 < ks);
       __builtin_amdgcn_sched_barrier(0);
-      compute(t8lds + (c & 1) * kT8Slot);
+      if constexpr (I8)
+        compute_i8(t8lds + (c & 1) * kT8Slot);
+      else
+        compute(t8lds + (c & 1) * kT8Slot);
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_vmcnt<0>();  // the empty copy past the end
@@ -248,87 +307,177 @@ __device__ __forceinline__ void tiled8_list(const GemmParams& p, const int4* til
     raw_barrier();    // every wave is done with the slots before the next task refills them
 
     // ------------------------------------------------------------- epilogue
-    if constexpr (GATEUP) {
-      // h of unit u = 4q + (wn NPW + pp) / 2 (pp even: gate, pp + 1: up), per
-      // token amax over the task's 128 h columns: this wave's, then over WN
-      float h[RT][NPW / 2][2][4];
+    if constexpr (I8) {
+      // W8A8: the task's scales from slot 0's scale area: row m at Sx[m];
+      // gate/up: the gate and up scales of h column c at Sc0[c], Sc1[c];
+      // down: output column c of the task at Sc0[c]
+      const float* Sx = reinterpret_cast<const float*>(t8lds + kT8ScaleOff);
+      const float* Sc0 = Sx + 256;
+      const float* Sc1 = Sx + 512;
+      const bool odd = (kg & 1) != 0;
+      // lane pairs (kg, kg ^ 1) of a token swap one half each, so every lane
+      // stores 8 consecutive bf16 columns (16 bytes) from column 32 * unit
+      auto store_pair = [&](uint8_t* orow, const int unit, const float (&v)[2][4], const bool nt) {
+        uint2 o0, o1;
+        o0.x = pack_bf16x2(v[0][0], v[0][1]);
+        o0.y = pack_bf16x2(v[0][2], v[0][3]);
+        o1.x = pack_bf16x2(v[1][0], v[1][1]);
+        o1.y = pack_bf16x2(v[1][2], v[1][3]);
+        const uint2 snd = odd ? o0 : o1;
+        uint2 rcv;
+        rcv.x = __shfl_xor(snd.x, 16, 64);
+        rcv.y = __shfl_xor(snd.y, 16, 64);
+        const uint4 w = odd ? make_uint4(rcv.x, rcv.y, o1.x, o1.y) : make_uint4(o0.x, o0.y, rcv.x, rcv.y);
+        uint8_t* dst = orow + (int64_t)(odd ? 32 * unit + 16 + 4 * (kg - 1) : 32 * unit + 4 * kg) * 2;
+        if (nt)
+          store16<true>(dst, w);
+        else
+          store16(dst, w);
+      };
+      if constexpr (GATEUP) {
+        float h[RT][NPW / 2][2][4];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        float a = 0.0f;
+        for (int rt = 0; rt < RT; ++rt) {
+          const float sx = Sx[wm * WR + rt * 16 + tok];
+          float a = 0.0f;
 #pragma unroll
-        for (int u = 0; u < NPW / 2; ++u)
+          for (int u = 0; u < NPW / 2; ++u)
 #pragma unroll
-          for (int sh = 0; sh < 2; ++sh)
+            for (int sh = 0; sh < 2; ++sh)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-              const float v = silu_mul(acc[rt][4 * u + sh][r4], acc[rt][4 * u + 2 + sh][r4]);
-              h[rt][u][sh][r4] = v;
-              a = fmaxf(a, fabsf(v));
-            }
-        a = fmaxf(a, __shfl_xor(a, 16, 64));
-        a = fmaxf(a, __shfl_xor(a, 32, 64));
-        if (kg == 0) red[wave * 64 + rt * 16 + tok] = a;
-      }
-      lds_reads_done();
-      raw_barrier();
+              for (int r4 = 0; r4 < 4; ++r4) {
+                const int c = 32 * ((wn * NPW) / 2 + u) + 16 * sh + 4 * kg + r4;
+                const float v = silu_mul((float)acc[rt][4 * u + sh][r4] * sx * Sc0[c],
+                                         (float)acc[rt][4 * u + 2 + sh][r4] * sx * Sc1[c]);
+                h[rt][u][sh][r4] = v;
+                a = fmaxf(a, fabsf(v));
+              }
+          a = fmaxf(a, __shfl_xor(a, 16, 64));
+          a = fmaxf(a, __shfl_xor(a, 32, 64));
+          if (kg == 0) red[wave * 64 + rt * 16 + tok] = a;
+        }
+        lds_reads_done();
+        raw_barrier();
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int mi = rt * 16 + tok;
-        const int m = wm * WR + mi;
-        float amax = 0.0f;
+        for (int rt = 0; rt < RT; ++rt) {
+          const int mi = rt * 16 + tok;
+          const int m = wm * WR + mi;
+          float amax = 0.0f;
 #pragma unroll
-        for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, red[(wm * WN + w2) * 64 + mi]);
-        const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
-        const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
-        if (m < rows) {
+          for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, red[(wm * WN + w2) * 64 + mi]);
+          if (m >= rows) continue;
           uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes;
 #pragma unroll
-          for (int u = 0; u < NPW / 2; ++u) {
-            const int unit = 4 * q + (wn * NPW) / 2 + u;
-            uint32_t o[2];
+          for (int u = 0; u < NPW / 2; ++u) store_pair(orow, 4 * q + (wn * NPW) / 2 + u, h[rt][u], false);
+          if (wn == 0 && kg == 0) p.c_scales[(int64_t)q * p.c_scale_ld + row0 + m] = amax;
+        }
+      } else {
 #pragma unroll
-            for (int sh = 0; sh < 2; ++sh) {
-              float v[4];
+        for (int rt = 0; rt < RT; ++rt) {
+          const int m = wm * WR + rt * 16 + tok;
+          if (m >= rows) continue;
+          uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes;
+          const float sx = Sx[m];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = fminf(fmaxf(h[rt][u][sh][e] * inv, -448.0f), 448.0f);
-              o[sh] = pack_fp8x4(v[0], v[1], v[2], v[3]);
-            }
-            // lanes kg and kg ^ 1 swap one half each: 8 consecutive codes per lane
-            const bool odd = (kg & 1) != 0;
-            const uint32_t rcv = __shfl_xor(odd ? o[0] : o[1], 16, 64);
-            const uint2 w = odd ? make_uint2(rcv, o[1]) : make_uint2(o[0], rcv);
-            *reinterpret_cast<uint2*>(orow + 32 * unit + (odd ? 16 + 4 * (kg - 1) : 4 * kg)) = w;
+          for (int pp = 0; pp < NPW; ++pp) {
+            const int P = q * kT8Panels + wn * NPW + pp;
+            if (P >= p.n_panels) continue;
+            float v[2][4];
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+              for (int r4 = 0; r4 < 4; ++r4)
+                v[sh][r4] = (float)acc[rt][pp * 2 + sh][r4] * sx * Sc0[32 * (wn * NPW + pp) + 16 * sh + 4 * kg + r4];
+            store_pair(orow, P, v, true);
           }
-          if (wn == 0 && kg == 0) p.c_scales[(int64_t)q * p.c_scale_ld + row0 + m] = scale;
         }
       }
+      // the next task's scale copy rewrites the area (and red[])
       lds_reads_done();
-      raw_barrier();  // red[] is rewritten by the next task
+      raw_barrier();
     } else {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int m = wm * WR + rt * 16 + tok;
-        if (m >= rows) continue;
-        uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes;
-#pragma unroll
-        for (int pp = 0; pp < NPW; ++pp) {
-          const int P = q * kT8Panels + wn * NPW + pp;
-          if (P >= p.n_panels) continue;
-          // lane pairs (kg, kg ^ 1) of a token swap one half panel each, so
-          // every lane stores 8 consecutive columns (16 bytes)
-          uint2 o0, o1;
-          o0.x = pack_bf16x2(acc[rt][pp * 2][0], acc[rt][pp * 2][1]);
-          o0.y = pack_bf16x2(acc[rt][pp * 2][2], acc[rt][pp * 2][3]);
-          o1.x = pack_bf16x2(acc[rt][pp * 2 + 1][0], acc[rt][pp * 2 + 1][1]);
-          o1.y = pack_bf16x2(acc[rt][pp * 2 + 1][2], acc[rt][pp * 2 + 1][3]);
-          const bool odd = (kg & 1) != 0;
-          const uint2 snd = odd ? o0 : o1;
-          uint2 rcv;
-          rcv.x = __shfl_xor(snd.x, 16, 64);
-          rcv.y = __shfl_xor(snd.y, 16, 64);
-          const uint4 v = odd ? make_uint4(rcv.x, rcv.y, o1.x, o1.y) : make_uint4(o0.x, o0.y, rcv.x, rcv.y);
-          const int col = odd ? 32 * P + 16 + 4 * (kg - 1) : 32 * P + 4 * kg;
-          store16<true>(orow + (int64_t)col * 2, v);
+      if constexpr (GATEUP) {
+        // h of unit u = 4q + (wn NPW + pp) / 2 (pp even: gate, pp + 1: up), per
+        // token amax over the task's 128 h columns: this wave's, then over WN
+        float h[RT][NPW / 2][2][4];
+  #pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          float a = 0.0f;
+  #pragma unroll
+          for (int u = 0; u < NPW / 2; ++u)
+  #pragma unroll
+            for (int sh = 0; sh < 2; ++sh)
+  #pragma unroll
+              for (int r4 = 0; r4 < 4; ++r4) {
+                const float v = silu_mul(acc[rt][4 * u + sh][r4], acc[rt][4 * u + 2 + sh][r4]);
+                h[rt][u][sh][r4] = v;
+                a = fmaxf(a, fabsf(v));
+              }
+          a = fmaxf(a, __shfl_xor(a, 16, 64));
+          a = fmaxf(a, __shfl_xor(a, 32, 64));
+          if (kg == 0) red[wave * 64 + rt * 16 + tok] = a;
+        }
+        lds_reads_done();
+        raw_barrier();
+  #pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int mi = rt * 16 + tok;
+          const int m = wm * WR + mi;
+          float amax = 0.0f;
+  #pragma unroll
+          for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, red[(wm * WN + w2) * 64 + mi]);
+          const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+          const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
+          if (m < rows) {
+            uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes;
+  #pragma unroll
+            for (int u = 0; u < NPW / 2; ++u) {
+              const int unit = 4 * q + (wn * NPW) / 2 + u;
+              uint32_t o[2];
+  #pragma unroll
+              for (int sh = 0; sh < 2; ++sh) {
+                float v[4];
+  #pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = fminf(fmaxf(h[rt][u][sh][e] * inv, -448.0f), 448.0f);
+                o[sh] = pack_fp8x4(v[0], v[1], v[2], v[3]);
+              }
+              // lanes kg and kg ^ 1 swap one half each: 8 consecutive codes per lane
+              const bool odd = (kg & 1) != 0;
+              const uint32_t rcv = __shfl_xor(odd ? o[0] : o[1], 16, 64);
+              const uint2 w = odd ? make_uint2(rcv, o[1]) : make_uint2(o[0], rcv);
+              *reinterpret_cast<uint2*>(orow + 32 * unit + (odd ? 16 + 4 * (kg - 1) : 4 * kg)) = w;
+            }
+            if (wn == 0 && kg == 0) p.c_scales[(int64_t)q * p.c_scale_ld + row0 + m] = scale;
+          }
+        }
+        lds_reads_done();
+        raw_barrier();  // red[] is rewritten by the next task
+      } else {
+  #pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int m = wm * WR + rt * 16 + tok;
+          if (m >= rows) continue;
+          uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes;
+  #pragma unroll
+          for (int pp = 0; pp < NPW; ++pp) {
+            const int P = q * kT8Panels + wn * NPW + pp;
+            if (P >= p.n_panels) continue;
+            // lane pairs (kg, kg ^ 1) of a token swap one half panel each, so
+            // every lane stores 8 consecutive columns (16 bytes)
+            uint2 o0, o1;
+            o0.x = pack_bf16x2(acc[rt][pp * 2][0], acc[rt][pp * 2][1]);
+            o0.y = pack_bf16x2(acc[rt][pp * 2][2], acc[rt][pp * 2][3]);
+            o1.x = pack_bf16x2(acc[rt][pp * 2 + 1][0], acc[rt][pp * 2 + 1][1]);
+            o1.y = pack_bf16x2(acc[rt][pp * 2 + 1][2], acc[rt][pp * 2 + 1][3]);
+            const bool odd = (kg & 1) != 0;
+            const uint2 snd = odd ? o0 : o1;
+            uint2 rcv;
+            rcv.x = __shfl_xor(snd.x, 16, 64);
+            rcv.y = __shfl_xor(snd.y, 16, 64);
+            const uint4 v = odd ? make_uint4(rcv.x, rcv.y, o1.x, o1.y) : make_uint4(o0.x, o0.y, rcv.x, rcv.y);
+            const int col = odd ? 32 * P + 16 + 4 * (kg - 1) : 32 * P + 4 * kg;
+            store16<true>(orow + (int64_t)col * 2, v);
+          }
         }
       }
     }

@@ -51,6 +51,7 @@ CASES = {
     # block-FP8 with the LDS-tiled list (experts of 256 rows or more) beside
     # the ring's heavy and light lists
     "fp8_tiled_three_lists": (cfg("fp8", 1100, 256, 256, 16, 4, routing="zipf", shared=256), 60),
+    "w8a8_tiled_three_lists": (cfg("w8a8", 1100, 256, 256, 16, 4, routing="zipf", shared=256), 61),
     # bf16: the dispatch keeps every expert light (light-only streaming, 32-
     # and 64-row tiles), chooses the mixed split for a skewed batch, or always
     # takes it (shared expert, many rows per expert)

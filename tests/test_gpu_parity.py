@@ -63,6 +63,8 @@ SMALL_CASES = {
     "fp8_tiled_ragged": (small("fp8", 700, 256, 384, 4, 2), 23),
     "fp8_tiled_shared_parts": (small("fp8", 600, 512, 256, 4, 2, shared=384), 24),
     "fp8_tiled_three_lists": (small("fp8", 1100, 256, 256, 16, 4, routing="zipf"), 25),
+    "w8a8_tiled_ragged": (small("w8a8", 700, 256, 384, 4, 2), 26),
+    "w8a8_tiled_three_lists": (small("w8a8", 1100, 256, 256, 16, 4, routing="zipf"), 27),
 }
 
 
@@ -115,10 +117,12 @@ LARGEST = {
     "bf16_uniform_T16384": inputs.workload("decode", T=16384),
     "bf16_zipf_T16384": inputs.workload("aggregated", T=16384),
     "fp8_shared_T16384": inputs.workload("fp8_shared", T=16384),
+    "w8a8_shared_T16384": inputs.workload("w8a8_shared", T=16384),
 }
 # tiles per list whose first and last rows are compared (None: all); the
-# block-FP8 oracle takes about 7 core-seconds per token of that shape
-LARGEST_TILES = {"bf16_uniform_T16384": None, "bf16_zipf_T16384": None, "fp8_shared_T16384": 40}
+# 8-bit oracle takes about 7 core-seconds per token of that shape
+LARGEST_TILES = {"bf16_uniform_T16384": None, "bf16_zipf_T16384": None, "fp8_shared_T16384": 40,
+                 "w8a8_shared_T16384": 16}
 
 
 @pytest.mark.parametrize("name", sorted(LARGEST))

@@ -16,7 +16,9 @@ steps with every stage timed.
 Other modes: --copy-calibration runs a plain device copy of known size (the
 reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters);
 --mfma-ceiling measures the MFMA rate sustained with no memory traffic and
-the shader clock meanwhile (the ceiling of the MFMA fractions);
+the shader clock meanwhile (the ceiling of the MFMA fractions), and the bf16
+rate of the LDS-tiled GEMM's inner loop with and without its LDS fragment
+reads;
 --no-cpu-baseline skips the oracle timing; --graph also times the step
 captured in a HIP graph and replayed; --sweep times the layer at the
 workload's shape over a range of batch sizes T (the FFN-side time T_e as a
@@ -231,7 +233,12 @@ def main():
         for dt, spec in (("bf16", PEAK_TFLOPS["bf16"]), ("fp8", PEAK_TFLOPS["fp8"]), ("w8a8", PEAK_TFLOPS["w8a8"])):
             tf, ghz = afd.afd_ffn_mfma_peak(dt)
             res[dt] = {"tflops": round(tf, 1), "clock_ghz": round(ghz, 3), "frac_of_spec": round(tf / spec, 4)}
-        print(json.dumps({"mfma_ceiling": res, "note": "8 waves per CU, register operands, no memory traffic"}))
+        for name, reads in (("bf16_tile_loop_fragments_in_registers", 0), ("bf16_tile_loop_with_lds_reads", 6)):
+            tf, ghz = afd.afd_ffn_mfma_lds_peak(reads)
+            res[name] = {"tflops": round(tf, 1), "clock_ghz": round(ghz, 3),
+                         "frac_of_spec": round(tf / PEAK_TFLOPS["bf16"], 4)}
+        print(json.dumps({"mfma_ceiling": res, "note": "8 waves per CU, no memory traffic; bf16_tile_loop_*: the "
+                          "LDS-tiled GEMM's 8 MFMAs per 16-deep k slice, with its 6 LDS fragment reads or without"}))
         return
     if args.copy_calibration:
         n = 1 << 30

@@ -280,6 +280,20 @@ afd_status afd_ffn_routing_errors(afd_ffn_t *handle, int32_t *count, void *strea
  */
 afd_status afd_ffn_mfma_peak(int32_t dtype, int32_t device, int32_t iters, double *tflops, double *clock_ghz);
 
+/*
+ * Measurement helper (not part of a forward): the bf16 MFMA rate of the
+ * LDS-tiled GEMM's inner loop without its memory traffic.  8 waves per CU each
+ * issue, per step, the eight 32x32x16 bf16 MFMAs of a 64-row x 4-panel wave
+ * tile's 16-deep k slice; with lds_reads = 6 they first read that step's six
+ * 16-byte fragments from LDS (two activation, four weight fragments: the
+ * GEMM's ratio of LDS reads to MFMAs), with lds_reads = 0 the fragments stay
+ * in registers.  `iters` steps (rounded down to a multiple of 3, at least 3).
+ * *tflops: flops per second over the launch; *clock_ghz as for
+ * afd_ffn_mfma_peak.  AFD_ERR_INVALID_ARG for lds_reads other than 0 or 6.
+ * Allocates a few bytes, synchronises the device.
+ */
+afd_status afd_ffn_mfma_lds_peak(int32_t device, int32_t iters, int32_t lds_reads, double *tflops, double *clock_ghz);
+
 #define AFD_NUM_STAGES 5
 afd_status afd_ffn_set_timing(afd_ffn_t *handle, int32_t enable);
 afd_status afd_ffn_set_timing_stages(afd_ffn_t *handle, uint32_t stage_mask);

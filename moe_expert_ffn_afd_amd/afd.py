@@ -29,7 +29,8 @@ EXPORTS = ("afd_ffn_validate_config", "afd_ffn_create", "afd_ffn_clone", "afd_ff
            "afd_ffn_forward_noalloc",
            "afd_ffn_destroy", "afd_ffn_status_string", "afd_ffn_last_error", "afd_ffn_debug_dispatch",
            "afd_ffn_routing_errors", "afd_ffn_set_timing", "afd_ffn_set_timing_stages", "afd_ffn_get_timing",
-           "afd_ffn_set_concurrency", "afd_ffn_set_fused", "afd_ffn_fused_errors", "afd_ffn_mfma_peak")
+           "afd_ffn_set_concurrency", "afd_ffn_set_fused", "afd_ffn_fused_errors", "afd_ffn_mfma_peak",
+           "afd_ffn_mfma_lds_peak")
 
 
 class afd_ffn_config(ctypes.Structure):
@@ -75,6 +76,8 @@ def load(path: str = LIB_PATH):
     lib.afd_ffn_set_concurrency.argtypes = [vp, i32]
     lib.afd_ffn_set_fused.argtypes = [vp, i32]
     lib.afd_ffn_mfma_peak.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    lib.afd_ffn_mfma_lds_peak.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(ctypes.c_double)]
     lib.afd_ffn_fused_errors.argtypes = [vp, ctypes.POINTER(i32), vp]
     lib.afd_ffn_get_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
     for name in EXPORTS:
@@ -190,6 +193,14 @@ def afd_ffn_fused_errors(handle, stream=None) -> int:
     if st not in (AFD_OK, AFD_ERR_HIP):
         _check(st)
     return int(n.value)
+
+
+def afd_ffn_mfma_lds_peak(lds_reads: int, device: int = 0, iters: int = 90000):
+    """(TFLOP/s, shader GHz) of the LDS-tiled bf16 GEMM's MFMA loop with (6) or without (0)
+    its LDS fragment reads, no memory traffic."""
+    t, c = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    _check(load().afd_ffn_mfma_lds_peak(int(device), int(iters), int(lds_reads), ctypes.byref(t), ctypes.byref(c)))
+    return t.value, c.value
 
 
 def afd_ffn_mfma_peak(dtype: str, device: int = 0, iters: int = 200000):

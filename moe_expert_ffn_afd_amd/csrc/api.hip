@@ -980,6 +980,18 @@ afd_status afd_ffn_mfma_peak(int32_t dtype, int32_t device, int32_t iters, doubl
   return AFD_OK;
 }
 
+afd_status afd_ffn_mfma_lds_peak(int32_t device, int32_t iters, int32_t lds_reads, double* tflops, double* clock_ghz) {
+  g_last_error.clear();
+  if (!tflops || !clock_ghz || iters < 3) return fail(AFD_ERR_INVALID_ARG, "NULL output or iters < 3");
+  if (lds_reads != 0 && lds_reads != 6) return fail(AFD_ERR_INVALID_ARG, "lds_reads must be 0 or 6, not %d", lds_reads);
+  DeviceGuard dg(device);
+  if (!dg.ok) return fail(AFD_ERR_HIP, "cannot select device %d", device);
+  int cus = 0;
+  AFD_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device));
+  AFD_HIP(mfma_peak(lds_reads ? 4 : 3, cus, iters, tflops, clock_ghz));
+  return AFD_OK;
+}
+
 afd_status afd_ffn_set_fused(afd_ffn_t* a, int32_t enable) {
   g_last_error.clear();
   if (!a) return fail(AFD_ERR_INVALID_ARG, "handle is NULL");

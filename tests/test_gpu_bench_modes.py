@@ -71,3 +71,8 @@ def test_mfma_ceiling_line():
         say("  mfma ceiling", dt, d[dt])
         # a real, sustained rate: above a tenth of the spec peak, below the spec peak at 2.4 GHz
         assert 0.1 < d[dt]["frac_of_spec"] <= 1.02 and 0.5 < d[dt]["clock_ghz"] < 2.6
+    for k in ("bf16_tile_loop_fragments_in_registers", "bf16_tile_loop_with_lds_reads"):
+        say("  mfma ceiling", k, d[k])
+        assert 0.1 < d[k]["frac_of_spec"] <= 1.02 and 0.5 < d[k]["clock_ghz"] < 2.6
+    # the LDS reads cost MFMA time: never faster than the same loop without them
+    assert d["bf16_tile_loop_with_lds_reads"]["tflops"] <= 1.03 * d["bf16_tile_loop_fragments_in_registers"]["tflops"]

@@ -110,6 +110,13 @@ def test_null_arguments_rejected_on_host(lib):
     assert lib.afd_ffn_set_timing_stages(None, 4) == afd.AFD_ERR_INVALID_ARG
     assert lib.afd_ffn_set_concurrency(None, 2) == afd.AFD_ERR_INVALID_ARG
     assert lib.afd_ffn_destroy(None) == afd.AFD_OK
+    # measurement helpers: argument errors come back before any device call
+    t, c = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    assert lib.afd_ffn_mfma_peak(1, 0, 100, None, ctypes.byref(c)) == afd.AFD_ERR_INVALID_ARG
+    assert lib.afd_ffn_mfma_peak(0, 0, 100, ctypes.byref(t), ctypes.byref(c)) == afd.AFD_ERR_UNSUPPORTED  # fp32
+    assert lib.afd_ffn_mfma_lds_peak(0, 90, 5, ctypes.byref(t), ctypes.byref(c)) == afd.AFD_ERR_INVALID_ARG
+    assert lib.afd_ffn_mfma_lds_peak(0, 2, 6, ctypes.byref(t), ctypes.byref(c)) == afd.AFD_ERR_INVALID_ARG
+    assert lib.afd_ffn_mfma_lds_peak(0, 90, 0, None, ctypes.byref(c)) == afd.AFD_ERR_INVALID_ARG
 
 
 def test_status_strings(lib):

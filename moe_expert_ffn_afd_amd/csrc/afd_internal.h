@@ -109,7 +109,7 @@ struct DispatchParams {
                            //      rows; else every expert is light, in tiles of bm_light_only
                            //      rows; 0: heavy_min_rows alone
   int32_t bm_light_only;   // light tile rows when auto_heavy_rows keeps every expert light
-  int32_t* pool;           // [2] the ring GEMMs' tail-pool counters, zeroed here (or nullptr)
+  int32_t* pool;           // [2] the GEMMs' tail-pool counters, zeroed here (or nullptr)
 };
 
 // The launch the dispatch chose for a bf16 call whose routing the host cannot
@@ -166,8 +166,8 @@ struct GemmParams {
   int32_t n_panels;              // panels of one output matrix (I/32 or H/32)
   int32_t only_launch;           // 0: always run; kLaunchLight / kLaunchMixed: return at once
                                  // unless the dispatch chose that launch (num_mtiles[3])
-  int32_t* pool;                 // ring GEMM: [2] counters of the light list's tail pool (gate/up,
-                                 // down), zeroed by the dispatch; nullptr: no pool
+  int32_t* pool;                 // [2] tail-pool counters (gate/up, down), zeroed by the dispatch:
+                                 // the ring GEMM's light list, the bf16 heavy tiles; nullptr: no pool
   uint8_t* c;                    // output rows
   int64_t c_row_bytes;
   float* c_scales;               // fp8 gate/up: h scales, step-major [I/128][c_scale_ld]

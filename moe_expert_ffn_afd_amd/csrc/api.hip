@@ -556,7 +556,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
   d.bm_tiled = kTiled8Rows;
   d.tiled_min_rows = tiled8 ? kTiled8Rows : 0x7fffffff;
   d.num_mtiles = w.num_mtiles;
-  d.pool = fp8 ? w.pool : nullptr;
+  d.pool = dt != kF32 ? w.pool : nullptr;  // the tail pools of the ring and the bf16 tiled GEMMs
 
   // the whole layer in one persistent launch (afd_ffn_set_fused; not fp32)
   const bool use_fused = own_ws && a->fused && dt != kF32 && T > 0;
@@ -682,7 +682,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
     g.c_row_bytes = rows_ld_h;
     g.c_scales = w8 ? w.pamax : w.h_scales;  // W8A8: each row's amax per task, for quant.hip
     g.c_scale_ld = (int32_t)w.h_rows;
-    g.pool = fp8 ? w.pool : nullptr;  // the ring GEMMs' tail pool
+    g.pool = dt != kF32 ? w.pool : nullptr;  // the ring GEMMs' and the bf16 heavy tiles' tail pools
     g.mtiles3 = tiled8 ? w.mtiles_tiled : nullptr;  // block-FP8: the tiled list, run first
     g.num_mtiles3 = w.num_mtiles + 4;
     GemmParams gu_light = g;

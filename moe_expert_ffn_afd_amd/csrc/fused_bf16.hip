@@ -30,6 +30,7 @@ __device__ __forceinline__ void bf16_stage(const FusedParams& f, const GemmParam
   const int L = min(max(uniform(light.num_mtiles[2]), 0), G);
   if (b < L) {
     stream_body<GATEUP, MR, 2>(light, b, L);
+    tiled_pool<GATEUP>(heavy, G - L);
     return;
   }
   tiled_body<GATEUP>(heavy, b - L, G - L);

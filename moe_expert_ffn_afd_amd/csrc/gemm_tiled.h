@@ -69,6 +69,9 @@ namespace {
 #ifndef AFD_TILED_MB
 #define AFD_TILED_MB 4  // m-tiles per rasterisation block
 #endif
+#ifndef AFD_TILED_POOL
+#define AFD_TILED_POOL 1  // the heavy list's last tasks claimed by the workgroups done first
+#endif
 
 // NW waves form a WM x WN grid over BM rows x 8 panels; SUB ring slots per
 // super-step (a slot holds 128/SUB bytes of K per row).
@@ -97,9 +100,15 @@ __device__ inline int swz(int r) {
 
 }  // namespace
 
-// The heavy tasks as workgroup b of G.
+// The heavy tasks first, first + stride, ... below the pool, then pool tasks
+// claimed one at a time until none is left.  The pool is the list's last
+// min(tasks, Gh) tasks (Gh: the workgroups with a static share), claimed from
+// the counter p.pool[stage] (zeroed by the dispatch) by every workgroup done
+// with its own work, the light ones included: tasks take about 120 us
+// (gate/up) and a static share of 8.4 tasks leaves some workgroups a whole
+// task behind the others.  first past the static tasks: pool tasks only.
 template <bool GATEUP>
-__device__ __forceinline__ void tiled_body(const GemmParams& p, const int b, const int G) {
+__device__ __forceinline__ void tiled_tasks(const GemmParams& p, const int first, const int stride, const int Gh) {
   constexpr int NW = kNW, WM = kWM, WN = kWN, BM = kBM, NS = kNS, SUB = kSUB;
   constexpr int RB = kStepBytes / SUB;        // activation bytes per row and slot
   constexpr int PB = kStepPanelBytes / SUB;   // weight bytes per panel and slot
@@ -129,15 +138,23 @@ __device__ __forceinline__ void tiled_body(const GemmParams& p, const int b, con
   const int bpanel = (int)p.b_panel_bytes;
   const auto ra = make_rsrc(p.a, p.a_bytes);
 
-  // Task order: blocks of kMB m-tiles x all column groups, column group
-  // outer within a block, and workgroup ranks renumbered so each XCD owns a
-  // contiguous run of tasks.  The ~32 tiles an XCD runs at once then share a
-  // few activation chunks and weight panels through its L2.
-  const int rank = (AFD_TILED_XCD_REMAP && G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
   const int nq = p.n_groups;
   const int full = (num_mt / kMB) * kMB * nq;  // tasks in complete blocks
   const int rem = num_mt % kMB;
-  for (int task = rank; task < num_tasks; task += G) {
+  const int pool = (AFD_TILED_POOL && p.pool) ? min(num_tasks, Gh) : 0;
+  const int limit = num_tasks - pool;  // static tasks below, pool tasks from here
+  __shared__ int claim_slot;
+  auto claim = [&]() -> int {  // every thread calls it
+    if (pool == 0) return num_tasks;
+    if (tid == 0)
+      claim_slot = __hip_atomic_fetch_add(p.pool + (GATEUP ? 0 : 1), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int c = uniform(claim_slot);
+    __syncthreads();  // claim_slot is rewritten by the next claim
+    return c < pool ? limit + c : num_tasks;
+  };
+  int task = first < limit ? first : claim();
+  while (task < num_tasks) {
     int mt, q;
     if (task < full) {
       const int blk = task / (kMB * nq), w = task % (kMB * nq);
@@ -294,7 +311,28 @@ __device__ __forceinline__ void tiled_body(const GemmParams& p, const int b, con
         }
       }
     }
+    task = task + stride < limit ? task + stride : claim();
   }
+}
+
+// The heavy tasks as workgroup b of the G workgroups with a static share.
+// Task order: blocks of kMB m-tiles x all column groups, column group outer
+// within a block, and workgroup ranks renumbered so each XCD owns a
+// contiguous run of tasks.  The ~32 tiles an XCD runs at once then share a few
+// activation chunks and weight panels through its L2.
+template <bool GATEUP>
+__device__ __forceinline__ void tiled_body(const GemmParams& p, const int b, const int G) {
+  const int rank = (AFD_TILED_XCD_REMAP && G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
+  tiled_tasks<GATEUP>(p, rank, G, G);
+}
+
+// A workgroup done with other work (a light one of the mixed split) helps
+// with the heavy pool of the Gh heavy workgroups.  Its LDS use must be over.
+template <bool GATEUP>
+__device__ __forceinline__ void tiled_pool(const GemmParams& p, const int Gh) {
+  if (!AFD_TILED_POOL || !p.pool || Gh <= 0) return;
+  __syncthreads();
+  tiled_tasks<GATEUP>(p, 0x7fffffff, 1, Gh);
 }
 
 }  // namespace afd

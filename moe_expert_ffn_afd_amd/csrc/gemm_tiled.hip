@@ -23,6 +23,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void gemm_mixed_kernel(GemmParams heav
   const int L = min(max(uniform(light.num_mtiles[2]), 0), n);
   if ((int)blockIdx.x < L) {
     stream_body<GATEUP, MR, 2>(light, blockIdx.x, L);
+    tiled_pool<GATEUP>(heavy, n - L);  // then the heavy list's tail, with the heavy workgroups
     return;
   }
   tiled_body<GATEUP>(heavy, blockIdx.x - L, n - L);

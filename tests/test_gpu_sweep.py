@@ -3,7 +3,7 @@
 Each case draws H, I (multiples of 128), E, K, T, the routing kind and a shared
 expert from a fixed seed, so the sweep covers combinations the hand-written
 cases do not (odd panel counts, K close to E, experts on both sides of the
-light/heavy split, tails of every tile size) while staying reproducible.
+light/heavy split, tails of every tile size, shared experts of other widths) while staying reproducible.
 Same bar as the parity tests: bit-exact dispatch, max|err| <= tol * max|ref|.
 """
 import os
@@ -27,6 +27,8 @@ def draw_case(dtype: str, i: int) -> dict:
     T = int(rng.integers(1, 400))
     routing = str(rng.choice(["uniform", "zipf"]))
     shared = I if rng.random() < 0.3 else 0
+    if shared and rng.random() < 0.5:  # a shared expert of another width
+        shared = 128 * int(rng.integers(1, 6))
     return dict(dtype=dtype, T=T, H=H, I=I, E=E, K=K, routing=routing, shared_inter=shared)
 
 

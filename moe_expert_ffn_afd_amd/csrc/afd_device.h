@@ -71,6 +71,48 @@ __device__ inline void store_pair16(uint8_t* dst, uint2 lo, uint2 hi_v, bool upp
   store16<NT>(dst, upper ? make_uint4(rcv.x, rcv.y, hi_v.x, hi_v.y) : make_uint4(lo.x, lo.y, rcv.x, rcv.y));
 }
 
+// 16x16 MFMA outputs of the down GEMMs (ring and tiled 8-bit): lane l =
+// tok + 16 kg holds 4 columns of each 16-column half of a 32-column panel for
+// token tok (o0: columns 4 kg + 0..3, o1: 16 + 4 kg + 0..3).  Lane pairs
+// (kg, kg ^ 1) swap one half each, so every lane holds 8 consecutive bf16
+// columns (16 bytes); lanes kg = 0, 2, 1, 3 hold the panel's parts 0 .. 3.
+// Both lanes of a pair must be active.
+__device__ inline uint4 pair16_cols(uint2 o0, uint2 o1, int kg) {
+  const bool odd = (kg & 1) != 0;
+  const uint2 snd = odd ? o0 : o1;
+  uint2 rcv;
+  rcv.x = __shfl_xor(snd.x, 16, 64);
+  rcv.y = __shfl_xor(snd.y, 16, 64);
+  return odd ? make_uint4(rcv.x, rcv.y, o1.x, o1.y) : make_uint4(o0.x, o0.y, rcv.x, rcv.y);
+}
+
+// Stores one 16-token tile's outputs of panels P and P + 1 (P even: one
+// 128-byte line of each row) as whole lines.  a, b: this lane's 16 bytes of
+// panel P and P + 1, as pair16_cols leaves them.  Tokens tok and tok ^ 8
+// swap their b (a DPP rotation by 8 within each 16-lane row), so store h
+// covers the 8 tokens 8h .. 8h + 7 whole, each lane writing its own a or the
+// swapped-in b.  Half-line stores (one panel of 16 tokens each) leave every
+// line's other half to another store, and with non-temporal stores the down
+// launches wrote about 1.45x the bytes of y back.  Token t of the tile is
+// output row row0 + mb + t at c + row * row_bytes; rows mb + t >= rows and
+// panels >= n_panels are not stored.  Every lane calls it.
+template <bool NT>
+__device__ inline void store_line_pair(uint8_t* c, int64_t row_bytes, int n_panels, int row0, int rows, int mb, int P,
+                                       uint4 a, uint4 b, int tok, int kg) {
+  const uint4 bx = make_uint4((uint32_t)__builtin_amdgcn_update_dpp(0, (int)b.x, 0x128, 0xf, 0xf, false),
+                              (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b.y, 0x128, 0xf, 0xf, false),
+                              (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b.z, 0x128, 0xf, 0xf, false),
+                              (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b.w, 0x128, 0xf, 0xf, false));
+  const int part = ((kg & 1) << 1) | (kg >> 1);  // this lane's 16-byte part of a panel
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const bool own = (tok >> 3) == h;
+    const int m = mb + (own ? tok : tok ^ 8);
+    const int pn = own ? P : P + 1;
+    if (m < rows && pn < n_panels) store16<NT>(c + (int64_t)(row0 + m) * row_bytes + (int64_t)(32 * pn + 8 * part) * 2, own ? a : bx);
+  }
+}
+
 // Four 16-byte LDS reads at the given byte addresses, waited for inside the
 // same asm block (the outputs are complete when it ends).  For reads the
 // compiler must not order against in-flight copies into LDS.

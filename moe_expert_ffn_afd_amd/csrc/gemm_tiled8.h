@@ -374,21 +374,24 @@ __device__ __forceinline__ void tiled8_list(const GemmParams& p, const int4* til
       } else {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const int m = wm * WR + rt * 16 + tok;
-          if (m >= rows) continue;
-          uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes;
-          const float sx = Sx[m];
+          const float sx = Sx[wm * WR + rt * 16 + tok];  // (of a row past the task's: never stored)
 #pragma unroll
-          for (int pp = 0; pp < NPW; ++pp) {
+          for (int pp = 0; pp < NPW; pp += 2) {
             const int P = q * kT8Panels + wn * NPW + pp;
             if (P >= p.n_panels) continue;
-            float v[2][4];
+            uint4 v[2];
 #pragma unroll
-            for (int sh = 0; sh < 2; ++sh)
+            for (int k = 0; k < 2; ++k) {
+              float f[2][4];
 #pragma unroll
-              for (int r4 = 0; r4 < 4; ++r4)
-                v[sh][r4] = (float)acc[rt][pp * 2 + sh][r4] * sx * Sc0[32 * (wn * NPW + pp) + 16 * sh + 4 * kg + r4];
-            store_pair(orow, P, v, true);
+              for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                  f[sh][r4] = (float)acc[rt][(pp + k) * 2 + sh][r4] * sx * Sc0[32 * (wn * NPW + pp + k) + 16 * sh + 4 * kg + r4];
+              v[k] = pair16_cols(make_uint2(pack_bf16x2(f[0][0], f[0][1]), pack_bf16x2(f[0][2], f[0][3])),
+                                 make_uint2(pack_bf16x2(f[1][0], f[1][1]), pack_bf16x2(f[1][2], f[1][3])), kg);
+            }
+            store_line_pair<true>(p.c, p.c_row_bytes, p.n_panels, row0, rows, wm * WR + rt * 16, P, v[0], v[1], tok, kg);
           }
         }
       }
@@ -453,32 +456,23 @@ __device__ __forceinline__ void tiled8_list(const GemmParams& p, const int4* til
         lds_reads_done();
         raw_barrier();  // red[] is rewritten by the next task
       } else {
-  #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const int m = wm * WR + rt * 16 + tok;
-          if (m >= rows) continue;
-          uint8_t* orow = p.c + (int64_t)(row0 + m) * p.c_row_bytes;
-  #pragma unroll
-          for (int pp = 0; pp < NPW; ++pp) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int pp = 0; pp < NPW; pp += 2) {
             const int P = q * kT8Panels + wn * NPW + pp;
             if (P >= p.n_panels) continue;
-            // lane pairs (kg, kg ^ 1) of a token swap one half panel each, so
-            // every lane stores 8 consecutive columns (16 bytes)
-            uint2 o0, o1;
-            o0.x = pack_bf16x2(acc[rt][pp * 2][0], acc[rt][pp * 2][1]);
-            o0.y = pack_bf16x2(acc[rt][pp * 2][2], acc[rt][pp * 2][3]);
-            o1.x = pack_bf16x2(acc[rt][pp * 2 + 1][0], acc[rt][pp * 2 + 1][1]);
-            o1.y = pack_bf16x2(acc[rt][pp * 2 + 1][2], acc[rt][pp * 2 + 1][3]);
-            const bool odd = (kg & 1) != 0;
-            const uint2 snd = odd ? o0 : o1;
-            uint2 rcv;
-            rcv.x = __shfl_xor(snd.x, 16, 64);
-            rcv.y = __shfl_xor(snd.y, 16, 64);
-            const uint4 v = odd ? make_uint4(rcv.x, rcv.y, o1.x, o1.y) : make_uint4(o0.x, o0.y, rcv.x, rcv.y);
-            const int col = odd ? 32 * P + 16 + 4 * (kg - 1) : 32 * P + 4 * kg;
-            store16<true>(orow + (int64_t)col * 2, v);
+            uint4 v[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+              const int b = (pp + k) * 2;
+              v[k] = pair16_cols(
+                  make_uint2(pack_bf16x2(acc[rt][b][0], acc[rt][b][1]), pack_bf16x2(acc[rt][b][2], acc[rt][b][3])),
+                  make_uint2(pack_bf16x2(acc[rt][b + 1][0], acc[rt][b + 1][1]), pack_bf16x2(acc[rt][b + 1][2], acc[rt][b + 1][3])),
+                  kg);
+            }
+            store_line_pair<true>(p.c, p.c_row_bytes, p.n_panels, row0, rows, wm * WR + rt * 16, P, v[0], v[1], tok, kg);
           }
-        }
       }
     }
   }

@@ -57,6 +57,23 @@ def test_empty_and_tiny_batches(dtype):
     layer.close()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8", "w8a8"])
+def test_largest_expert_count_and_top_k(dtype):
+    """E = 512 local experts and top-32 (the limits the library accepts), with a
+    shared expert for the 16-bit and 8-bit formats: 40 tokens make 1280
+    assignments spread thinly over the experts (most hold 1-5 rows, some none),
+    and a skewed batch puts hundreds on a few."""
+    for routing, T, seed in (("uniform", 40, 71), ("zipf", 96, 72)):
+        c = dict(dtype=dtype, T=T, H=256, I=256, E=512, K=32, routing=routing,
+                 shared_inter=0 if dtype == "f32" else 256)
+        say("case", c)
+        p = problem(c, seed=seed)
+        layer, out = run_layer(p)
+        check_dispatch(layer, p)
+        compare(out, oracle_out(to_host_problem(p)), dtype, what="E=512 K=32 " + routing)
+        layer.close()
+
+
 def test_dispatch_either_side_of_the_single_launch_limit():
     """Up to 4096 flat slots one dispatch launch also places the slots; above it a
     second launch does.  Both must give the oracle's bit-exact dispatch."""

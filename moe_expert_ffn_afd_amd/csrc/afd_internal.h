@@ -120,6 +120,10 @@ constexpr int32_t kLaunchLight = 1;
 // rows of the 8-bit LDS-tiled GEMM's m-tiles, and the fewest routed rows per
 // expert on average (and the fewest of an expert) that use it
 constexpr int kTiled8Rows = 256;
+// 8-bit batches of at least kTiled8MeanRows routed rows per expert on average
+// put every expert of more rows than one 128-row ring tile in the tiled list
+constexpr int kTiled8MeanRows = 128;
+constexpr int kTiled8MinRows = 129;
 constexpr int32_t kLaunchMixed = 2;
 
 // Cost of one heavy bf16 m-tile (tiled_rows() rows, both GEMMs) in units of

@@ -548,13 +548,14 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
   d.shared_row0 = (int32_t)nmax;
   d.mtiles = w.mtiles;
   d.mtiles_heavy = w.mtiles_heavy;
-  // 8-bit batches of at least 256 routed rows per expert on average: the
-  // experts with at least 256 rows take the LDS-tiled 8-bit body (256-row
-  // tiles, gemm_tiled8.h) instead of the ring's 128-row ones
-  const bool tiled8 = fp8 && n_flat >= (int64_t)kTiled8Rows * E;
+  // 8-bit batches of at least 128 routed rows per expert on average: the
+  // experts of more rows than one 128-row ring tile take the LDS-tiled 8-bit
+  // body (256-row tiles, gemm_tiled8.h) instead of two or more ring tiles,
+  // each of which would stream the expert's weights again
+  const bool tiled8 = fp8 && n_flat >= (int64_t)kTiled8MeanRows * E;
   d.mtiles_tiled = w.mtiles_tiled;
   d.bm_tiled = kTiled8Rows;
-  d.tiled_min_rows = tiled8 ? kTiled8Rows : 0x7fffffff;
+  d.tiled_min_rows = tiled8 ? kTiled8MinRows : 0x7fffffff;
   d.num_mtiles = w.num_mtiles;
   d.pool = dt != kF32 ? w.pool : nullptr;  // the tail pools of the ring and the bf16 tiled GEMMs
 
@@ -591,7 +592,10 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
 
   // upper bounds of the routed + shared m-tiles of this call, per list
   const int64_t mt_bound = n_flat / bm + std::min<int64_t>(E, n_flat) + (int64_t)a->S * ((T + bm - 1) / bm) + 1;
-  const int64_t mtt_bound = tiled8 ? n_flat / kTiled8Rows + (int64_t)a->S * ((T + kTiled8Rows - 1) / kTiled8Rows) + 1 : 0;
+  const int64_t mtt_bound =
+      tiled8 ? n_flat / kTiled8Rows + std::min<int64_t>(E, n_flat / kTiled8MinRows) +
+                   (int64_t)a->S * ((T + kTiled8Rows - 1) / kTiled8Rows) + 1
+             : 0;
   const int64_t mth_bound =
       light_only ? 0 : n_flat / heavy_min + (int64_t)a->S * ((T + bm_heavy - 1) / bm_heavy) + 1;
   const int64_t rows_ld_h = (int64_t)I * (w8 ? 2 : esize_of(dt));  // W8A8: bf16 h before re-quantisation

@@ -85,9 +85,9 @@ def tile_lists(dtype: str, T: int, E: int, K: int, counts, shared: bool):
     batches with no shared expert and at most 32 rows per expert on average keep
     every expert light (tiles of 32, or of 64 past 16 rows per expert on
     average) unless the largest expert exceeds two such tiles.  Block-FP8
-    and W8A8 batches of at least 256 routed rows per expert on average put
-    the experts of at least 256 rows (the shared expert too) in a third, tiled
-    list of 256-row tiles.
+    and W8A8 batches of at least 128 routed rows per expert on average put
+    the experts of more than 128 rows (the shared expert too) in a third,
+    tiled list of 256-row tiles.
     Returns {"light": [...], "heavy": [...], "tiled": [...]}, each tile
     (expert, first row in the expert, rows); the shared expert is expert E, its
     rows are tokens."""
@@ -104,7 +104,7 @@ def tile_lists(dtype: str, T: int, E: int, K: int, counts, shared: bool):
             mr_lo = 1 if n_flat <= 16 * E else 2
             if counts.max(initial=0) < 2 * 32 * mr_lo + 1:
                 bm, heavy_min = 32 * mr_lo, 1 << 30
-    tiled_min = 256 if dtype in ("fp8", "w8a8") and n_flat >= 256 * E else 1 << 30
+    tiled_min = 129 if dtype in ("fp8", "w8a8") and n_flat >= 128 * E else 1 << 30
     lists = {"light": [], "heavy": [], "tiled": []}
     sizes = list(enumerate(counts.tolist())) + ([(E, T)] if shared else [])
     for e, n in sizes:

@@ -56,15 +56,19 @@ SMALL_CASES = {
     "fp8_shared_1p5x_heavy": (small("fp8", 300, 256, 256, 6, 2, shared=384), 20),
     "w8a8_shared_3x": (small("w8a8", 50, 256, 128, 6, 2, shared=384), 21),
     "f32_shared_1p5x": (small("f32", 45, 256, 256, 5, 3, shared=384), 22),
-    # block-FP8 batches of at least 256 routed rows per expert on average: the
-    # experts of 256 rows or more (and the shared expert) take the LDS-tiled
-    # FP8 GEMM's 256-row tiles, ragged last tiles included; with Zipf routing
-    # all three lists (tiled, 128-row heavy, 64-row light) in one stage
+    # block-FP8 and W8A8 batches of at least 128 routed rows per expert on
+    # average: the experts of more than 128 rows (and the shared expert) take
+    # the LDS-tiled 8-bit GEMM's 256-row tiles, ragged last tiles included;
+    # with Zipf routing all three lists (tiled, 128-row heavy, 64-row light)
+    # in one stage; 150 rows per expert on average put experts on both sides
+    # of 128 rows
     "fp8_tiled_ragged": (small("fp8", 700, 256, 384, 4, 2), 23),
     "fp8_tiled_shared_parts": (small("fp8", 600, 512, 256, 4, 2, shared=384), 24),
     "fp8_tiled_three_lists": (small("fp8", 1100, 256, 256, 16, 4, routing="zipf"), 25),
     "w8a8_tiled_ragged": (small("w8a8", 700, 256, 384, 4, 2), 26),
     "w8a8_tiled_three_lists": (small("w8a8", 1100, 256, 256, 16, 4, routing="zipf"), 27),
+    "fp8_tiled_about_128_rows": (small("fp8", 600, 256, 384, 8, 2, shared=256), 28),
+    "w8a8_tiled_about_128_rows": (small("w8a8", 600, 256, 384, 8, 2), 29),
 }
 
 
@@ -118,11 +122,14 @@ LARGEST = {
     "bf16_zipf_T16384": inputs.workload("aggregated", T=16384),
     "fp8_shared_T16384": inputs.workload("fp8_shared", T=16384),
     "w8a8_shared_T16384": inputs.workload("w8a8_shared", T=16384),
+    # 128 routed rows per expert on average: every expert of more than one
+    # 128-row ring tile takes a 256-row tiled tile
+    "fp8_shared_T4096": inputs.workload("fp8_shared", T=4096),
 }
 # tiles per list whose first and last rows are compared (None: all); the
 # 8-bit oracle takes about 7 core-seconds per token of that shape
 LARGEST_TILES = {"bf16_uniform_T16384": None, "bf16_zipf_T16384": None, "fp8_shared_T16384": 40,
-                 "w8a8_shared_T16384": 16}
+                 "w8a8_shared_T16384": 16, "fp8_shared_T4096": 24}
 
 
 @pytest.mark.parametrize("name", sorted(LARGEST))

@@ -641,7 +641,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
     g.kdim = H;
     g.ndim = I;
     g.c = (float*)w.h;
-    int grid = (int)std::min<int64_t>(mt_bound * ((I + 63) / 64), (int64_t)cus * occupancy_wgs);
+    int grid = (int)std::min<int64_t>(mt_bound * (I / 16), (int64_t)cus * occupancy_wgs);
     AFD_HIP(launch_gemm_f32(true, g, grid, s));
     if ((st = mark(3))) return st;
     g.gather = 0;
@@ -651,7 +651,7 @@ afd_status forward_impl(afd_ffn* a, const Workspace& w, bool timed, bool own_ws,
     g.kdim = I;
     g.ndim = H;
     g.c = (float*)w.y;
-    grid = (int)std::min<int64_t>(mt_bound * ((H + 63) / 64), (int64_t)cus * occupancy_wgs);
+    grid = (int)std::min<int64_t>(mt_bound * (H / 16), (int64_t)cus * occupancy_wgs);
     AFD_HIP(launch_gemm_f32(false, g, grid, s));
     if ((st = mark(4))) return st;
   } else {

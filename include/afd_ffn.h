@@ -253,6 +253,30 @@ afd_status afd_ffn_debug_dispatch(afd_ffn_t *handle, int32_t *counts, int32_t *o
 afd_status afd_ffn_routing_errors(afd_ffn_t *handle, int32_t *count, void *stream);
 
 /*
+ * Canary-guarded workspace, a memory-safety check for tests (GPU address
+ * sanitizers are not available for these kernels): with guard_bytes > 0 (a
+ * multiple of 256, at most 16 MiB) the handle's workspace is allocated again
+ * with a band of guard_bytes bytes of the canary value 0xA5 before its first
+ * buffer and right after the last byte of every buffer it holds (dispatch
+ * arrays, tile lists, pool counters, h, its scales, y, the fused launch's
+ * state); 0 removes the bands.  Synchronises the device and frees the old
+ * workspace, so no forward of this handle may be in flight; the dispatch of
+ * the last forward is forgotten.  Results of later forwards are unchanged.
+ * A clone starts with its source's setting.  afd_ffn_forward_noalloc does
+ * not use the handle's workspace and is not covered.  Returns
+ * AFD_ERR_INVALID_ARG for a bad size, AFD_ERR_OUT_OF_MEMORY if the new
+ * workspace does not fit (the old one is kept).
+ */
+afd_status afd_ffn_set_canaries(afd_ffn_t *handle, int64_t guard_bytes);
+
+/* Check every guard band of the handle's workspace (synchronises the stream,
+ * then copies the bands to the host; *damaged_bytes is host memory): the
+ * number of band bytes that no longer hold the canary.  Returns
+ * AFD_ERR_HIP if > 0 (afd_ffn_last_error names the buffers the damaged
+ * bands follow), AFD_ERR_INVALID_ARG if the handle has no canaries. */
+afd_status afd_ffn_check_canaries(afd_ffn_t *handle, int64_t *damaged_bytes, void *stream);
+
+/*
  * Per-kernel timing of forwards, for measurement.  When enabled, forward
  * records HIP events on its stream around each timed stage; the query
  * synchronises on each forward's last event and returns, per stage, the

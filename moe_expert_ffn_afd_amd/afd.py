@@ -30,7 +30,7 @@ EXPORTS = ("afd_ffn_validate_config", "afd_ffn_create", "afd_ffn_clone", "afd_ff
            "afd_ffn_destroy", "afd_ffn_status_string", "afd_ffn_last_error", "afd_ffn_debug_dispatch",
            "afd_ffn_routing_errors", "afd_ffn_set_timing", "afd_ffn_set_timing_stages", "afd_ffn_get_timing",
            "afd_ffn_set_concurrency", "afd_ffn_set_fused", "afd_ffn_fused_errors", "afd_ffn_mfma_peak",
-           "afd_ffn_mfma_lds_peak")
+           "afd_ffn_mfma_lds_peak", "afd_ffn_set_canaries", "afd_ffn_check_canaries")
 
 
 class afd_ffn_config(ctypes.Structure):
@@ -80,6 +80,8 @@ def load(path: str = LIB_PATH):
                                           ctypes.POINTER(ctypes.c_double)]
     lib.afd_ffn_fused_errors.argtypes = [vp, ctypes.POINTER(i32), vp]
     lib.afd_ffn_get_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+    lib.afd_ffn_set_canaries.argtypes = [vp, ctypes.c_int64]
+    lib.afd_ffn_check_canaries.argtypes = [vp, ctypes.POINTER(ctypes.c_int64), vp]
     for name in EXPORTS:
         if name not in ("afd_ffn_status_string", "afd_ffn_last_error"):
             getattr(lib, name).restype = ctypes.c_int
@@ -195,6 +197,20 @@ def afd_ffn_fused_errors(handle, stream=None) -> int:
     return int(n.value)
 
 
+def afd_ffn_set_canaries(handle, guard_bytes: int) -> None:
+    """Re-allocate the handle's workspace with canary bands of guard_bytes (0: none)."""
+    _check(load().afd_ffn_set_canaries(handle, int(guard_bytes)))
+
+
+def afd_ffn_check_canaries(handle, stream=None) -> int:
+    """Workspace guard-band bytes that lost the canary (0 when every band is intact)."""
+    n = ctypes.c_int64(0)
+    st = load().afd_ffn_check_canaries(handle, ctypes.byref(n), _stream(stream))
+    if st not in (AFD_OK, AFD_ERR_HIP) or (st == AFD_ERR_HIP and n.value == 0):
+        _check(st)
+    return int(n.value)
+
+
 def afd_ffn_mfma_lds_peak(lds_reads: int, device: int = 0, iters: int = 90000):
     """(TFLOP/s, shader GHz) of the LDS-tiled bf16 GEMM's MFMA loop with (6) or without (0)
     its LDS fragment reads, no memory traffic."""
@@ -277,6 +293,14 @@ class Layer:
     def set_fused(self, enable: bool) -> None:
         """Later forwards as one persistent launch (block-FP8 and W8A8 layers)."""
         afd_ffn_set_fused(self.handle, enable)
+
+    def set_canaries(self, guard_bytes: int = 1 << 16) -> None:
+        """Canary bands of guard_bytes around every workspace buffer (0: none)."""
+        afd_ffn_set_canaries(self.handle, guard_bytes)
+
+    def check_canaries(self, stream=None) -> int:
+        """Bytes of the workspace's canary bands that were overwritten."""
+        return afd_ffn_check_canaries(self.handle, stream)
 
     def out_like(self, T: int, device="cuda"):
         dt = torch.float32 if self.dtype == "f32" else torch.bfloat16

@@ -120,6 +120,15 @@ afd_status scratch_address(int device, uint8_t** out) {
 
 namespace {
 
+// A canary guard band of a workspace: `off` bytes into the allocation, after
+// the region `after` (the first band, before every region: "start").
+struct GuardBand {
+  int64_t off;
+  const char* after;
+};
+constexpr uint8_t kCanaryByte = 0xA5;
+constexpr int64_t kMaxGuardBytes = 16ll << 20;
+
 // Per-forward device buffers (section "Workspace" of afd_internal.h), carved
 // out of one allocation for a token capacity `tcap`.
 struct Workspace {
@@ -153,6 +162,10 @@ struct afd_ffn {
   WeightStore* w = nullptr;
   uint8_t* ws_mem = nullptr;  // the handle's workspace allocation (sized for Tmax)
   Workspace ws;
+  // canary guard bands of ws_mem (afd_ffn_set_canaries): band bytes (0: none)
+  // and, per band, its offset and the region before it
+  int64_t guard = 0;
+  std::vector<GuardBand> bands;
   int last_T = 0;
   // per-stage timing: bit s of the mask times stage s (boundaries s and s + 1)
   uint32_t timing_mask = 0;
@@ -226,8 +239,11 @@ afd_status check_config(const afd_ffn_config* c) {
 }
 
 // Lay the workspace of a token capacity `tcap` out from `base` (which may be
-// null: sizes only) and return its size in bytes.
-int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w) {
+// null: sizes only) and return its size in bytes.  guard > 0 puts a band of
+// that many bytes (a multiple of 256) before the first region and right after
+// the last byte of every region, listed in `bands` when given.
+int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w, int64_t guard = 0,
+                         std::vector<GuardBand>* bands = nullptr) {
   const int64_t nmax = (int64_t)tcap * a->K;
   const int64_t rows = nmax + (int64_t)a->S * tcap;  // routed rows, then the shared expert's parts
   const int64_t max_chunks = (nmax + 1023) / 1024;
@@ -236,21 +252,38 @@ int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w
   const int ys = a->dtype == kF32 ? 4 : 2;
   const bool w8 = a->dtype == kW8A8;
   int64_t off = 0;
-  auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + bytes, 256); return o; };
-  const int64_t o_counts = take(4ll * a->E), o_offsets = take(4ll * (a->E + 1)), o_err = take(4),
-                o_nmt = take(32), o_cb = take(4ll * max_chunks * a->E), o_sa = take(4 * nmax),
-                o_ro = take(4 * nmax), o_mt = take(16ll * max_mtiles), o_mth = take(16ll * max_mtiles),
-                o_mtt = take(a->dtype == kFP8 || w8 ? 16ll * max_mtiles : 0),
-                o_pool = take(16),
-                o_h = take(rows * a->I * (w8 ? 2 : es)),
-                o_hs = take(a->dtype == kFP8 ? rows * (a->I / 128) * 4 : w8 ? rows * 4 : 0),
-                o_xs = take(a->dtype == kFP8 ? rows * (a->H / 128) * 4 : w8 ? rows * 4 : 0),
-                o_h8 = take(w8 ? rows * a->I : 0), o_pm = take(w8 ? rows * (a->I / 128) * 4 : 0),
-                o_y = take(rows * a->H * ys);
+  if (bands) bands->clear();
+  if (guard > 0) {  // the band before every region
+    if (bands) bands->push_back({0, "start"});
+    off = guard;
+  }
+  auto take = [&](int64_t bytes, const char* name) {  // a region, then its band from its exact end
+    const int64_t o = off;
+    if (guard > 0 && bytes > 0) {
+      if (bands) bands->push_back({o + bytes, name});
+      off = align_up(o + bytes + guard, 256);
+    } else {
+      off = align_up(o + bytes, 256);
+    }
+    return o;
+  };
+  const int64_t o_counts = take(4ll * a->E, "counts"), o_offsets = take(4ll * (a->E + 1), "offsets"),
+                o_err = take(4, "err"), o_nmt = take(32, "num_mtiles"),
+                o_cb = take(4ll * max_chunks * a->E, "chunk_base"), o_sa = take(4 * nmax, "sorted_assign"),
+                o_ro = take(4 * nmax, "row_of"), o_mt = take(16ll * max_mtiles, "mtiles"),
+                o_mth = take(16ll * max_mtiles, "mtiles_heavy"),
+                o_mtt = take(a->dtype == kFP8 || w8 ? 16ll * max_mtiles : 0, "mtiles_tiled"),
+                o_pool = take(16, "pool"),
+                o_h = take(rows * a->I * (w8 ? 2 : es), "h"),
+                o_hs = take(a->dtype == kFP8 ? rows * (a->I / 128) * 4 : w8 ? rows * 4 : 0, "h_scales"),
+                o_xs = take(a->dtype == kFP8 ? rows * (a->H / 128) * 4 : w8 ? rows * 4 : 0, "x_scales"),
+                o_h8 = take(w8 ? rows * a->I : 0, "h8"), o_pm = take(w8 ? rows * (a->I / 128) * 4 : 0, "pamax"),
+                o_y = take(rows * a->H * ys, "y");
   const bool fz = a->dtype != kF32;  // the fused launch's state
   const int64_t fg = fz ? std::min(a->num_cus, kFusedMaxGrid) : 0;
-  const int64_t o_bar = take(fz ? 16 : 0), o_fcc = take(4 * fg * a->E), o_fcb = take(4 * fg),
-                o_flb = take(4 * fg * a->E), o_ftot = take(fz ? 4ll * a->E : 0);
+  const int64_t o_bar = take(fz ? 16 : 0, "bar"), o_fcc = take(4 * fg * a->E, "chunk_counts"),
+                o_fcb = take(4 * fg, "chunk_bad"), o_flb = take(4 * fg * a->E, "local_base"),
+                o_ftot = take(fz ? 4ll * a->E : 0, "totals");
   if (base && w) {
     w->counts = (int32_t*)(base + o_counts);
     w->offsets = (int32_t*)(base + o_offsets);
@@ -284,14 +317,16 @@ int64_t layout_workspace(const afd_ffn* a, int tcap, uint8_t* base, Workspace* w
 }
 
 afd_status alloc_workspace(afd_ffn* a) {
-  const int64_t bytes = layout_workspace(a, a->Tmax, nullptr, nullptr);
+  const int64_t bytes = layout_workspace(a, a->Tmax, nullptr, nullptr, a->guard);
   if (hipMalloc((void**)&a->ws_mem, bytes) != hipSuccess) {
     (void)hipGetLastError();
     a->ws_mem = nullptr;
     return fail(AFD_ERR_OUT_OF_MEMORY, "workspace of %lld bytes", (long long)bytes);
   }
-  layout_workspace(a, a->Tmax, a->ws_mem, &a->ws);
+  layout_workspace(a, a->Tmax, a->ws_mem, &a->ws, a->guard, &a->bands);
   AFD_HIP(hipMemset(a->ws_mem, 0, bytes));
+  for (const GuardBand& b : a->bands) AFD_HIP(hipMemset(a->ws_mem + b.off, kCanaryByte, a->guard));
+  AFD_HIP(hipDeviceSynchronize());
   return AFD_OK;
 }
 
@@ -888,6 +923,7 @@ afd_status afd_ffn_clone(const afd_ffn_t* src, afd_ffn_t** out_handle) {
   a->num_cus = src->num_cus;
   a->concurrency = src->concurrency;
   a->fused = src->fused;
+  a->guard = src->guard;
   a->w = src->w;
   a->w->refs.fetch_add(1);
   afd_status st = alloc_workspace(a);
@@ -969,6 +1005,66 @@ afd_status afd_ffn_set_concurrency(afd_ffn_t* a, int32_t streams) {
     return fail(AFD_ERR_INVALID_ARG, "concurrency %d outside [1, %d]", streams, a->num_cus);
   a->concurrency = streams;
   return AFD_OK;
+}
+
+afd_status afd_ffn_set_canaries(afd_ffn_t* a, int64_t guard_bytes) {
+  g_last_error.clear();
+  if (!a) return fail(AFD_ERR_INVALID_ARG, "handle is NULL");
+  if (guard_bytes < 0 || guard_bytes > kMaxGuardBytes || guard_bytes % 256)
+    return fail(AFD_ERR_INVALID_ARG, "guard_bytes %lld: a multiple of 256 in [0, %lld]", (long long)guard_bytes,
+                (long long)kMaxGuardBytes);
+  DeviceGuard dg(a->device);
+  if (!dg.ok) return fail(AFD_ERR_HIP, "cannot select device %d", a->device);
+  AFD_HIP(hipDeviceSynchronize());  // no forward of the handle may still use the old workspace
+  uint8_t* old_mem = a->ws_mem;
+  const Workspace old_ws = a->ws;
+  const int64_t old_guard = a->guard;
+  std::vector<GuardBand> old_bands = a->bands;
+  a->guard = guard_bytes;
+  a->ws_mem = nullptr;
+  afd_status st = alloc_workspace(a);
+  if (st) {  // keep the old workspace
+    if (a->ws_mem) (void)hipFree(a->ws_mem);
+    a->ws_mem = old_mem;
+    a->ws = old_ws;
+    a->guard = old_guard;
+    a->bands = old_bands;
+    return st;
+  }
+  AFD_HIP(hipFree(old_mem));
+  a->last_T = 0;
+  return AFD_OK;
+}
+
+afd_status afd_ffn_check_canaries(afd_ffn_t* a, int64_t* damaged_bytes, void* stream) {
+  g_last_error.clear();
+  if (!a || !damaged_bytes) return fail(AFD_ERR_INVALID_ARG, "NULL argument");
+  *damaged_bytes = 0;
+  if (a->guard <= 0) return fail(AFD_ERR_INVALID_ARG, "the handle has no canaries (afd_ffn_set_canaries)");
+  DeviceGuard dg(a->device);
+  if (!dg.ok) return fail(AFD_ERR_HIP, "cannot select device %d", a->device);
+  AFD_HIP(hipStreamSynchronize((hipStream_t)stream));
+  std::vector<uint8_t> host(a->guard);
+  std::string where;
+  int64_t bad = 0;
+  for (const GuardBand& b : a->bands) {
+    AFD_HIP(hipMemcpy(host.data(), a->ws_mem + b.off, a->guard, hipMemcpyDeviceToHost));
+    int64_t n = 0, first = -1;
+    for (int64_t i = 0; i < a->guard; ++i)
+      if (host[i] != kCanaryByte) {
+        if (first < 0) first = i;
+        ++n;
+      }
+    if (n) {
+      char buf[128];
+      snprintf(buf, sizeof buf, "%s%lld bytes after %s (first at +%lld)", where.empty() ? "" : "; ", (long long)n,
+               b.after, (long long)first);
+      where += buf;
+    }
+    bad += n;
+  }
+  *damaged_bytes = bad;
+  return bad ? fail(AFD_ERR_HIP, "canaries overwritten: %s", where.c_str()) : AFD_OK;
 }
 
 afd_status afd_ffn_mfma_peak(int32_t dtype, int32_t device, int32_t iters, double* tflops, double* clock_ghz) {

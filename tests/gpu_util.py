@@ -28,6 +28,29 @@ def to_host_problem(p: dict) -> dict:
     return {k: (v.detach().cpu() if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
 
 
+# canary-guarded buffers: bytes of each workspace band, output elements before
+# and after a caller's out inside its guarded tensor, and that tensor's canary
+GUARD = 1 << 16
+PAD = 1 << 15
+CANARY = 0x5A
+
+
+def guarded_out(layer, T):
+    """(buffer, out): out[T, H] inside a larger tensor filled with CANARY bytes."""
+    dt = torch.float32 if layer.dtype == "f32" else torch.bfloat16
+    buf = torch.empty(T * layer.H + 2 * PAD, dtype=dt, device="cuda")
+    buf.view(torch.uint8).fill_(CANARY)
+    return buf, buf[PAD:PAD + T * layer.H].view(T, layer.H)
+
+
+def check_out_guard(buf, T, H):
+    b = buf.view(torch.uint8)
+    esz = buf.element_size()
+    head, tail = b[:PAD * esz], b[(PAD + T * H) * esz:]
+    assert bool((head == CANARY).all()), "bytes before out[0, 0] were written"
+    assert bool((tail == CANARY).all()), "bytes after out[T-1, H-1] were written"
+
+
 def run_layer(p: dict, layer=None, stream=None, max_tokens=None):
     layer = layer or afd.Layer(p, max_tokens=max_tokens)
     out = layer.forward(p["hidden"], p["hidden_scales"], p["ids"], p["weights"], stream=stream)

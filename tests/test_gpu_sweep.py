@@ -5,13 +5,18 @@ expert from a fixed seed, so the sweep covers combinations the hand-written
 cases do not (odd panel counts, K close to E, experts on both sides of the
 light/heavy split, tails of every tile size, shared experts of other widths) while staying reproducible.
 Same bar as the parity tests: bit-exact dispatch, max|err| <= tol * max|ref|.
+Every case runs with canary bands around the handle's workspace buffers and
+its output, which must come back untouched.
 """
 import os
 
 import numpy as np
 import pytest
+import torch
 
-from gpu_util import check_dispatch, compare, oracle_out, problem, run_layer, say, to_host_problem
+from gpu_util import (GUARD, check_dispatch, check_out_guard, compare, guarded_out, oracle_out, problem, say,
+                      to_host_problem)
+from moe_expert_ffn_afd_amd import afd
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +43,13 @@ def test_random_shapes(dtype, i):
     cfg = draw_case(dtype, i)
     say("case", dtype, i, cfg)
     p = problem(cfg, seed=100 + i)
-    layer, out = run_layer(p)
+    layer = afd.Layer(p)
+    layer.set_canaries(GUARD)
+    buf, out = guarded_out(layer, cfg["T"])
+    layer.forward(p["hidden"], p["hidden_scales"], p["ids"], p["weights"], out=out)
+    torch.cuda.synchronize()
+    check_out_guard(buf, cfg["T"], cfg["H"])
+    assert layer.check_canaries() == 0
     check_dispatch(layer, p)
     ref = oracle_out(to_host_problem(p))
     compare(out, ref, dtype, what="%s #%d %s" % (dtype, i, cfg))

@@ -11,7 +11,9 @@ T=2048, H=7168, E=256, I=2048, top-8.  Prints one JSON line with
 routed tokens/s, the roofline of the dominant kernel (timed with HIP events
 on its own stream inside the timed region, the only stage timed there) and
 the oracle's CPU baseline; the per-stage breakdown comes from up to 20 further
-steps with every stage timed.
+steps with every stage timed.  The oracle's sample also checks the measured
+run ("check": the sampled tokens' outputs within the stated tolerance, every
+microbatch's dispatch bit for bit); the run exits nonzero if that fails.
 
 Other modes: --copy-calibration runs a plain device copy of known size (the
 reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters);
@@ -110,8 +112,10 @@ def algorithmic_units(cfg: dict, ids) -> dict:
                 gu_flops=4.0 * H * h_elems, dn_flops=2.0 * H * h_elems, layer_flops=6.0 * H * h_elems)
 
 
-def cpu_baseline(p: dict, cfg: dict, budget_s: float = 12.0) -> dict:
-    """Time the fp64 oracle (as it stands) on a bounded sample of the same batch."""
+def cpu_baseline(p: dict, cfg: dict, budget_s: float = 12.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same batch.
+    Returns the baseline record and the oracle's outputs of the sampled tokens
+    (the first n of the batch, [n, H] fp64)."""
     import numpy as np
     import torch
 
@@ -122,18 +126,46 @@ def cpu_baseline(p: dict, cfg: dict, budget_s: float = 12.0) -> dict:
     T = cfg["T"]
     n = min(T, cores)
     t0 = time.perf_counter()
-    orc.forward(host, tokens=np.arange(n, dtype=np.int32), nthreads=cores)
+    refs = [orc.forward(host, tokens=np.arange(n, dtype=np.int32), nthreads=cores)]
     t1 = time.perf_counter() - t0
     total_t, total_n = t1, n
     if t1 < budget_s and n < T:
         n2 = int(min(T - n, max(cores, (budget_s - t1) / max(t1, 1e-3) * n)))
         n2 = max(cores, n2 // cores * cores) if n2 >= cores else n2
         t0 = time.perf_counter()
-        orc.forward(host, tokens=np.arange(n, n + n2, dtype=np.int32), nthreads=cores)
+        refs.append(orc.forward(host, tokens=np.arange(n, n + n2, dtype=np.int32), nthreads=cores))
         total_t += time.perf_counter() - t0
         total_n += n2
-    return {"value": total_n / total_t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "first %d of the %d tokens of the same seeded batch, fp64, %.1f s" % (total_n, T, total_t)}
+    rec = {"value": total_n / total_t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": "first %d of the %d tokens of the same seeded batch, fp64, %.1f s" % (total_n, T, total_t)}
+    return rec, np.concatenate(refs, axis=0)
+
+
+# stated accuracy of the layer against the fp64 oracle: max|out - ref| <= tol * max|ref|
+CHECK_TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "w8a8": 6e-2}
+
+
+def check_run(cfg: dict, out, ref, layers, parts) -> dict:
+    """The timed run's own outputs on the oracle's sampled tokens, and every
+    microbatch's dispatch against the oracle's, bit for bit."""
+    import numpy as np
+
+    from oracle import oracle as orc
+
+    n = ref.shape[0]
+    got = out[:n].double().cpu().numpy()
+    err = float(np.max(np.abs(got - ref))) if n else 0.0
+    scale = float(np.max(np.abs(ref))) if n else 0.0
+    ratio = err / scale if scale else 0.0
+    exact = True
+    for layer, q in zip(layers, parts):
+        d = layer.dispatch(q["T"])
+        want = orc.dispatch(q["ids"].cpu().numpy(), cfg["E"])
+        exact = exact and all(np.array_equal(d[k], want[k]) for k in ("counts", "offsets", "sorted_assign", "row_of"))
+    tol = CHECK_TOL[cfg["dtype"]]
+    finite = bool(np.isfinite(got).all())
+    return {"tokens": n, "max_err_over_max_ref": float("%.4g" % ratio), "tol": tol, "dispatch_exact": exact,
+            "ok": bool(exact and finite and ratio <= tol)}
 
 
 SWEEP_TOKENS = (64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384)
@@ -438,11 +470,18 @@ def main():
     }
     if graph_ms is not None:
         result["graph_ms_per_step"] = round(graph_ms, 4)
+    ok = True
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(p, cfg)
+        result["cpu_baseline"], ref = cpu_baseline(p, cfg)
+        # the oracle's sample doubles as a check of the measured run's outputs
+        torch.cuda.synchronize()
+        result["check"] = check_run(cfg, torch.cat(outs) if mbs > 1 else outs[0], ref, layers, parts)
+        ok = result["check"]["ok"]
     print(json.dumps(result), flush=True)
     for layer in layers[::-1]:
         layer.close()
+    if not ok:
+        sys.exit("the measured run's outputs or dispatch disagree with the oracle")
 
 
 if __name__ == "__main__":

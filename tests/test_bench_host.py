@@ -1,4 +1,4 @@
-"""Host-side checks of bench.py: the one-GPU guard and the algorithmic units."""
+"""Host-side checks of bench.py: the one-GPU guard, the algorithmic units and the check of a measured run."""
 import importlib.util
 import os
 import subprocess
@@ -60,3 +60,40 @@ def test_roofline_kernel_labels_follow_the_tile_policy():
     assert "gemm_mixed_kernel<true, 1>" in b.gate_up_kernels(dict(inputs.workload("decode"), shared_inter=1536), 512)
     assert "gemm_ring_kernel<true>" in b.gate_up_kernels(inputs.workload("fp8_shared"), 2048)
     assert "gemm_f32_kernel<true>" in b.gate_up_kernels(inputs.workload("tiny"), 64)
+
+
+def test_check_of_the_measured_run():
+    """bench.py's check of a run: outputs of the sampled tokens against the
+    oracle's within the tolerance, and each microbatch's dispatch bit for bit
+    (here a stand-in for the layer handle returns a dispatch on the host)."""
+    import torch
+
+    from oracle import oracle as orc
+
+    b = _bench()
+    ids = np.array([[0, 2], [1, -1], [2, 0], [3, 3]], dtype=np.int32)
+    cfg = {"dtype": "bf16", "E": 4}
+
+    class Handle:
+        def __init__(self, d):
+            self.d = d
+
+        def dispatch(self, T):
+            return self.d
+
+    q = {"T": 4, "ids": torch.from_numpy(ids)}
+    good = orc.dispatch(ids, 4)
+    ref = np.array([[1.0, -2.0], [0.5, 4.0]])
+    out = torch.tensor([[1.0, -2.0], [0.5, 4.0], [9.0, 9.0], [9.0, 9.0]])
+    c = b.check_run(cfg, out, ref, [Handle(good)], [q])
+    assert c["ok"] and c["dispatch_exact"] and c["tokens"] == 2 and c["max_err_over_max_ref"] == 0.0
+    # an error of 3 % of max|ref| is past the bf16 tolerance (2 %)
+    c = b.check_run(cfg, out + torch.tensor([[0.0, 0.12], [0.0, 0.0], [0, 0], [0, 0]]), ref, [Handle(good)], [q])
+    assert not c["ok"] and abs(c["max_err_over_max_ref"] - 0.03) < 1e-9
+    # one moved row of the permutation fails the dispatch check
+    bad = dict(good, sorted_assign=good["sorted_assign"][::-1].copy())
+    c = b.check_run(cfg, out, ref, [Handle(bad)], [q])
+    assert not c["ok"] and not c["dispatch_exact"]
+    # non-finite outputs fail
+    c = b.check_run(cfg, torch.tensor([[float("nan"), 0.0], [0.5, 4.0]]), ref, [Handle(good)], [q])
+    assert not c["ok"]

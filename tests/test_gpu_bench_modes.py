@@ -1,4 +1,5 @@
-"""bench.py's other modes on the GPU, at the tiny fp32 workload: the step
+"""bench.py's modes on the GPU, at the tiny fp32 workload: a line with the
+oracle's CPU baseline and the check of its own run, the step
 replayed from a HIP graph (graph_ms_per_step next to the eager line) and the
 batch-size sweep (one JSON line per T, every T of the sweep that fits; the
 sweep's own path, one handle for the largest T running prefixes of one batch,
@@ -60,6 +61,18 @@ def test_sweep_path_matches_oracle():
         compare(out, oracle_out(to_host_problem(q)), cfg["dtype"], what="sweep T=%d" % T)
         assert np.isfinite(out.cpu().numpy()).all()
     layer.close()
+
+
+def test_default_line_checks_its_run():
+    """With the oracle's CPU baseline on, a bench line checks its own run."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--steps", "5",
+                        "--warmup", "2"], capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    say("  check", d["check"], "cpu baseline", d["cpu_baseline"])
+    assert d["check"]["ok"] and d["check"]["dispatch_exact"] and d["check"]["tokens"] == 64
+    assert 0.0 <= d["check"]["max_err_over_max_ref"] <= 1e-5
+    assert d["cpu_baseline"]["kind"] == "oracle" and d["cpu_baseline"]["value"] > 0
 
 
 def test_mfma_ceiling_line():

@@ -51,6 +51,19 @@ def check_out_guard(buf, T, H):
     assert bool((tail == CANARY).all()), "bytes after out[T-1, H-1] were written"
 
 
+def run_layer_guarded(p: dict):
+    """The forward on a handle with canary bands, into a guarded output; asserts
+    that no band byte (workspace or output) was written."""
+    layer = afd.Layer(p)
+    layer.set_canaries(GUARD)
+    buf, out = guarded_out(layer, p["T"])
+    layer.forward(p["hidden"], p["hidden_scales"], p["ids"], p["weights"], out=out)
+    torch.cuda.synchronize()
+    check_out_guard(buf, p["T"], p["H"])
+    assert layer.check_canaries() == 0
+    return layer, out
+
+
 def run_layer(p: dict, layer=None, stream=None, max_tokens=None):
     layer = layer or afd.Layer(p, max_tokens=max_tokens)
     out = layer.forward(p["hidden"], p["hidden_scales"], p["ids"], p["weights"], stream=stream)

@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import check_dispatch, compare, oracle_out, problem, run_layer, say, to_host_problem
+from gpu_util import check_dispatch, compare, oracle_out, problem, run_layer, run_layer_guarded, say, to_host_problem
 from moe_expert_ffn_afd_amd import afd
 
 pytestmark = pytest.mark.gpu
@@ -72,6 +72,47 @@ def test_largest_expert_count_and_top_k(dtype):
         check_dispatch(layer, p)
         compare(out, oracle_out(to_host_problem(p)), dtype, what="E=512 K=32 " + routing)
         layer.close()
+
+
+LARGEST_WIDTHS = {
+    # H and I at the 8-bit formats' limit (128 scale blocks, int32 sums of
+    # 16384 int8 products) and bf16 at the same widths; one width at its
+    # limit with the other at its smallest
+    # (tokens: the oracle takes about 1.5 core-seconds per token and expert
+    # at 16384 x 16384)
+    "fp8_H16384_I16384": ("fp8", 16384, 16384, 12),
+    "w8a8_H16384_I16384": ("w8a8", 16384, 16384, 12),
+    "bf16_H16384_I16384": ("bf16", 16384, 16384, 12),
+    "fp8_H128_I16384": ("fp8", 128, 16384, 33),
+    "bf16_H16384_I128": ("bf16", 16384, 128, 33),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LARGEST_WIDTHS))
+def test_largest_hidden_and_intermediate_widths(name):
+    """The widest reductions the library accepts: top-2 of 3 experts, every
+    token against the oracle, inside canary bands."""
+    dtype, H, I, T = LARGEST_WIDTHS[name]
+    c = dict(dtype=dtype, T=T, H=H, I=I, E=3, K=2, routing="uniform", shared_inter=0)
+    say("case", name, c)
+    p = problem(c, seed=81)
+    layer, out = run_layer_guarded(p)
+    check_dispatch(layer, p)
+    compare(out, oracle_out(to_host_problem(p)), dtype, what=name)
+    layer.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8", "w8a8"])
+def test_widest_shared_expert(dtype):
+    """A shared expert of 16 times the routed width (the most parts the
+    library takes): 16 parts of width I added to every token in order."""
+    c = dict(dtype=dtype, T=70, H=256, I=128, E=4, K=2, routing="uniform", shared_inter=16 * 128)
+    say("case", c)
+    p = problem(c, seed=82)
+    layer, out = run_layer_guarded(p)
+    check_dispatch(layer, p)
+    compare(out, oracle_out(to_host_problem(p)), dtype, what="shared expert of 16 parts")
+    layer.close()
 
 
 def test_dispatch_either_side_of_the_single_launch_limit():

@@ -126,3 +126,16 @@ def test_status_strings(lib):
     for st in range(6):
         assert afd.afd_ffn_status_string(st)
     assert "unknown" in afd.afd_ffn_status_string(99)
+
+
+def test_c_program_is_built_and_links():
+    """The plain-C user of the ABI (tests/c_abi/abi_forward, run on the GPU by
+    test_gpu_c_abi.py) is built and every library it needs resolves."""
+    import subprocess
+
+    binary = os.path.join(ROOT, "tests", "c_abi", "abi_forward")
+    assert os.path.exists(binary), "run the build step (it builds tests/c_abi/abi_forward)"
+    r = subprocess.run(["ldd", binary], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and "not found" not in r.stdout, r.stdout
+    for lib in ("libafd_ffn.so", "libafd_oracle.so", "libamdhip64"):
+        assert lib in r.stdout, lib

@@ -137,8 +137,21 @@ def cpu_baseline(p: dict, cfg: dict, budget_s: float = 12.0):
         total_t += time.perf_counter() - t0
         total_n += n2
     rec = {"value": total_n / total_t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-           "sample": "first %d of the %d tokens of the same seeded batch, fp64, %.1f s" % (total_n, T, total_t)}
+           "sample": "first %d of the %d tokens of the same seeded batch, fp64, %.1f s" % (total_n, T, total_t),
+           "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
     return rec, np.concatenate(refs, axis=0)
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first processor of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # stated accuracy of the layer against the fp64 oracle: max|out - ref| <= tol * max|ref|

@@ -276,6 +276,14 @@ afd_status afd_ffn_set_canaries(afd_ffn_t *handle, int64_t guard_bytes);
  * bands follow), AFD_ERR_INVALID_ARG if the handle has no canaries. */
 afd_status afd_ffn_check_canaries(afd_ffn_t *handle, int64_t *damaged_bytes, void *stream);
 
+/* Test facility: overwrite byte `offset` of guard band `band` (0 = the band
+ * before the first buffer, then one per non-empty buffer in workspace order)
+ * with a value other than the canary, from the host (synchronises the
+ * device), so a test can show that afd_ffn_check_canaries finds the damage
+ * and names the buffer the band follows.  AFD_ERR_INVALID_ARG without
+ * canaries or for a band or offset out of range. */
+afd_status afd_ffn_debug_poke_canary(afd_ffn_t *handle, int32_t band, int64_t offset);
+
 /*
  * Per-kernel timing of forwards, for measurement.  When enabled, forward
  * records HIP events on its stream around each timed stage; the query

@@ -30,7 +30,7 @@ EXPORTS = ("afd_ffn_validate_config", "afd_ffn_create", "afd_ffn_clone", "afd_ff
            "afd_ffn_destroy", "afd_ffn_status_string", "afd_ffn_last_error", "afd_ffn_debug_dispatch",
            "afd_ffn_routing_errors", "afd_ffn_set_timing", "afd_ffn_set_timing_stages", "afd_ffn_get_timing",
            "afd_ffn_set_concurrency", "afd_ffn_set_fused", "afd_ffn_fused_errors", "afd_ffn_mfma_peak",
-           "afd_ffn_mfma_lds_peak", "afd_ffn_set_canaries", "afd_ffn_check_canaries")
+           "afd_ffn_mfma_lds_peak", "afd_ffn_set_canaries", "afd_ffn_check_canaries", "afd_ffn_debug_poke_canary")
 
 
 class afd_ffn_config(ctypes.Structure):
@@ -82,6 +82,7 @@ def load(path: str = LIB_PATH):
     lib.afd_ffn_get_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
     lib.afd_ffn_set_canaries.argtypes = [vp, ctypes.c_int64]
     lib.afd_ffn_check_canaries.argtypes = [vp, ctypes.POINTER(ctypes.c_int64), vp]
+    lib.afd_ffn_debug_poke_canary.argtypes = [vp, i32, ctypes.c_int64]
     for name in EXPORTS:
         if name not in ("afd_ffn_status_string", "afd_ffn_last_error"):
             getattr(lib, name).restype = ctypes.c_int
@@ -209,6 +210,11 @@ def afd_ffn_check_canaries(handle, stream=None) -> int:
     if st not in (AFD_OK, AFD_ERR_HIP) or (st == AFD_ERR_HIP and n.value == 0):
         _check(st)
     return int(n.value)
+
+
+def afd_ffn_debug_poke_canary(handle, band: int, offset: int) -> None:
+    """Overwrite one byte of a guard band (a positive control of the canary check)."""
+    _check(load().afd_ffn_debug_poke_canary(handle, int(band), int(offset)))
 
 
 def afd_ffn_mfma_lds_peak(lds_reads: int, device: int = 0, iters: int = 90000):

@@ -1067,6 +1067,21 @@ afd_status afd_ffn_check_canaries(afd_ffn_t* a, int64_t* damaged_bytes, void* st
   return bad ? fail(AFD_ERR_HIP, "canaries overwritten: %s", where.c_str()) : AFD_OK;
 }
 
+afd_status afd_ffn_debug_poke_canary(afd_ffn_t* a, int32_t band, int64_t offset) {
+  g_last_error.clear();
+  if (!a) return fail(AFD_ERR_INVALID_ARG, "handle is NULL");
+  if (a->guard <= 0) return fail(AFD_ERR_INVALID_ARG, "the handle has no canaries (afd_ffn_set_canaries)");
+  if (band < 0 || band >= (int32_t)a->bands.size() || offset < 0 || offset >= a->guard)
+    return fail(AFD_ERR_INVALID_ARG, "band %d, offset %lld outside %d bands of %lld bytes", band, (long long)offset,
+                (int)a->bands.size(), (long long)a->guard);
+  DeviceGuard dg(a->device);
+  if (!dg.ok) return fail(AFD_ERR_HIP, "cannot select device %d", a->device);
+  AFD_HIP(hipDeviceSynchronize());
+  AFD_HIP(hipMemset(a->ws_mem + a->bands[band].off + offset, (int)(uint8_t)~kCanaryByte, 1));
+  AFD_HIP(hipDeviceSynchronize());
+  return AFD_OK;
+}
+
 afd_status afd_ffn_mfma_peak(int32_t dtype, int32_t device, int32_t iters, double* tflops, double* clock_ghz) {
   g_last_error.clear();
   if (!tflops || !clock_ghz || iters <= 0) return fail(AFD_ERR_INVALID_ARG, "NULL output or iters <= 0");

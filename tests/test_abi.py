@@ -112,6 +112,7 @@ def test_null_arguments_rejected_on_host(lib):
     assert lib.afd_ffn_set_canaries(None, 65536) == afd.AFD_ERR_INVALID_ARG
     n = ctypes.c_int64(-1)
     assert lib.afd_ffn_check_canaries(None, ctypes.byref(n), None) == afd.AFD_ERR_INVALID_ARG
+    assert lib.afd_ffn_debug_poke_canary(None, 0, 0) == afd.AFD_ERR_INVALID_ARG
     assert lib.afd_ffn_destroy(None) == afd.AFD_OK
     # measurement helpers: argument errors come back before any device call
     t, c = ctypes.c_double(0.0), ctypes.c_double(0.0)
